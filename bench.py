@@ -1,0 +1,208 @@
+"""Benchmark: RACE attention layer forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+One step = race_attn_fwd (bucket reduce, bank sums, readout) followed by
+race_attn_bwd (Q-side gradients with the gradient-bank reduce, bank sums,
+K/V-side gradients) over one batch of seeded synthetic inputs already
+resident in HBM.  Default workload: non-causal, B=1, H=4, N=12,000,000,
+d=128, P=4, L=2, beta=4, bf16 I/O with float32 accumulation.
+
+Prints one JSON line.  ``roofline`` covers the kernel with the largest share
+of the timed region: algorithmic bytes per launch (the token rows it must
+read and write) over its mean launch time, measured with HIP events that the
+library records on the launch stream during the timed steps.  ``traffic``
+comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counts of that kernel
+(scaled by a plain copy kernel's counts), or null when the kernel sources
+changed since they were taken.  ``cpu_baseline`` times the fp64 oracle on a
+bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+# bytes of token rows each kernel must move, per (token, head), in units of d * elem_size
+ROW_PASSES = {
+    "race_bucket_reduce": 2,   # read K, V
+    "race_readout_norm": 2,    # read Q, write O
+    "race_bwd_q": 3,           # read Q, dO, write dQ
+    "race_bwd_kv": 4,          # read K, V, write dK, dV
+    "race_causal_fwd": 4,      # read Q, K, V, write O
+    "race_causal_bwd_q": 5,    # read Q, K, V, dO, write dQ
+    "race_causal_bwd_kv": 6,   # read Q, K, V, dO, write dK, dV
+    "race_causal_segsum": 2,   # read K, V
+}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "linear_attention_soft_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 18)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, copy 1 GiB once (reference kernel for rocprofv3 byte counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, w, n_tok):
+    """fp64 oracle, forward + backward, on head (0, 0)'s first n_tok tokens taken as one sequence."""
+    import numpy as np
+    from oracle import race_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    n = min(n_tok, w.N)
+    f64 = lambda t: t[0, 0, :n].to("cpu").double().numpy()
+    Q, K, V, dO = (f64(inp[k]) for k in ("Q", "K", "V", "dO"))
+    Wn = inp["W"].double().numpy()
+    t0 = time.perf_counter()
+    if w.causal:
+        orc.causal_forward_head(Q, K, V, Wn, w.beta)
+    else:
+        orc.forward_head(Q, K, V, Wn, w.beta)
+    if "bwd" in w.phases:
+        orc.backward_head(Q, K, V, Wn, w.beta, dO, w.causal)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head (0,0), first {n} tokens as one sequence, fwd+bwd fp64 numpy, {dt:.1f} s"}
+
+
+def load_traffic(workload_name: str, kernel: str, launches_tokens: int):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return float(k["bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the layer shards by heads or by sequence segments; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_attention_soft_amd as race
+    import race_inputs as ri
+
+    w = ri.WORKLOADS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    race.lib()
+    dev = "cuda"
+    print(f"# workload {w.name}: generating inputs on the GPU", file=sys.stderr, flush=True)
+    inp = ri.make_inputs(w, device=dev, with_grad_out=True)
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    W = inp["W"].to(dev)
+    O = torch.empty_like(Q)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    shape = race._shape_of(Q)
+    st = torch.empty(race.race_attn_state_bytes(shape, w.P, w.L, w.causal), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, False), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, True), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        race.race_attn_fwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, O=O, state=st, workspace=wsf)
+        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, dQ=dQ, dK=dK, dV=dV, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    race.profile_reset()
+    race.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    race.profile_enable(False)
+    kern = race.profile_report()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens = w.B * w.N
+    value = tokens * args.steps / (max(ms_step * args.steps, wall * 1e3) * 1e-3)
+
+    elem = 2 if w.dtype == "bf16" else 4
+    row_bytes = w.B * w.H * w.N * w.d * elem
+    dom = max(kern.items(), key=lambda kv: kv[1][1])
+    dname, (dl, dms) = dom
+    avg_ms = dms / dl
+    alg_bytes = ROW_PASSES.get(dname, 0) * row_bytes
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name, dname, tokens)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the fp64 oracle on a CPU sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, w, args.cpu_sample_tokens)
+
+    out = {
+        "metric": "RACE layer fwd+bwd tokens/s at N=12M, H=4, d=128; % of HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; iid N(0,1) Q, K, V, dO; Gaussian W)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "L": w.L,
+                   "beta": w.beta, "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": dname, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": avg_ms},
+        "step_hbm_frac": (11 * row_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/*
+ * race_attn.h -- C ABI of the MI355X (gfx950) RACE attention library.
+ *
+ * RACE attention ("RACE Attention" slides on arXiv 2510.04008v5, frames
+ * "Soft corner assignments make hashing differentiable", "Each bucket stores
+ * mass and a weighted value sum", "Normalize after combining the tables" and
+ * "Causality is a prefix update of the same statistics"; reading notes
+ * sections 2.4-2.6) computes, per batch row b and head h, with L tables of
+ * P Gaussian hyperplanes each (R = 2^P corners v_r in {+1,-1}^P):
+ *
+ *   u^(l)(x)   = tanh(W^(l) x)                                   (P values)
+ *   phi^(l)(x) = softmax_r(beta * u^(l)(x) . v_r)                (R values)
+ *   mass^(l)   = sum_j phi^(l)(K_j),  content^(l) = sum_j phi^(l)(K_j) V_j^T
+ *   O_i        = sum_l phi^(l)(Q_i) content^(l) / sum_l phi^(l)(Q_i) mass^(l)
+ *
+ * The causal variant replaces the sums over all j by inclusive prefix sums
+ * over j <= i (the current key is added before the query reads).
+ * Corner order: v_{r,t} = +1 exactly when bit t of r is set.
+ *
+ * Conventions shared by every entry point
+ *  - Q, K, V, O, dO, dQ, dK, dV are device pointers to contiguous
+ *    [B][H][N][d] arrays of the I/O dtype (RACE_F32 or RACE_BF16), 16-byte
+ *    aligned.  Outputs must not overlap inputs.
+ *  - W is a device pointer to float32 [L][P][d] (table l, hyperplane t,
+ *    column c at (l*P + t)*d + c), shared by every batch row and head.
+ *  - beta is a host float; any finite value is accepted.
+ *  - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; device-side faults surface at the
+ *    caller's next synchronisation.
+ *  - The caller owns and allocates every buffer; the library never
+ *    allocates device memory in these calls.
+ *  - Argument checks run on the host before anything is enqueued.  On any
+ *    error nothing is enqueued and no output is written.
+ *  - Supported: P in [1, 8]; L >= 1 with L * 2^max(P,3) <= 256;
+ *    N >= 1; B*H >= 1; d in {64, 128}.  Other valid shapes return
+ *    RACE_ERR_UNSUPPORTED.
+ */
+#ifndef RACE_ATTN_H
+#define RACE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* race_stream_t;   /* same type as hipStream_t */
+
+typedef enum {
+  RACE_OK = 0,
+  RACE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, non-finite beta, ... */
+  RACE_ERR_UNSUPPORTED = 2,   /* valid arguments, no compiled kernel for them */
+  RACE_ERR_WORKSPACE = 3,     /* state or workspace smaller than required     */
+  RACE_ERR_HIP = 4            /* a HIP runtime call failed; see race_last_error */
+} race_status;
+
+typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype;
+
+typedef struct {
+  int64_t B, H, N, d;
+  int32_t dtype;              /* race_dtype */
+} race_shape;
+
+/* Bytes of the state buffer the forward pass fills and the backward pass
+ * reads.  Non-causal: the bucket bank, content[B*H][LRP][d] float32
+ * followed by mass[B*H][LRP] float32, where LRP = L * 2^max(P,3) rounded up
+ * to a multiple of 32 (rows past L*2^max(P,3) are zero; for P < 3 each table
+ * is widened with zero hyperplanes, which leaves O unchanged).  Causal: the
+ * inclusive bucket bank at each segment end, plus one float32 per token.
+ * Returns 0 for invalid arguments. */
+size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal);
+
+/* Bytes of scratch workspace for the forward (is_bwd = 0) or backward
+ * (is_bwd = 1) call.  Returns 0 for invalid arguments. */
+size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd);
+
+/* Forward pass: O = RACE(Q, K, V; W, beta, P, L, causal).
+ * state (may be NULL when state_bytes is 0) receives the statistics the
+ * backward pass needs; workspace must hold race_attn_workspace_bytes(..., 0). */
+race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W,
+                          float beta, int P, int L, int causal, void* O,
+                          const race_shape* shape, void* state, size_t state_bytes,
+                          void* workspace, size_t workspace_bytes, race_stream_t stream);
+
+/* Backward pass: the exact gradients dQ, dK, dV of sum(O * dO) with W and
+ * beta held fixed (softmax, tanh and projection backward on both sides).
+ * state must be the one written by race_attn_fwd on the same inputs; O may be
+ * NULL (it is recomputed, not read).  workspace must hold
+ * race_attn_workspace_bytes(..., 1). */
+race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W,
+                          float beta, int P, int L, int causal, const void* O,
+                          const void* dO, void* dQ, void* dK, void* dV,
+                          const race_shape* shape, const void* state, size_t state_bytes,
+                          void* workspace, size_t workspace_bytes, race_stream_t stream);
+
+/* Test export: the soft assignments phi^(l)(X) as float32 [B*H][N][L][2^P]
+ * (slides frame "Soft corner assignments make hashing differentiable").
+ * X has the I/O dtype; no workspace. */
+race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L,
+                                  const race_shape* shape, float* phi_out,
+                                  race_stream_t stream);
+
+/* Kernel timing for profiling tools.  While enabled, every kernel that the
+ * calls above launch is bracketed by two HIP events recorded on the same
+ * stream.  race_profile_report waits for the recorded events and writes one
+ * line per kernel name, "name<TAB>launches<TAB>total_ms", NUL-terminated,
+ * into buf (truncated to len bytes); it returns the bytes needed.
+ * race_profile_reset forgets the records.  Events are created by the HIP
+ * runtime on first use and reused; no device memory is allocated. */
+race_status race_profile_enable(int on);
+void race_profile_reset(void);
+size_t race_profile_report(char* buf, size_t len);
+
+/* Human-readable name of a status code (static storage). */
+const char* race_status_string(race_status status);
+
+/* Message of the last error raised on the calling thread ("" if none). */
+const char* race_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RACE_ATTN_H */

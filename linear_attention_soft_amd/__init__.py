@@ -1,0 +1,204 @@
+"""Python binding of the gfx950 RACE attention library (librace_attn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/race_attn.h``.  PyTorch
+provides device memory and the current stream.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RaceError", "lib", "library_path", "race_attn_fwd", "race_attn_bwd", "race_softbucket_debug",
+    "race_attn_state_bytes", "race_attn_workspace_bytes", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "librace_attn.so")
+
+RACE_F32, RACE_BF16 = 0, 1
+EXPORTED_SYMBOLS = ("race_attn_fwd", "race_attn_bwd", "race_attn_state_bytes", "race_attn_workspace_bytes",
+                    "race_softbucket_debug", "race_status_string", "race_last_error", "race_profile_enable",
+                    "race_profile_reset", "race_profile_report")
+
+
+class RaceError(RuntimeError):
+    def __init__(self, status: int, name: str, msg: str):
+        super().__init__(f"{name}: {msg}")
+        self.status = status
+        self.name = name
+
+
+class race_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librace_attn.so (built in place by ``linear_attention_soft_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing; build it with "
+                               f"`python -m linear_attention_soft_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+        sp = ctypes.POINTER(race_shape)
+        L.race_attn_state_bytes.argtypes = [sp, i32, i32, i32]
+        L.race_attn_state_bytes.restype = sz
+        L.race_attn_workspace_bytes.argtypes = [sp, i32, i32, i32, i32]
+        L.race_attn_workspace_bytes.restype = sz
+        L.race_attn_fwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, sp, vp, sz, vp, sz, vp]
+        L.race_attn_fwd.restype = i32
+        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp, sz, vp, sz, vp]
+        L.race_attn_bwd.restype = i32
+        L.race_softbucket_debug.argtypes = [vp, vp, f32, i32, i32, sp, vp, vp]
+        L.race_softbucket_debug.restype = i32
+        L.race_status_string.argtypes = [i32]
+        L.race_status_string.restype = ctypes.c_char_p
+        L.race_last_error.argtypes = []
+        L.race_last_error.restype = ctypes.c_char_p
+        L.race_profile_enable.argtypes = [i32]
+        L.race_profile_enable.restype = i32
+        L.race_profile_reset.argtypes = []
+        L.race_profile_reset.restype = None
+        L.race_profile_report.argtypes = [ctypes.c_char_p, sz]
+        L.race_profile_report.restype = sz
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise RaceError(status, L.race_status_string(status).decode(), L.race_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RACE_F32
+    if t.dtype == torch.bfloat16:
+        return RACE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def make_shape(B, H, N, d, dtype) -> race_shape:
+    code = dtype if isinstance(dtype, int) else (RACE_BF16 if dtype == torch.bfloat16 else RACE_F32)
+    return race_shape(int(B), int(H), int(N), int(d), code)
+
+
+def _shape_of(x: torch.Tensor) -> race_shape:
+    if x.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    return race_shape(B, H, N, d, _dtype_code(x))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def race_attn_state_bytes(shape: race_shape, P: int, L: int, causal: bool) -> int:
+    return int(lib().race_attn_state_bytes(ctypes.byref(shape), P, L, int(causal)))
+
+
+def race_attn_workspace_bytes(shape: race_shape, P: int, L: int, causal: bool, is_bwd: bool) -> int:
+    return int(lib().race_attn_workspace_bytes(ctypes.byref(shape), P, L, int(causal), int(is_bwd)))
+
+
+def _bytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def _buffer(nbytes: int, device, given=None):
+    if given is not None:
+        return given
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, workspace=None, stream=None):
+    """O = RACE(Q, K, V; W, beta, P, L, causal).  Returns (O, state)."""
+    shape = _shape_of(Q)
+    if O is None:
+        O = torch.empty_like(Q)
+    sb = race_attn_state_bytes(shape, P, L, causal)
+    wb = race_attn_workspace_bytes(shape, P, L, causal, False)
+    if sb == 0 or wb == 0:
+        # surface the library's own diagnosis
+        _check(lib().race_attn_fwd(None, None, None, None, float(beta), P, L, int(causal), None,
+                                   ctypes.byref(shape), None, 0, None, 0, None))
+    state = _buffer(sb, Q.device, state)
+    workspace = _buffer(wb, Q.device, workspace)
+    _check(lib().race_attn_fwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                               int(L), int(causal), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"),
+                               _bytes(state), _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
+    return O, state
+
+
+def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK=None, dV=None,
+                  workspace=None, stream=None):
+    """Exact gradients of sum(O * dO).  Returns (dQ, dK, dV)."""
+    shape = _shape_of(Q)
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(V) if dV is None else dV
+    wb = race_attn_workspace_bytes(shape, P, L, causal, True)
+    if wb == 0:
+        _check(lib().race_attn_bwd(None, None, None, None, float(beta), P, L, int(causal), None, None, None, None,
+                                   None, ctypes.byref(shape), None, 0, None, 0, None))
+    workspace = _buffer(wb, Q.device, workspace)
+    _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                               int(L), int(causal), O.data_ptr() if O is not None else None, _dev(dO, "dO"),
+                               _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"), ctypes.byref(shape),
+                               _dev(state, "state"), _bytes(state), _dev(workspace, "workspace"),
+                               _bytes(workspace), _stream(stream)))
+    return dQ, dK, dV
+
+
+def profile_enable(on: bool = True):
+    """Bracket every kernel launch with HIP events on its stream (see race_profile_report)."""
+    lib().race_profile_enable(int(on))
+
+
+def profile_reset():
+    lib().race_profile_reset()
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded since the last reset."""
+    L = lib()
+    n = L.race_profile_report(None, 0)
+    buf = ctypes.create_string_buffer(n + 16)
+    L.race_profile_report(buf, len(buf))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split("\t")
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
+def race_softbucket_debug(X, W, beta, P, L, stream=None):
+    """Soft assignments phi^(l)(X) as float32 [B, H, N, L, 2^P] (test export)."""
+    B, H, N, d = X.shape
+    out = torch.empty((B, H, N, L, 1 << P), dtype=torch.float32, device=X.device)
+    shape = _shape_of(X)
+    _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
+                                       ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
+    return out

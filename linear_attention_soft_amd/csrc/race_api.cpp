@@ -1,0 +1,421 @@
+// C ABI of the RACE attention library: argument checks, size queries, kernel
+// selection and launch.  Every check runs on the host before any work is
+// enqueued; the library allocates no device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/race_attn.h"
+#include "race_causal.hpp"
+#include "race_noncausal.hpp"
+#include "race_registry.hpp"
+
+namespace race {
+// ------------------------------------------------------------------ fixed-order chunk sums
+// bank[bh][lr][c] = sum over chunks of part[bh][chunk][lr][c] (c = d is the mass).
+__global__ void race_bank_finalize(const float* __restrict__ part, int nchunk, int LRP, int D, int BH,
+                                   float* __restrict__ content, float* __restrict__ mass) {
+  const int64_t per = (int64_t)LRP * (D + 1);
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= per * BH) return;
+  const int64_t bh = idx / per, rem = idx % per;
+  const int lr = (int)(rem / (D + 1)), c = (int)(rem % (D + 1));
+  const float* p = part + (size_t)bh * nchunk * per + rem;
+  float s = 0.f;
+  for (int k = 0; k < nchunk; ++k) s += p[(size_t)k * per];
+  if (c < D) content[((size_t)bh * LRP + lr) * D + c] = s;
+  else mass[(size_t)bh * LRP + lr] = s;
+}
+
+}  // namespace race
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// ---- optional kernel timing: HIP events recorded on the launch stream
+struct ProfRec {
+  hipEvent_t start, stop;
+  const char* name;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  hipStream_t s;
+  const char* name;
+  hipEvent_t a = nullptr;
+  ProfScope(hipStream_t st, const char* n) : s(st), name(n) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    a = prof_event();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    hipEvent_t b = prof_event();
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    g_prof_recs.push_back({a, b, name});
+  }
+};
+
+race_status fail(race_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+struct Plan {
+  int dtype = 0;
+  int64_t B = 0, H = 0, N = 0, D = 0, BH = 0;
+  int P = 0, L = 0, PE = 0, LR = 0, LRP = 0;
+  bool causal = false;
+  // non-causal chunking
+  int nchunk = 0;
+  int64_t chunk_tokens = 0;
+  // causal segmentation
+  int nseg = 0;
+  int64_t seg_tokens = 0;
+  const race::KernelSet* ks = nullptr;
+};
+
+size_t elem_size(int dtype) { return dtype == RACE_BF16 ? 2 : 4; }
+
+const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool causal) {
+  int count = 0;
+  const race::KernelSet* sets = dtype == RACE_BF16 ? race::kernel_sets_bf16(&count) : race::kernel_sets_f32(&count);
+  const race::KernelSet* best = nullptr;
+  for (int i = 0; i < count; ++i) {
+    const race::KernelSet& k = sets[i];
+    if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
+    if (causal && !k.causal_fwd) continue;
+    if (!best || k.LRP < best->LRP) best = &k;
+  }
+  return best;
+}
+
+// Tokens per workgroup: about 1024 workgroups over the whole problem
+// (several per compute unit on 256 CUs), at least one 128-token tile each.
+void chunking(int64_t N, int64_t BH, int* nchunk, int64_t* chunk_tokens) {
+  const int64_t tiles = (N + race::TT - 1) / race::TT;
+  int64_t want = (1024 + BH - 1) / BH;
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  int64_t per_tiles = (tiles + want - 1) / want;
+  *chunk_tokens = per_tiles * race::TT;
+  *nchunk = (int)((N + *chunk_tokens - 1) / *chunk_tokens);
+}
+
+race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bool need_kernels) {
+  if (!s) return fail(RACE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->N < 1 || s->d < 1)
+    return fail(RACE_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
+  if (s->dtype != RACE_F32 && s->dtype != RACE_BF16) return fail(RACE_ERR_INVALID_ARG, "dtype must be RACE_F32 or RACE_BF16");
+  if (P < 1 || P > 8) return fail(RACE_ERR_INVALID_ARG, "P must be in [1, 8]");
+  if (L < 1) return fail(RACE_ERR_INVALID_ARG, "L must be >= 1");
+  if (causal != 0 && causal != 1) return fail(RACE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (s->B > (int64_t)1 << 31 || s->H > (int64_t)1 << 31 || s->N > (int64_t)1 << 40 || s->d > 4096)
+    return fail(RACE_ERR_INVALID_ARG, "shape out of range");
+  p->dtype = s->dtype;
+  p->B = s->B; p->H = s->H; p->N = s->N; p->D = s->d; p->BH = s->B * s->H;
+  if (p->BH > 65535) return fail(RACE_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
+  p->P = P; p->L = L; p->PE = P < 3 ? 3 : P;
+  if ((int64_t)L << p->PE > 256) return fail(RACE_ERR_UNSUPPORTED, "L * 2^max(P,3) above 256 is not supported");
+  p->LR = L << p->PE;
+  p->LRP = (p->LR + 31) / 32 * 32;
+  p->causal = causal != 0;
+  if (p->D != 64 && p->D != 128) return fail(RACE_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  if (need_kernels) {
+    p->ks = find_set(p->dtype, (int)p->D, p->PE, p->LRP, p->causal);
+    if (!p->ks) return fail(RACE_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, d, P, L, causal)");
+    p->LRP = p->ks->LRP;
+  }
+  chunking(p->N, p->BH, &p->nchunk, &p->chunk_tokens);
+  race::causal_segmentation(p->N, p->BH, &p->nseg, &p->seg_tokens);
+  return RACE_OK;
+}
+
+// ---- sizes (bytes)
+size_t bank_bytes(const Plan& p) { return (size_t)p.BH * p.LRP * (p.D + 1) * sizeof(float); }
+size_t part_bytes(const Plan& p) { return (size_t)p.BH * p.nchunk * p.LRP * (p.D + 1) * sizeof(float); }
+size_t seg_bank_bytes(const Plan& p) { return (size_t)p.BH * p.nseg * p.LRP * (p.D + 1) * sizeof(float); }
+size_t tok_bytes(const Plan& p) { return (size_t)p.BH * p.N * sizeof(float); }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t state_bytes(const Plan& p) {
+  if (!p.causal) return bank_bytes(p);
+  return align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
+}
+
+size_t workspace_bytes(const Plan& p, bool bwd) {
+  if (!p.causal) {
+    size_t w = align256(part_bytes(p));
+    if (!bwd) w += align256(bank_bytes(p));          // bank when no state buffer is given
+    else w += align256(bank_bytes(p));               // gradient bank dcontent, dmass
+    return w;
+  }
+  if (!bwd) return align256(seg_bank_bytes(p)) + align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
+  // causal backward: per-segment gradient aggregates, their suffix scan, per-token h
+  return align256(seg_bank_bytes(p)) + align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+race_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RACE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return RACE_OK;
+}
+
+void launch_finalize(const float* part, int nchunk, const Plan& p, float* content, float* mass, hipStream_t st) {
+  const int64_t total = p.BH * (int64_t)p.LRP * (p.D + 1);
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(race::race_bank_finalize, dim3((unsigned)blocks), dim3(threads), 0, st, part, nchunk,
+                     p.LRP, (int)p.D, (int)p.BH, content, mass);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal) {
+  Plan p;
+  if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
+  const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
+  if (ks) p.LRP = ks->LRP;
+  return state_bytes(p);
+}
+
+size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd) {
+  Plan p;
+  if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
+  const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
+  if (ks) p.LRP = ks->LRP;
+  return workspace_bytes(p, is_bwd != 0);
+}
+
+race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
+                          int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
+                          void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
+  g_last_error.clear();
+  Plan p;
+  race_status st = make_plan(shape, P, L, causal, &p, true);
+  if (st != RACE_OK) return st;
+  if (!Q || !K || !V || !W || !O) return fail(RACE_ERR_INVALID_ARG, "Q, K, V, W and O must be non-NULL");
+  if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(W) ||
+      (state && !aligned16(state)) || (workspace && !aligned16(workspace)))
+    return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) || overlaps(O, tbytes, V, tbytes))
+    return fail(RACE_ERR_INVALID_ARG, "O overlaps an input");
+  const size_t need_ws = workspace_bytes(p, false);
+  if (!workspace || workspace_bytes_in < need_ws)
+    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+  const size_t need_state = state_bytes(p);
+  if (state && state_bytes_in < need_state)
+    return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
+  if (state && (overlaps(state, need_state, O, tbytes) || overlaps(state, need_state, workspace, need_ws)))
+    return fail(RACE_ERR_INVALID_ARG, "state overlaps O or the workspace");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  if (p.causal) return race::causal_forward(*p.ks, Q, K, V, W, beta, p.L, p.P, p.N, (int)p.BH, p.LRP, (int)p.D,
+                                            p.nseg, p.seg_tokens, O, state, ws, s, &g_last_error);
+
+  float* part = reinterpret_cast<float*>(ws);
+  float* bank = state ? static_cast<float*>(state) : reinterpret_cast<float*>(ws + align256(part_bytes(p)));
+  float* content = bank;
+  float* mass = bank + (size_t)p.BH * p.LRP * p.D;
+
+  race::NCArgs a{};
+  a.X = K; a.Y = V; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.part = part;
+  {
+    ProfScope ps(s, "race_bucket_reduce");
+    p.ks->reduce(a, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bucket_reduce")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nchunk, p, content, mass, s);
+  }
+  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
+  race::NCArgs r{};
+  r.X = Q; r.out0 = O; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
+  r.st_content = content; r.st_mass = mass; r.chunk_tokens = p.chunk_tokens; r.nchunk = p.nchunk;
+  {
+    ProfScope ps(s, "race_readout_norm");
+    p.ks->readout(r, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  return check_launch("race_readout_norm");
+}
+
+race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
+                          int causal, const void* O, const void* dO, void* dQ, void* dK, void* dV,
+                          const race_shape* shape, const void* state, size_t state_bytes_in, void* workspace,
+                          size_t workspace_bytes_in, race_stream_t stream) {
+  (void)O;
+  g_last_error.clear();
+  Plan p;
+  race_status st = make_plan(shape, P, L, causal, &p, true);
+  if (st != RACE_OK) return st;
+  if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV)
+    return fail(RACE_ERR_INVALID_ARG, "Q, K, V, W, dO, dQ, dK and dV must be non-NULL");
+  if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
+  if (!state) return fail(RACE_ERR_INVALID_ARG, "state from race_attn_fwd is required");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || !aligned16(state) || (workspace && !aligned16(workspace)))
+    return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const void* ins[] = {Q, K, V, dO};
+  void* outs[] = {dQ, dK, dV};
+  for (void* o : outs) {
+    for (const void* i : ins)
+      if (overlaps(o, tbytes, i, tbytes)) return fail(RACE_ERR_INVALID_ARG, "an output overlaps an input");
+    for (void* o2 : outs)
+      if (o2 != o && overlaps(o, tbytes, o2, tbytes)) return fail(RACE_ERR_INVALID_ARG, "outputs overlap");
+  }
+  const size_t need_state = state_bytes(p);
+  if (state_bytes_in < need_state)
+    return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
+  const size_t need_ws = workspace_bytes(p, true);
+  if (!workspace || workspace_bytes_in < need_ws)
+    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  if (p.causal)
+    return race::causal_backward(*p.ks, Q, K, V, W, beta, p.L, p.P, p.N, (int)p.BH, p.LRP, (int)p.D, p.nseg,
+                                 p.seg_tokens, dO, dQ, dK, dV, state, ws, s, &g_last_error);
+
+  const float* content = static_cast<const float*>(state);
+  const float* mass = content + (size_t)p.BH * p.LRP * p.D;
+  float* part = reinterpret_cast<float*>(ws);
+  float* dbank = reinterpret_cast<float*>(ws + align256(part_bytes(p)));
+  float* dcontent = dbank;
+  float* dmass = dbank + (size_t)p.BH * p.LRP * p.D;
+
+  race::NCArgs a{};
+  a.X = Q; a.Y = dO; a.out0 = dQ; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.st_content = content; a.st_mass = mass; a.part = part;
+  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
+  {
+    ProfScope ps(s, "race_bwd_q");
+    p.ks->bwd_q(a, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bwd_q")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nchunk, p, dcontent, dmass, s);
+  }
+  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
+  race::NCArgs b{};
+  b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = W; b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
+  b.st_content = dcontent; b.st_mass = dmass; b.chunk_tokens = p.chunk_tokens; b.nchunk = p.nchunk;
+  {
+    ProfScope ps(s, "race_bwd_kv");
+    p.ks->bwd_kv(b, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  return check_launch("race_bwd_kv");
+}
+
+race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L, const race_shape* shape,
+                                  float* phi_out, race_stream_t stream) {
+  g_last_error.clear();
+  Plan p;
+  race_status st = make_plan(shape, P, L, 0, &p, true);
+  if (st != RACE_OK) return st;
+  if (P < 3) return fail(RACE_ERR_UNSUPPORTED, "the soft-assignment export needs P >= 3");
+  if (!X || !W || !phi_out) return fail(RACE_ERR_INVALID_ARG, "X, W and phi_out must be non-NULL");
+  if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
+  if (!aligned16(X) || !aligned16(W) || !aligned16(phi_out)) return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  int64_t blocks = (p.N + race::TT - 1) / race::TT;
+  if (blocks > 4096) blocks = 4096;
+  p.ks->softbucket_dbg(X, W, beta, p.L, p.P, p.N, phi_out, dim3((unsigned)blocks, (unsigned)p.BH),
+                       reinterpret_cast<hipStream_t>(stream));
+  return check_launch("race_softbucket_dbg");
+}
+
+const char* race_status_string(race_status status) {
+  switch (status) {
+    case RACE_OK: return "RACE_OK";
+    case RACE_ERR_INVALID_ARG: return "RACE_ERR_INVALID_ARG";
+    case RACE_ERR_UNSUPPORTED: return "RACE_ERR_UNSUPPORTED";
+    case RACE_ERR_WORKSPACE: return "RACE_ERR_WORKSPACE";
+    case RACE_ERR_HIP: return "RACE_ERR_HIP";
+  }
+  return "RACE_ERR_UNKNOWN";
+}
+
+const char* race_last_error(void) { return g_last_error.c_str(); }
+
+race_status race_profile_enable(int on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = on != 0;
+  return RACE_OK;
+}
+
+void race_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+}
+
+size_t race_profile_report(char* buf, size_t len) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  std::map<std::string, std::pair<int, double>> agg;
+  for (auto& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess) continue;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) continue;
+    auto& a = agg[r.name];
+    a.first += 1;
+    a.second += ms;
+  }
+  std::string out;
+  for (auto& kv : agg) {
+    char line[256];
+    std::snprintf(line, sizeof(line), "%s\t%d\t%.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (buf && len) {
+    std::size_t n = out.size() < len - 1 ? out.size() : len - 1;
+    std::memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return out.size() + 1;
+}
+
+}  // extern "C"

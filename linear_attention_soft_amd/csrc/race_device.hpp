@@ -1,0 +1,448 @@
+// Device building blocks of the gfx950 RACE attention kernels.
+//
+// Lane layouts (CDNA4, 64-wide waves).  Every contraction runs on the
+// 32x32 MFMA: v_mfma_f32_32x32x16_bf16 for bf16 I/O and eight
+// v_mfma_f32_32x32x2_f32 for float32 I/O.  A "K16 step" contracts 16
+// logical k indices; lane l = 32*h + n holds 8 of them for row/column n and
+// half h.  The accumulator of a 32x32 tile puts element (m, n) in lane
+// n + 32*((m/4)%2), register (m%4) + 4*(m/8).
+//
+// Token-major vectors ("TLAYOUT"): a per-token vector x of length M
+// (M a multiple of 32) is held by the 64 lanes of a wave for 32 tokens:
+// lane (tok, h) owns x[32*a + 8*j + 4*h + k] in register 16*a + 4*j + k.
+// This is exactly the accumulator layout of a C^T[m][tok] tile, and read
+// eight registers at a time it is a K16-step B operand whose logical index
+// (h, i) of step q is  kmap(q, h, i) = 16*q + 8*(i/4) + 4*h + (i%4).
+// Constant A operands that meet such a B operand are built with the same
+// kmap, so no data moves between the MFMA that produces a TLAYOUT vector and
+// the MFMA that consumes it.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace race {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ constexpr int kmap(int q, int h, int i) {
+  return 16 * q + 8 * (i >> 2) + 4 * h + (i & 3);
+}
+
+// ---------------------------------------------------------------- MFMA engines
+template <typename T> struct Eng;
+
+template <> struct Eng<bf16> {
+  using frag = bf16x8;          // 8 bf16 per lane: one K16 step
+  using vec4 = bf16x4;
+  static constexpr int NSPLIT = 2;   // float operands are split hi + lo
+  static constexpr int HPT = 8;      // hyperplanes per projection tile (hi and lo rows)
+  __device__ __forceinline__ static void mma(const frag& a, const frag& b, f32x16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag pack(const float* v) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)v[i];
+    return f;
+  }
+  __device__ __forceinline__ static void split(const float* v, frag& hi, frag& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16 x = (bf16)v[i];
+      hi[i] = x;
+      lo[i] = (bf16)(v[i] - (float)x);
+    }
+  }
+  __device__ __forceinline__ static float round(float x) { return (float)(bf16)x; }
+  __device__ __forceinline__ static frag ones() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)1.0f;
+    return f;
+  }
+  __device__ __forceinline__ static frag zero() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)0.0f;
+    return f;
+  }
+};
+
+template <> struct Eng<float> {
+  using frag = f32x8;           // 8 floats per lane: one K16 step = 8 MFMAs
+  using vec4 = f32x4;
+  static constexpr int NSPLIT = 1;
+  static constexpr int HPT = 16;
+  __device__ __forceinline__ static void mma(const frag& a, const frag& b, f32x16& c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag pack(const float* v) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = v[i];
+    return f;
+  }
+  __device__ __forceinline__ static void split(const float* v, frag& hi, frag& lo) {
+    hi = pack(v);
+    lo = hi;
+  }
+  __device__ __forceinline__ static float round(float x) { return x; }
+  __device__ __forceinline__ static frag ones() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 1.0f;
+    return f;
+  }
+  __device__ __forceinline__ static frag zero() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+    return f;
+  }
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// ---------------------------------------------------------------- elementwise math
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh for any finite x: t = exp(-2|x|) in (0, 1], tanh|x| = (1 - t)/(1 + t).
+__device__ __forceinline__ float tanh_f(float x) {
+  float e = __expf(-2.f * fabsf(x));
+  float t = (1.f - e) * rcp(1.f + e);
+  return copysignf(t, x);
+}
+
+// sigma(z) and sigma(-z) without overflow for any finite z.
+__device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
+  float e = __expf(-fabsf(z));
+  float p = rcp(1.f + e);   // sigma(|z|)
+  float q = e * p;          // sigma(-|z|)
+  bool pos = z >= 0.f;
+  sp = pos ? p : q;
+  sm = pos ? q : p;
+}
+
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// ---------------------------------------------------------------- geometry
+// Compile-time geometry of one kernel instance.
+//   D     head dim (multiple of 32)
+//   PE    hyperplanes per table used in-kernel, max(P, 3)
+//   LRP   bucket rows, L * 2^PE rounded up to a multiple of 32
+template <typename T, int D_, int PE_, int LRP_>
+struct Geo {
+  static constexpr int D = D_;
+  static constexpr int PE = PE_;
+  static constexpr int R = 1 << PE_;
+  static constexpr int LRP = LRP_;
+  static constexpr int LMAX = LRP_ / (1 << PE_) > 0 ? LRP_ / (1 << PE_) : 1;  // table slots
+  static constexpr int NHP = LMAX * PE_;                       // hyperplane slots
+  static constexpr int HPT = Eng<T>::HPT;
+  static constexpr int NPT = cdiv(NHP, HPT);                   // projection tiles
+  static constexpr int KD = D_ / 16;                           // K16 steps over d
+  static constexpr int CT = D_ / 32;                           // 32-column tiles of d
+  static constexpr int AT = LRP_ / 32;                         // 32-row tiles of buckets
+  static constexpr int KL = LRP_ / 16;                         // K16 steps over buckets
+  static constexpr int NE = (Eng<T>::NSPLIT == 2 ? 3 : 1) * NHP; // dX contraction entries
+  static constexpr int NQS = cdiv(NE, 16);                     // K16 steps of the dX MFMA
+  static_assert(D_ % 32 == 0, "d must be a multiple of 32");
+  static_assert(LRP_ % 32 == 0, "LRP must be a multiple of 32");
+  static_assert(PE_ >= 3 && PE_ <= 8, "3 <= PE <= 8");
+  static_assert((1 << PE_) <= LRP_, "R must fit in LRP");
+};
+
+// ---------------------------------------------------------------- constant operands
+// Projection A operand: rows are hyperplane "slots" (bf16: 8 hi rows then 8 lo
+// rows per tile; f32: 16 rows), duplicated in both row halves so every lane
+// ends with all pre-activations of its token; columns follow the plain map
+// c = 16*q + 8*h + i of the token's row loads.
+template <typename T, class G>
+__device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
+                                 typename Eng<T>::frag* __restrict__ Wf) {
+  using E = Eng<T>;
+  for (int idx = threadIdx.x; idx < G::NPT * G::KD * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int q = (idx >> 6) % G::KD;
+    const int pt = (idx >> 6) / G::KD;
+    const int row = lane & 31, h = lane >> 5;
+    const int rho = 4 * (row >> 3) + (row & 3);
+    int hp, part;
+    if (E::NSPLIT == 2) { hp = 8 * pt + (rho & 7); part = rho >> 3; }
+    else                { hp = 16 * pt + rho;      part = 0; }
+    const int l = hp / G::PE, t = hp % G::PE;
+    const bool ok = (hp < G::NHP) && (l < L) && (t < P);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ok ? W[(size_t)(l * P + t) * G::D + 16 * q + 8 * h + i] : 0.f;
+    typename E::frag hi, lo;
+    E::split(v, hi, lo);
+    Wf[idx] = part ? lo : hi;
+  }
+}
+
+// dX A operand: W^T[c][e] for the contraction dX = dPre . W.  bf16 entries e
+// cover (hp, W_hi, dPre_hi), (hp, W_hi, dPre_lo), (hp, W_lo, dPre_hi).
+template <typename T, class G>
+__device__ void build_wt_frags(const float* __restrict__ W, int L, int P,
+                               typename Eng<T>::frag* __restrict__ WTf) {
+  using E = Eng<T>;
+  for (int idx = threadIdx.x; idx < G::CT * G::NQS * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int qs = (idx >> 6) % G::NQS;
+    const int ct = (idx >> 6) / G::NQS;
+    const int c = 32 * ct + (lane & 31), h = lane >> 5;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 16 * qs + 8 * h + i;
+      float w = 0.f;
+      if (e < G::NE) {
+        const int hp = e % G::NHP, which = e / G::NHP;
+        const int l = hp / G::PE, t = hp % G::PE;
+        if (l < L && t < P) {
+          const float x = W[(size_t)(l * P + t) * G::D + c];
+          const float xh = E::round(x);
+          w = (E::NSPLIT == 2 && which == 2) ? (x - xh) : (E::NSPLIT == 2 ? xh : x);
+        }
+      }
+      v[i] = w;
+    }
+    WTf[idx] = E::pack(v);
+  }
+}
+
+// ---------------------------------------------------------------- per-token front end
+// Load the B operand of the projection for token row `x` (nullptr -> zeros).
+template <typename T, class G>
+__device__ __forceinline__ void load_row_frags(const T* __restrict__ x, typename Eng<T>::frag (&xf)[G::KD]) {
+  using E = Eng<T>;
+  const int h = lane_id() >> 5;
+  if (x) {
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) xf[q] = *reinterpret_cast<const typename E::frag*>(x + 16 * q + 8 * h);
+  } else {
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) xf[q] = E::zero();
+  }
+}
+
+// pre[hp] = W_hp . x for every hyperplane slot of the lane's token.
+template <typename T, class G>
+__device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict__ Wf,
+                                        const typename Eng<T>::frag (&xf)[G::KD],
+                                        float (&pre)[G::NHP]) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+#pragma unroll
+  for (int pt = 0; pt < G::NPT; ++pt) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) E::mma(Wf[(pt * G::KD + q) * 64 + lane], xf[q], acc);
+    if (E::NSPLIT == 2) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        if (8 * pt + v < G::NHP) pre[8 * pt + v] = acc[v] + acc[v + 8];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (16 * pt + v < G::NHP) pre[16 * pt + v] = acc[v];
+    }
+  }
+}
+
+// Soft corner assignments in TLAYOUT (slides frame "Soft corner assignments
+// make hashing differentiable"; product-of-sigmoids form, reading notes
+// section 2.4): phi_r = prod_t sigma(2 beta u_t v_{r,t}), u = tanh(pre).
+// Lane half h owns the corners whose bit 2 equals h.  Rows of tables >= L
+// and padding rows are 0.
+template <class G>
+__device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float beta2, int L,
+                                            float (&u)[G::NHP], float (&phi)[G::LRP / 2]) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int hp = 0; hp < G::NHP; ++hp) u[hp] = tanh_f(pre[hp]);
+#pragma unroll
+  for (int l = 0; l < G::LMAX; ++l) {
+    float sp[G::PE], sm[G::PE];
+#pragma unroll
+    for (int t = 0; t < G::PE; ++t) sigmoid_pair(beta2 * u[l * G::PE + t], sp[t], sm[t]);
+    const float f2 = h ? sp[2] : sm[2];
+    float g[4];
+    g[0] = sm[0] * sm[1] * f2;
+    g[1] = sp[0] * sm[1] * f2;
+    g[2] = sm[0] * sp[1] * f2;
+    g[3] = sp[0] * sp[1] * f2;
+    constexpr int NH = 1 << (G::PE - 3);
+    float hi[NH];
+    hi[0] = 1.f;
+#pragma unroll
+    for (int t = 3; t < G::PE; ++t) {
+      constexpr int dummy = 0; (void)dummy;
+      const int half = 1 << (t - 3);
+#pragma unroll
+      for (int x = 0; x < half; ++x) {
+        hi[x + half] = hi[x] * sp[t];
+        hi[x] = hi[x] * sm[t];
+      }
+    }
+    const bool live = l < L;
+#pragma unroll
+    for (int a = 0; a < G::AT; ++a) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        if (lr0 / G::R == l) {
+          const int r0 = lr0 % G::R;
+          phi[16 * a + v] = live ? g[r0 & 3] * hi[r0 >> 3] : 0.f;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < G::AT; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if ((32 * a + 8 * (v >> 2) + (v & 3)) / G::R >= G::LMAX) phi[16 * a + v] = 0.f;
+}
+
+// B operand of K16 step q from a TLAYOUT vector held in registers.
+template <typename T, int M>
+__device__ __forceinline__ typename Eng<T>::frag tl_frag(const float (&x)[M / 2], int q) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[8 * q + i];
+  return Eng<T>::pack(v);
+}
+
+template <typename T, int M>
+__device__ __forceinline__ void tl_frag_split(const float (&x)[M / 2], int q,
+                                              typename Eng<T>::frag& hi, typename Eng<T>::frag& lo) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[8 * q + i];
+  Eng<T>::split(v, hi, lo);
+}
+
+// Backward through softmax, beta, corners and tanh for one token (TLAYOUT).
+// dLambda = phi * (dphi - sum_r phi dphi) per table; dU_t = beta sum_r dLambda_r v_{r,t};
+// dPre = dU * (1 - u^2).  Both lane halves end with every dPre value.
+template <class G>
+__device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], const float (&dphi)[G::LRP / 2],
+                                                const float (&u)[G::NHP], float beta,
+                                                float (&dpre)[G::NHP]) {
+  const int h = lane_id() >> 5;
+  const float sgn2 = h ? 1.f : -1.f;
+#pragma unroll
+  for (int l = 0; l < G::LMAX; ++l) {
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < G::AT; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        if (lr0 / G::R == l) s += phi[16 * a + v] * dphi[16 * a + v];
+      }
+    s += xor32(s);
+    float du[G::PE];
+#pragma unroll
+    for (int t = 0; t < G::PE; ++t) du[t] = 0.f;
+#pragma unroll
+    for (int a = 0; a < G::AT; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        if (lr0 / G::R == l) {
+          const int r0 = lr0 % G::R;
+          const float dl = phi[16 * a + v] * (dphi[16 * a + v] - s);
+#pragma unroll
+          for (int t = 0; t < G::PE; ++t) {
+            if (t == 2) du[t] += sgn2 * dl;
+            else du[t] += ((r0 >> t) & 1) ? dl : -dl;
+          }
+        }
+      }
+#pragma unroll
+    for (int t = 0; t < G::PE; ++t) {
+      const float d = du[t] + xor32(du[t]);
+      const float uu = u[l * G::PE + t];
+      dpre[l * G::PE + t] = beta * d * (1.f - uu * uu);
+    }
+  }
+}
+
+// B operand of the dX contraction, step qs (entries e = 16 qs + 8 h + i).
+template <typename T, class G>
+__device__ __forceinline__ typename Eng<T>::frag dpre_frag(const float (&dpre)[G::NHP], int qs) {
+  using E = Eng<T>;
+  const int h = lane_id() >> 5;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float a = 0.f, b = 0.f;   // values for h = 0 and h = 1
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int e = 16 * qs + 8 * hh + i;
+      float w = 0.f;
+      if (e < G::NE) {
+        const int hp = e % G::NHP, which = e / G::NHP;
+        const float x = dpre[hp];
+        if (E::NSPLIT == 2) {
+          const float xh = E::round(x);
+          w = (which == 1) ? (x - xh) : xh;
+        } else {
+          w = x;
+        }
+      }
+      if (hh == 0) a = w; else b = w;
+    }
+    v[i] = h ? b : a;
+  }
+  return E::pack(v);
+}
+
+// Store a TLAYOUT row of D values (4 consecutive columns per register group).
+template <typename T, int D>
+__device__ __forceinline__ void store_tl_row(T* __restrict__ row, const float (&x)[D / 2]) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typename Eng<T>::vec4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (T)x[16 * mt + 4 * j + k];
+      *reinterpret_cast<typename Eng<T>::vec4*>(row + 32 * mt + 8 * j + 4 * h) = w;
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_tl_row(const T* __restrict__ row, float (&x)[D / 2]) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typename Eng<T>::vec4 w = *reinterpret_cast<const typename Eng<T>::vec4*>(row + 32 * mt + 8 * j + 4 * h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[16 * mt + 4 * j + k] = (float)w[k];
+    }
+}
+
+}  // namespace race

@@ -1,0 +1,70 @@
+// Launchers of one kernel instance; included by the per-dtype instance files.
+#pragma once
+#include "race_noncausal.hpp"
+#include "race_registry.hpp"
+
+namespace race {
+
+// Soft assignments of token rows written out as float32 [BH][N][L][R]
+// (a test export of the fused front end every kernel uses).
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, const float* W, float beta,
+                                                           int L, int P, int64_t N, float* out) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  build_proj_frags<T, G>(W, L, P, Wf);
+  __syncthreads();
+  const int bh = blockIdx.y;
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+  const T* X = static_cast<const T*>(Xv) + (size_t)bh * N * G::D;
+  const int LR = L << G::PE;
+  for (int64_t base = (int64_t)blockIdx.x * TT + 32 * w; base < N; base += (int64_t)gridDim.x * TT) {
+    const int64_t tok = base + n;
+    const bool valid = tok < N;
+    frag xf[G::KD];
+    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    project<T, G>(Wf, xf, pre);
+    soft_assign<G>(pre, 2.f * beta, L, u, phi);
+    if (valid) {
+#pragma unroll
+      for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (lr < LR) out[((size_t)bh * N + tok) * LR + lr] = phi[16 * at + v];
+        }
+    }
+  }
+}
+
+template <typename T, int D, int PE, int LRP>
+struct Inst {
+  using G = Geo<T, D, PE, LRP>;
+  static void reduce(const NCArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_bucket_reduce<T, G>), g, dim3(256), 0, s, a);
+  }
+  static void readout(const NCArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_readout_norm<T, G>), g, dim3(256), 0, s, a);
+  }
+  static void bwd_q(const NCArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_bwd_q<T, G>), g, dim3(256), 0, s, a);
+  }
+  static void bwd_kv(const NCArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_bwd_kv<T, G>), g, dim3(256), 0, s, a);
+  }
+  static void dbg(const void* X, const float* W, float beta, int L, int P, int64_t N, float* out,
+                  dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, out);
+  }
+  static KernelSet set(int dtype) {
+    KernelSet k{};
+    k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP;
+    k.reduce = reduce; k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv;
+    k.softbucket_dbg = dbg;
+    return k;
+  }
+};
+
+}  // namespace race

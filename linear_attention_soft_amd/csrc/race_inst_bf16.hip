@@ -1,0 +1,14 @@
+// Compiled kernel instances for bf16 I/O.
+#include "race_inst.hpp"
+
+namespace race {
+const KernelSet* kernel_sets_bf16(int* count) {
+  static const KernelSet sets[] = {
+      Inst<bf16, 64, 3, 32>::set(1),
+      Inst<bf16, 64, 4, 64>::set(1),
+      Inst<bf16, 128, 4, 32>::set(1),
+  };
+  *count = (int)(sizeof(sets) / sizeof(sets[0]));
+  return sets;
+}
+}  // namespace race

@@ -1,0 +1,513 @@
+// Non-causal RACE attention kernels for gfx950.
+//
+//   race_bucket_reduce  content^(l) = Phi_K^(l)^T V, mass^(l) = Phi_K^(l)^T 1
+//                       (slides frame "Each bucket stores mass and a weighted
+//                       value sum"): per-workgroup partial banks, then a
+//                       fixed-order sum over workgroups (deterministic).
+//   race_readout_norm   O = sum_l Phi_Q content / sum_l Phi_Q mass (slides
+//                       frame "Normalize after combining the tables").
+//   race_bwd_q          recompute O; g = dO/Den, h = -(dO.O)/Den;
+//                       dPhi_Q = content g + mass h -> dQ; reduce
+//                       dcontent = Phi_Q^T g, dmass = Phi_Q^T h.
+//   race_bwd_kv         dV = sum_l Phi_K dcontent; dPhi_K = dcontent V + dmass -> dK.
+//
+// Every kernel fuses the soft bucketing of its token rows (projection on
+// MFMA, tanh and sigmoids on VALU); Phi never reaches HBM.  Bucket banks are
+// float32.  With bf16 I/O the float32 operands of each contraction (bucket
+// bank, projection rows, gradients that may cancel) are split into bf16
+// hi + lo parts; per-token soft assignments are rounded to bf16 once and the
+// same rounded values feed both numerator and denominator.
+#pragma once
+#include "race_device.hpp"
+
+namespace race {
+
+struct NCArgs {
+  const void* X;            // Q (readout, bwd_q) or K (reduce, bwd_kv)
+  const void* Y;            // V (reduce, bwd_kv) or dO (bwd_q)
+  void* out0;               // O (readout), dQ (bwd_q), dV (bwd_kv)
+  void* out1;               // dK (bwd_kv)
+  const float* W;           // [L][P][d]
+  const float* st_content;  // [BH][LRP][d]   bucket (or gradient) bank
+  const float* st_mass;     // [BH][LRP]
+  float* part;              // [BH][nchunk][LRP][d+1] partial banks
+  float beta;
+  int L, P;
+  int64_t N;
+  int64_t chunk_tokens;     // tokens per workgroup, multiple of 128
+  int nchunk;
+};
+
+constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
+
+// Row padding (elements) of LDS staging tiles: keeps 16-byte (bf16) and
+// 32-byte (float32) fragment rows aligned and shifts rows across banks.
+template <typename T> struct Pad { static constexpr int v = 8; };
+
+// A operand of the readout: rows = value columns c (CT tiles) plus one tile
+// whose every row is the mass, so the denominator comes out of the same MFMA
+// with the same rounded Phi_Q.  k over buckets follows kmap.
+template <typename T, class G>
+__device__ void build_readout_frags(const float* __restrict__ content, const float* __restrict__ mass,
+                                    typename Eng<T>::frag* __restrict__ RF) {
+  using E = Eng<T>;
+  constexpr int NS = E::NSPLIT;
+  for (int idx = threadIdx.x; idx < (G::CT + 1) * G::KL * NS * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int sp = (idx >> 6) % NS;
+    const int q = ((idx >> 6) / NS) % G::KL;
+    const int mt = ((idx >> 6) / NS) / G::KL;
+    const int c = 32 * mt + (lane & 31), h = lane >> 5;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lr = kmap(q, h, i);
+      v[i] = (mt < G::CT) ? content[(size_t)lr * G::D + c] : mass[lr];
+    }
+    typename E::frag hi, lo;
+    E::split(v, hi, lo);
+    RF[idx] = sp ? lo : hi;
+  }
+}
+
+// A operand bank[lr][c] with rows = buckets and k over columns c, either by
+// kmap (B operand from a TLAYOUT register vector) or by the plain row map
+// c = 16 q + 8 h + i (B operand loaded straight from a token row).
+template <typename T, class G, bool KMAP>
+__device__ void build_bank_rows_frags(const float* __restrict__ content, typename Eng<T>::frag* __restrict__ DF) {
+  using E = Eng<T>;
+  constexpr int NS = E::NSPLIT;
+  for (int idx = threadIdx.x; idx < G::AT * G::KD * NS * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int sp = (idx >> 6) % NS;
+    const int q = ((idx >> 6) / NS) % G::KD;
+    const int at = ((idx >> 6) / NS) / G::KD;
+    const int lr = 32 * at + (lane & 31), h = lane >> 5;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = KMAP ? kmap(q, h, i) : 16 * q + 8 * h + i;
+      v[i] = content[(size_t)lr * G::D + c];
+    }
+    typename E::frag hi, lo;
+    E::split(v, hi, lo);
+    DF[idx] = sp ? lo : hi;
+  }
+}
+
+// A operand bank^T[c][lr] (rows = columns c, k over buckets by kmap), no mass tile.
+template <typename T, class G>
+__device__ void build_bank_cols_frags(const float* __restrict__ content, typename Eng<T>::frag* __restrict__ VF) {
+  using E = Eng<T>;
+  constexpr int NS = E::NSPLIT;
+  for (int idx = threadIdx.x; idx < G::CT * G::KL * NS * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int sp = (idx >> 6) % NS;
+    const int q = ((idx >> 6) / NS) % G::KL;
+    const int mt = ((idx >> 6) / NS) / G::KL;
+    const int c = 32 * mt + (lane & 31), h = lane >> 5;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = content[(size_t)kmap(q, h, i) * G::D + c];
+    typename E::frag hi, lo;
+    E::split(v, hi, lo);
+    VF[idx] = sp ? lo : hi;
+  }
+}
+
+// Readout of one token (TLAYOUT): acc[mt] = bank^T[mt] . Phi^T, acc[CT] = Den.
+template <typename T, class G>
+__device__ __forceinline__ void readout_mma(const typename Eng<T>::frag* __restrict__ RF,
+                                            const float (&phi)[G::LRP / 2], f32x16 (&acc)[G::CT + 1]) {
+  using E = Eng<T>;
+  constexpr int NS = E::NSPLIT;
+  const int lane = lane_id();
+#pragma unroll
+  for (int mt = 0; mt <= G::CT; ++mt) acc[mt] = zero16();
+#pragma unroll
+  for (int q = 0; q < G::KL; ++q) {
+    const typename E::frag b = tl_frag<T, G::LRP>(phi, q);
+#pragma unroll
+    for (int mt = 0; mt <= G::CT; ++mt)
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) E::mma(RF[((mt * G::KL + q) * NS + sp) * 64 + lane], b, acc[mt]);
+  }
+}
+
+// dX = dPre . W for one token (TLAYOUT over columns).
+template <typename T, class G>
+__device__ __forceinline__ void dx_mma(const typename Eng<T>::frag* __restrict__ WTf,
+                                       const float (&dpre)[G::NHP], float (&dx)[G::D / 2]) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+  typename E::frag bq[G::NQS];
+#pragma unroll
+  for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dpre, qs);
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int qs = 0; qs < G::NQS; ++qs) E::mma(WTf[(ct * G::NQS + qs) * 64 + lane], bq[qs], acc);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dx[16 * ct + v] = acc[v];
+  }
+}
+
+// Cooperative bucket reduction of one 128-token tile: acc[j] (tile w + 4 j of
+// the (AT) x (CT + 1) grid) += PhiT[lr][tok] * [B | extra][tok][c].
+// The extra column tile is all ones (mass) or hs[tok] (gradient mass).
+template <typename T, class G, int TTP, int BSP, int NTW>
+__device__ __forceinline__ void reduce_tile_mma(const T* __restrict__ PhiT, const T* __restrict__ Bs,
+                                                const float* __restrict__ hs, f32x16 (&acc)[NTW]) {
+  using E = Eng<T>;
+  constexpr int NTILE = G::AT * (G::CT + 1);
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int tidx = w + 4 * j;
+    if (tidx < NTILE) {
+      const int at = tidx / (G::CT + 1), ct = tidx % (G::CT + 1);
+#pragma unroll
+      for (int s = 0; s < TT / 16; ++s) {
+        const typename E::frag af =
+            *reinterpret_cast<const typename E::frag*>(PhiT + (32 * at + n) * TTP + 16 * s + 8 * h);
+        typename E::frag bf;
+        if (ct < G::CT) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bf[i] = Bs[(16 * s + 8 * h + i) * BSP + 32 * ct + n];
+        } else if (hs) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bf[i] = (T)hs[16 * s + 8 * h + i];
+        } else {
+          bf = E::ones();
+        }
+        E::mma(af, bf, acc[j]);
+      }
+    }
+  }
+}
+
+template <typename T, class G, int NTW>
+__device__ __forceinline__ void write_partials(float* __restrict__ part, const f32x16 (&acc)[NTW]) {
+  constexpr int NTILE = G::AT * (G::CT + 1);
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int tidx = w + 4 * j;
+    if (tidx < NTILE) {
+      const int at = tidx / (G::CT + 1), ct = tidx % (G::CT + 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (ct < G::CT) part[(size_t)lr * (G::D + 1) + 32 * ct + n] = acc[j][v];
+        else if (n == 0) part[(size_t)lr * (G::D + 1) + G::D] = acc[j][v];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ race_bucket_reduce
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int TTP = TT + Pad<T>::v;
+  constexpr int BSP = G::D + Pad<T>::v;
+  constexpr int NTW = cdiv(G::AT * (G::CT + 1), 4);
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ T PhiT[G::LRP * TTP];
+  __shared__ T Bs[TT * BSP];
+
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  __syncthreads();
+
+  const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
+  const T* Y = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
+  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
+  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const float beta2 = 2.f * a.beta;
+
+  f32x16 acc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) acc[j] = zero16();
+
+  for (int64_t base = t_begin; base < t_end; base += TT) {
+    const int tl = 32 * w + n;
+    const int64_t tok = base + tl;
+    const bool valid = tok < t_end;
+    frag xf[G::KD];
+    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    project<T, G>(Wf, xf, pre);
+    soft_assign<G>(pre, beta2, a.L, u, phi);
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        PhiT[lr * TTP + tl] = valid ? (T)phi[16 * at + v] : (T)0.f;
+      }
+    // value rows of the wave's 32 tokens, 16 bytes per lane per step
+    constexpr int CPR = G::D * (int)sizeof(T) / 16;      // 16-byte chunks per row
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int flat = it * 64 + lane;
+      const int row = flat / CPR, ch = flat % CPR;
+      const int64_t trow = base + 32 * w + row;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (trow < t_end) val = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
+    }
+    __syncthreads();
+    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, nullptr, acc);
+    __syncthreads();
+  }
+  write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), acc);
+}
+
+// ------------------------------------------------------------------ race_readout_norm
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ frag RF[(G::CT + 1) * G::KL * E::NSPLIT * 64];
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_readout_frags<T, G>(a.st_content + (size_t)bh * G::LRP * G::D, a.st_mass + (size_t)bh * G::LRP, RF);
+  __syncthreads();
+
+  const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
+  T* O = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
+  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
+  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const float beta2 = 2.f * a.beta;
+
+  for (int64_t base = t_begin + 32 * w; base < t_end; base += TT) {
+    const int64_t tok = base + n;
+    const bool valid = tok < t_end;
+    frag xf[G::KD];
+    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    project<T, G>(Wf, xf, pre);
+    soft_assign<G>(pre, beta2, a.L, u, phi);
+    f32x16 acc[G::CT + 1];
+    readout_mma<T, G>(RF, phi, acc);
+    const float inv = 1.f / acc[G::CT][0];
+    float o[G::D / 2];
+#pragma unroll
+    for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[16 * mt + v] = acc[mt][v] * inv;
+    if (valid) store_tl_row<T, G::D>(O + tok * G::D, o);
+  }
+}
+
+// ------------------------------------------------------------------ race_bwd_q
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int NS = E::NSPLIT;
+  constexpr int TTP = TT + Pad<T>::v;
+  constexpr int BSP = G::D + Pad<T>::v;
+  constexpr int NTW = cdiv(G::AT * (G::CT + 1), 4);
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ frag RF[(G::CT + 1) * G::KL * NS * 64];
+  __shared__ frag DF[G::AT * G::KD * NS * 64];
+  __shared__ frag WTf[G::CT * G::NQS * 64];
+  __shared__ float massL[G::LRP];
+  __shared__ T PhiT[G::LRP * TTP];
+  __shared__ T Bs[TT * BSP];
+  __shared__ float hs[TT];
+
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+  const float* content = a.st_content + (size_t)bh * G::LRP * G::D;
+  const float* mass = a.st_mass + (size_t)bh * G::LRP;
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_readout_frags<T, G>(content, mass, RF);
+  build_bank_rows_frags<T, G, true>(content, DF);
+  build_wt_frags<T, G>(a.W, a.L, a.P, WTf);
+  for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) massL[i] = mass[i];
+  __syncthreads();
+
+  const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
+  const T* dO = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
+  T* dQ = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
+  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
+  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const float beta2 = 2.f * a.beta;
+
+  f32x16 racc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) racc[j] = zero16();
+
+  for (int64_t base = t_begin; base < t_end; base += TT) {
+    const int tl = 32 * w + n;
+    const int64_t tok = base + tl;
+    const bool valid = tok < t_end;
+    frag xf[G::KD];
+    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    project<T, G>(Wf, xf, pre);
+    soft_assign<G>(pre, beta2, a.L, u, phi);
+    if (!valid) {
+#pragma unroll
+      for (int i = 0; i < G::LRP / 2; ++i) phi[i] = 0.f;
+    }
+    f32x16 acc[G::CT + 1];
+    readout_mma<T, G>(RF, phi, acc);
+    const float den = valid ? acc[G::CT][0] : 1.f;
+    const float inv = 1.f / den;
+    float g[G::D / 2];
+    if (valid) load_tl_row<T, G::D>(dO + tok * G::D, g);
+    else {
+#pragma unroll
+      for (int i = 0; i < G::D / 2; ++i) g[i] = 0.f;
+    }
+    float hd = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hd += g[16 * mt + v] * acc[mt][v];
+    hd += xor32(hd);
+    const float hval = -hd * inv * inv;        // -(dO . O) / Den with O = Num / Den
+#pragma unroll
+    for (int i = 0; i < G::D / 2; ++i) g[i] *= inv;
+
+    // dPhi_Q[lr] = content[lr] . g + mass[lr] h
+    float dphi[G::LRP / 2];
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at) {
+      f32x16 d = zero16();
+#pragma unroll
+      for (int q = 0; q < G::KD; ++q) {
+        frag gh, gl;
+        tl_frag_split<T, G::D>(g, q, gh, gl);
+        E::mma(DF[((at * G::KD + q) * NS + 0) * 64 + lane], gh, d);
+        if (NS == 2) {
+          E::mma(DF[((at * G::KD + q) * NS + 0) * 64 + lane], gl, d);
+          E::mma(DF[((at * G::KD + q) * NS + (NS - 1)) * 64 + lane], gh, d);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        dphi[16 * at + v] = d[v] + massL[lr] * hval;
+      }
+    }
+    float dpre[G::NHP];
+    assign_backward<G>(phi, dphi, u, a.beta, dpre);
+    float dx[G::D / 2];
+    dx_mma<T, G>(WTf, dpre, dx);
+    if (valid) store_tl_row<T, G::D>(dQ + tok * G::D, dx);
+
+    // stage Phi_Q^T, g, h for dcontent = Phi_Q^T g, dmass = Phi_Q^T h
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        PhiT[lr * TTP + tl] = (T)phi[16 * at + v];
+      }
+#pragma unroll
+    for (int mt = 0; mt < G::CT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typename E::vec4 wv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wv[k] = (T)g[16 * mt + 4 * j + k];
+        *reinterpret_cast<typename E::vec4*>(Bs + tl * BSP + 32 * mt + 8 * j + 4 * h) = wv;
+      }
+    if (h == 0) hs[tl] = valid ? hval : 0.f;
+    __syncthreads();
+    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, hs, racc);
+    __syncthreads();
+  }
+  write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), racc);
+}
+
+// ------------------------------------------------------------------ race_bwd_kv
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int NS = E::NSPLIT;
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ frag VF[G::CT * G::KL * NS * 64];
+  __shared__ frag KF[G::AT * G::KD * NS * 64];
+  __shared__ frag WTf[G::CT * G::NQS * 64];
+  __shared__ float dmassL[G::LRP];
+
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+  const float* dcontent = a.st_content + (size_t)bh * G::LRP * G::D;
+  const float* dmass = a.st_mass + (size_t)bh * G::LRP;
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_bank_cols_frags<T, G>(dcontent, VF);
+  build_bank_rows_frags<T, G, false>(dcontent, KF);
+  build_wt_frags<T, G>(a.W, a.L, a.P, WTf);
+  for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) dmassL[i] = dmass[i];
+  __syncthreads();
+
+  const T* Kx = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
+  const T* Vx = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
+  T* dV = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
+  T* dK = static_cast<T*>(a.out1) + (size_t)bh * a.N * G::D;
+  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
+  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const float beta2 = 2.f * a.beta;
+
+  for (int64_t base = t_begin + 32 * w; base < t_end; base += TT) {
+    const int64_t tok = base + n;
+    const bool valid = tok < t_end;
+    frag xf[G::KD];
+    load_row_frags<T, G>(valid ? Kx + tok * G::D : nullptr, xf);
+    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    project<T, G>(Wf, xf, pre);
+    soft_assign<G>(pre, beta2, a.L, u, phi);
+    // dV = sum_l Phi_K dcontent
+    float dv[G::D / 2];
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int q = 0; q < G::KL; ++q) {
+        const frag b = tl_frag<T, G::LRP>(phi, q);
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) E::mma(VF[((ct * G::KL + q) * NS + sp) * 64 + lane], b, acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dv[16 * ct + v] = acc[v];
+    }
+    if (valid) store_tl_row<T, G::D>(dV + tok * G::D, dv);
+    // dPhi_K[lr] = dcontent[lr] . V + dmass[lr]
+    frag yf[G::KD];
+    load_row_frags<T, G>(valid ? Vx + tok * G::D : nullptr, yf);
+    float dphi[G::LRP / 2];
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at) {
+      f32x16 d = zero16();
+#pragma unroll
+      for (int q = 0; q < G::KD; ++q)
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) E::mma(KF[((at * G::KD + q) * NS + sp) * 64 + lane], yf[q], d);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        dphi[16 * at + v] = d[v] + dmassL[lr];
+      }
+    }
+    float dpre[G::NHP];
+    assign_backward<G>(phi, dphi, u, a.beta, dpre);
+    float dx[G::D / 2];
+    dx_mma<T, G>(WTf, dpre, dx);
+    if (valid) store_tl_row<T, G::D>(dK + tok * G::D, dx);
+  }
+}
+
+}  // namespace race

@@ -1,0 +1,27 @@
+// Registry of compiled kernel instances, keyed by (dtype, d, PE, LRP).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace race {
+
+struct NCArgs;
+struct CArgs;
+
+typedef void (*nc_launch_fn)(const NCArgs&, dim3 grid, hipStream_t);
+typedef void (*c_launch_fn)(const CArgs&, dim3 grid, hipStream_t);
+typedef void (*dbg_launch_fn)(const void* X, const float* W, float beta, int L, int P, int64_t N,
+                              float* out, dim3 grid, hipStream_t);
+
+struct KernelSet {
+  int dtype;   // race_dtype
+  int D, PE, LRP;
+  nc_launch_fn reduce, readout, bwd_q, bwd_kv;
+  dbg_launch_fn softbucket_dbg;
+  c_launch_fn causal_fwd, causal_bwd_q, causal_bwd_kv;   // may be null
+};
+
+const KernelSet* kernel_sets_f32(int* count);
+const KernelSet* kernel_sets_bf16(int* count);
+
+}  // namespace race

@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/race_attn.h declares, answers size queries, and rejects invalid
+arguments on the host (nothing is launched in these tests)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "race_attn.h")
+
+race = pytest.importorskip("linear_attention_soft_amd")
+
+
+def _lib():
+    if not os.path.exists(race.library_path):
+        pytest.fail("librace_attn.so is not built (run __graft_entry__.build())")
+    return race.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(race_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("race_attn_fwd", "race_attn_bwd", "race_attn_state_bytes", "race_attn_workspace_bytes",
+              "race_status_string", "race_last_error", "race_softbucket_debug"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+    assert set(race.EXPORTED_SYMBOLS) == set(_declared_functions())
+
+
+def test_status_strings():
+    L = _lib()
+    assert L.race_status_string(0) == b"RACE_OK"
+    assert L.race_status_string(2) == b"RACE_ERR_UNSUPPORTED"
+
+
+def _shape(B=1, H=2, N=1000, d=64, dtype=1):
+    return race.race_shape(B, H, N, d, dtype)
+
+
+def test_size_queries():
+    s = _shape(N=4096, d=128)
+    sb = race.race_attn_state_bytes(s, 4, 2, False)
+    assert sb == 2 * 32 * 129 * 4            # B*H x LRP x (d + 1) float32
+    assert race.race_attn_workspace_bytes(s, 4, 2, False, False) > 0
+    assert race.race_attn_workspace_bytes(s, 4, 2, False, True) > 0
+    # invalid arguments give 0
+    assert race.race_attn_state_bytes(s, 0, 2, False) == 0
+    assert race.race_attn_state_bytes(s, 4, 0, False) == 0
+    assert race.race_attn_state_bytes(_shape(N=0), 4, 2, False) == 0
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails a host check first
+
+
+def _fwd(shape, P=3, L=2, causal=0, beta=1.0, q=FAKE, o=FAKE + 0x10000000, ws=FAKE + 0x20000000, wsb=1 << 30,
+         state=None, stateb=0):
+    Lb = _lib()
+    k, v, w = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+    return Lb.race_attn_fwd(q, k, v, w, ctypes.c_float(beta), P, L, causal, o,
+                            ctypes.byref(shape) if shape is not None else None, state, stateb, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(shape=None), 1),
+    (dict(P=0), 1), (dict(P=9), 1), (dict(L=0), 1), (dict(causal=2), 1),
+    (dict(beta=math.nan), 1), (dict(beta=math.inf), 1),
+    (dict(q=None), 1),
+    (dict(q=FAKE + 4), 1),                      # misaligned
+    (dict(o=FAKE), 1),                          # O overlaps Q
+    (dict(wsb=16), 3),                          # workspace too small
+    (dict(ws=None), 3),
+    (dict(state=FAKE + 0x30000000, stateb=8), 3),
+    (dict(L=64), 2),                            # L * 2^P above 256
+])
+def test_forward_rejects_bad_arguments(kw, code):
+    shape = kw.pop("shape", _shape())
+    st = _fwd(shape, **kw)
+    assert st == code, (kw, st, _lib().race_last_error())
+    assert _lib().race_last_error() != b""
+
+
+@pytest.mark.parametrize("shape,code", [
+    (_shape(d=96), 2), (_shape(d=0), 1), (_shape(N=0), 1), (_shape(B=0), 1), (_shape(dtype=7), 1),
+])
+def test_forward_rejects_bad_shapes(shape, code):
+    assert _fwd(shape) == code
+
+
+def test_backward_rejects_bad_arguments():
+    Lb = _lib()
+    s = _shape()
+    base = [FAKE + i * 0x1000000 for i in range(12)]
+
+    def call(state=base[9], stateb=1 << 30, ws=base[10], wsb=1 << 30, beta=1.0, dq=base[6]):
+        return Lb.race_attn_bwd(base[0], base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, 0, None, base[5],
+                                dq, base[7], base[8], ctypes.byref(s), state, stateb, ws, wsb, None)
+
+    assert call(state=None) == 1
+    assert call(beta=math.nan) == 1
+    assert call(stateb=4) == 3
+    assert call(wsb=4) == 3
+    assert call(dq=base[0]) == 1                # dQ overlaps Q
+
+
+def test_softbucket_debug_rejects_small_P():
+    Lb = _lib()
+    s = _shape()
+    assert Lb.race_softbucket_debug(FAKE, FAKE + 0x1000000, ctypes.c_float(1.0), 2, 2, ctypes.byref(s),
+                                    FAKE + 0x2000000, None) == 2
