@@ -109,7 +109,8 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
   for (int i = 0; i < count; ++i) {
     const race::KernelSet& k = sets[i];
     if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
-    if (causal && !k.causal_fwd) continue;
+    if (causal && !k.c_o) continue;
+    if (!causal && !k.readout) continue;
     if (!best || k.LRP < best->LRP) best = &k;
   }
   return best;
@@ -168,6 +169,31 @@ size_t state_bytes(const Plan& p) {
   return align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
 }
 
+int nhp_of(const Plan& p) {
+  const int R = 1 << p.PE;
+  const int lmax = p.LRP / R > 0 ? p.LRP / R : 1;
+  return lmax * p.PE;
+}
+
+// Causal backward workspace: h partials [BH][N][d/32], h [BH][N], gradient
+// segment sums and their reverse scan [BH][nseg][LRP][d+1] each, dPre of Q
+// and of K [BH][N][NHP] each.
+struct CausalBwdWs {
+  size_t hpart, h, gpart, gsuf, dpq, dpk, total;
+};
+CausalBwdWs causal_bwd_ws(const Plan& p) {
+  CausalBwdWs w{};
+  size_t off = 0;
+  w.hpart = off; off += align256((size_t)p.BH * p.N * (p.D / 32) * sizeof(float));
+  w.h = off;     off += align256(tok_bytes(p));
+  w.gpart = off; off += align256(seg_bank_bytes(p));
+  w.gsuf = off;  off += align256(seg_bank_bytes(p));
+  w.dpq = off;   off += align256((size_t)p.BH * p.N * nhp_of(p) * sizeof(float));
+  w.dpk = off;   off += align256((size_t)p.BH * p.N * nhp_of(p) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
 size_t workspace_bytes(const Plan& p, bool bwd) {
   if (!p.causal) {
     size_t w = align256(part_bytes(p));
@@ -175,9 +201,10 @@ size_t workspace_bytes(const Plan& p, bool bwd) {
     else w += align256(bank_bytes(p));               // gradient bank dcontent, dmass
     return w;
   }
+  // forward: segment sums, and (when no state buffer is given) the segment
+  // banks and Den
   if (!bwd) return align256(seg_bank_bytes(p)) + align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
-  // causal backward: per-segment gradient aggregates, their suffix scan, per-token h
-  return align256(seg_bank_bytes(p)) + align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
+  return causal_bwd_ws(p).total;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -200,6 +227,136 @@ void launch_finalize(const float* part, int nchunk, const Plan& p, float* conten
   const int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(race::race_bank_finalize, dim3((unsigned)blocks), dim3(threads), 0, st, part, nchunk,
                      p.LRP, (int)p.D, (int)p.BH, content, mass);
+}
+
+
+// ---- causal sequences
+race_status causal_forward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                           void* O, void* state, char* ws, hipStream_t s) {
+  race_status st;
+  const int per = p.LRP * (int)(p.D + 1);
+  float* part = reinterpret_cast<float*>(ws);
+  char* sbase = state ? static_cast<char*>(state) : ws + align256(seg_bank_bytes(p));
+  float* prefix = reinterpret_cast<float*>(sbase);
+  float* den = reinterpret_cast<float*>(sbase + align256(seg_bank_bytes(p)));
+  race::NCArgs r{};
+  r.X = K; r.Y = V; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
+  r.chunk_tokens = p.seg_tokens; r.nchunk = p.nseg; r.part = part;
+  {
+    ProfScope ps(s, "race_causal_segsum");
+    p.ks->reduce(r, dim3(p.nseg, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_causal_segsum")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_seg_scan");
+    const int64_t tot = p.BH * (int64_t)per;
+    hipLaunchKernelGGL(race::race_seg_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, part, prefix,
+                       p.nseg, per, (int)p.BH, 0);
+  }
+  if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
+  race::CArgs c{};
+  c.A_src = Q; c.B_src = K; c.X_src = V; c.W = W; c.seg_state = prefix; c.den = den; c.den_out = den; c.out = O;
+  c.beta = beta; c.L = p.L; c.P = p.P; c.N = p.N; c.seg_tokens = p.seg_tokens; c.nseg = p.nseg;
+  c.units = (int64_t)p.nseg * p.BH;
+  {
+    ProfScope ps(s, "race_causal_den");
+    p.ks->c_den(c, dim3((unsigned)((c.units + 3) / 4)), s);
+  }
+  if ((st = check_launch("race_causal_den")) != RACE_OK) return st;
+  c.units = (int64_t)p.nseg * p.BH * (p.D / 32);
+  {
+    ProfScope ps(s, "race_causal_fwd");
+    p.ks->c_o(c, dim3((unsigned)((c.units + 3) / 4)), s);
+  }
+  return check_launch("race_causal_fwd");
+}
+
+race_status causal_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                            const void* dO, void* dQ, void* dK, void* dV, const void* state, char* ws,
+                            hipStream_t s) {
+  race_status st;
+  const int per = p.LRP * (int)(p.D + 1);
+  const int CT = (int)(p.D / 32);
+  const float* prefix = static_cast<const float*>(state);
+  const float* den = reinterpret_cast<const float*>(static_cast<const char*>(state) + align256(seg_bank_bytes(p)));
+  const CausalBwdWs L = causal_bwd_ws(p);
+  float* hpart = reinterpret_cast<float*>(ws + L.hpart);
+  float* h = reinterpret_cast<float*>(ws + L.h);
+  float* gpart = reinterpret_cast<float*>(ws + L.gpart);
+  float* gsuf = reinterpret_cast<float*>(ws + L.gsuf);
+  float* dpq = reinterpret_cast<float*>(ws + L.dpq);
+  float* dpk = reinterpret_cast<float*>(ws + L.dpk);
+  const int R = 1 << p.PE;
+  const int URP = R > 32 ? R : 32;
+  const int NTG = p.LRP / URP;
+
+  race::CArgs c{};
+  c.W = W; c.beta = beta; c.L = p.L; c.P = p.P; c.N = p.N; c.seg_tokens = p.seg_tokens; c.nseg = p.nseg;
+  c.den = den;
+  // 1. per-column-tile partial dO . O, then h = -(dO . O) / Den
+  c.A_src = Q; c.B_src = K; c.X_src = V; c.dO = dO; c.hpart = hpart; c.seg_state = prefix;
+  c.units = (int64_t)p.nseg * p.BH * CT;
+  {
+    ProfScope ps(s, "race_causal_h");
+    p.ks->c_h(c, dim3((unsigned)((c.units + 3) / 4)), s);
+  }
+  if ((st = check_launch("race_causal_h")) != RACE_OK) return st;
+  {
+    const int64_t tot = p.BH * p.N;
+    hipLaunchKernelGGL(race::race_h_final, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, hpart, den, h, tot,
+                       CT);
+  }
+  if ((st = check_launch("race_h_final")) != RACE_OK) return st;
+  // 2. gradient segment sums Phi_Q^T [g | h], reverse exclusive scan
+  race::NCArgs r{};
+  r.X = Q; r.Y = dO; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
+  r.chunk_tokens = p.seg_tokens; r.nchunk = p.nseg; r.part = gpart; r.tok_den = den; r.tok_extra = h;
+  {
+    ProfScope ps(s, "race_causal_gradsum");
+    p.ks->reduce(r, dim3(p.nseg, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
+  {
+    const int64_t tot = p.BH * (int64_t)per;
+    hipLaunchKernelGGL(race::race_seg_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, gpart, gsuf,
+                       p.nseg, per, (int)p.BH, 1);
+  }
+  if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
+  // 3. dV: reverse walk of the readout with Phi_K as query, Phi_Q as key, g as value
+  race::CArgs v = c;
+  v.A_src = K; v.B_src = Q; v.X_src = dO; v.out = dV; v.seg_state = gsuf;
+  v.units = (int64_t)p.nseg * p.BH * CT;
+  {
+    ProfScope ps(s, "race_causal_dv");
+    p.ks->c_dv(v, dim3((unsigned)((v.units + 3) / 4)), s);
+  }
+  if ((st = check_launch("race_causal_dv")) != RACE_OK) return st;
+  // 4. dPhi_Q (forward walk) and dPhi_K (reverse walk) -> dPre
+  race::CArgs q = c;
+  q.A_src = Q; q.B_src = K; q.X_src = V; q.U_src = dO; q.hvec = h; q.seg_state = prefix; q.dpre_out = dpq;
+  q.units = (int64_t)p.nseg * p.BH * NTG;
+  {
+    ProfScope ps(s, "race_causal_dphi_q");
+    p.ks->c_dq(q, dim3((unsigned)((q.units + 3) / 4)), s);
+  }
+  if ((st = check_launch("race_causal_dphi_q")) != RACE_OK) return st;
+  race::CArgs k = c;
+  k.A_src = K; k.B_src = Q; k.X_src = dO; k.U_src = V; k.hvec = h; k.seg_state = gsuf; k.dpre_out = dpk;
+  k.units = (int64_t)p.nseg * p.BH * NTG;
+  {
+    ProfScope ps(s, "race_causal_dphi_k");
+    p.ks->c_dk(k, dim3((unsigned)((k.units + 3) / 4)), s);
+  }
+  if ((st = check_launch("race_causal_dphi_k")) != RACE_OK) return st;
+  // 5. dQ, dK = dPre . W
+  {
+    const int64_t tiles = (p.BH * p.N + race::TT - 1) / race::TT;
+    const unsigned blocks = (unsigned)(tiles < 8192 ? tiles : 8192);
+    ProfScope ps(s, "race_causal_dx");
+    p.ks->dx(dpq, W, p.L, p.P, p.N, p.BH, dQ, dim3(blocks), s);
+    p.ks->dx(dpk, W, p.L, p.P, p.N, p.BH, dK, dim3(blocks), s);
+  }
+  return check_launch("race_causal_dx");
 }
 
 }  // namespace
@@ -248,8 +405,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  if (p.causal) return race::causal_forward(*p.ks, Q, K, V, W, beta, p.L, p.P, p.N, (int)p.BH, p.LRP, (int)p.D,
-                                            p.nseg, p.seg_tokens, O, state, ws, s, &g_last_error);
+  if (p.causal) return causal_forward(p, Q, K, V, W, beta, O, state, ws, s);
 
   float* part = reinterpret_cast<float*>(ws);
   float* bank = state ? static_cast<float*>(state) : reinterpret_cast<float*>(ws + align256(part_bytes(p)));
@@ -313,9 +469,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  if (p.causal)
-    return race::causal_backward(*p.ks, Q, K, V, W, beta, p.L, p.P, p.N, (int)p.BH, p.LRP, (int)p.D, p.nseg,
-                                 p.seg_tokens, dO, dQ, dK, dV, state, ws, s, &g_last_error);
+  if (p.causal) return causal_backward(p, Q, K, V, W, beta, dO, dQ, dK, dV, state, ws, s);
 
   const float* content = static_cast<const float*>(state);
   const float* mass = content + (size_t)p.BH * p.LRP * p.D;

@@ -1,4 +1,29 @@
-// Causal RACE attention (prefix bucket sums).  Host-side entry points.
+// Causal RACE attention for gfx950: prefix bucket sums (slides frame
+// "Causality is a prefix update of the same statistics", paper Algorithm 2;
+// reading notes section 2.6).  The key at position t is added before the
+// query at t reads, so token t sees keys j <= t.
+//
+// The sequence of every (batch, head) is cut into segments.  One wave walks
+// a segment in 32-token chunks and carries the running bucket bank in MFMA
+// accumulators; the bank at each segment start comes from a segment-sum
+// reduce plus an exclusive scan over segments.  Inside a chunk the bank
+// before the chunk is read with Phi_Q (inter part) and the chunk's own keys
+// enter through the masked 32x32 kernel tile Phi_Q Phi_K^T (intra part).
+//
+// A bank of L*R rows x (d+1) columns is too large for one wave at the wide
+// settings (L = 4, P = 6: 256 x 129 floats), so waves split it:
+//   race_causal_readout     one wave per 32-column slice of the values:
+//                           contracts the bank over buckets (O, Den, dV).
+//   race_causal_transposed  one wave per window of whole tables (bucket
+//                           rows): contracts the bank over value columns
+//                           (dPhi_Q, dPhi_K), then softmax, tanh and
+//                           projection backward of those tables.
+// Backward (exact gradient of the causal forward map, W and beta fixed):
+//   g_t = dO_t / Den_t,  h_t = -(dO_t . O_t) / Den_t
+//   dPhi_Q,t = sum_{j<=t} phi_K,j (V_j . g_t + h_t)          (transposed, forward walk)
+//   dPhi_K,j = sum_{t>=j} phi_Q,t (g_t . V_j + h_t)          (transposed, reverse walk)
+//   dV_j     = sum_{t>=j} (phi_K,j . phi_Q,t) g_t             (readout, reverse walk)
+// and dQ, dK = dPre . W.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -6,11 +31,38 @@
 #include <string>
 
 #include "../../include/race_attn.h"
+#include "race_noncausal.hpp"
 #include "race_registry.hpp"
 
 namespace race {
 
-// Segments of the sequence processed by one workgroup each.
+constexpr int CC = 32;   // tokens per causal chunk
+
+struct CArgs {
+  const void* A_src;      // rows whose features take the output (query) role
+  const void* B_src;      // rows whose features take the state (key) role
+  const void* X_src;      // value rows of the state role (V; or dO, divided by Den)
+  const void* U_src;      // value rows of the output role (transposed kernel: dO or V)
+  const void* dO;         // readout in h mode
+  void* out;              // readout: O or dV rows
+  float* dpre_out;        // transposed: [BH][N][NHP] dPre of the output role
+  const float* W;
+  const float* seg_state; // [BH][nseg][LRP][d+1]: bank before (forward walk) / after (reverse walk) the segment
+  const float* den;       // [BH][N]
+  float* den_out;         // [BH][N]
+  float* hpart;           // [BH][N][d/32]
+  const float* hvec;      // [BH][N]
+  float beta;
+  int L, P;
+  int64_t N;
+  int64_t seg_tokens;
+  int nseg;
+  int64_t units;
+};
+
+enum { RO_O = 0, RO_DEN = 1, RO_H = 2, RO_DV = 3 };
+
+// Segments: about 4096 waves of work over the whole problem, 64-token multiples.
 inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_tokens) {
   int64_t want = (1024 + BH - 1) / BH;
   const int64_t tiles = (N + 63) / 64;
@@ -21,18 +73,539 @@ inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_t
   *nseg = (int)((N + *seg_tokens - 1) / *seg_tokens);
 }
 
-inline race_status causal_forward(const KernelSet&, const void*, const void*, const void*, const float*, float, int,
-                                  int, int64_t, int, int, int, int, int64_t, void*, void*, char*, hipStream_t,
-                                  std::string* err) {
-  *err = "causal kernels are not built";
-  return RACE_ERR_UNSUPPORTED;
+// Load a 32-token x 32-column slice of value rows into an LDS tile (row
+// stride XSP), optionally divided by den[token]; rows past s1 are zero.
+template <typename T, int D, int XSP>
+__device__ __forceinline__ void stage_cols(const T* __restrict__ src, int64_t t0, int64_t s1, int c0,
+                                           const float* __restrict__ den, T* __restrict__ Xs) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int CPR = 32 / EPC;
+  const int lane = lane_id();
+#pragma unroll
+  for (int it = 0; it < 32 * CPR / 64; ++it) {
+    const int flat = it * 64 + lane;
+    const int row = flat / CPR, ch = flat % CPR;
+    const int64_t tr = t0 + row;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (tr < s1) {
+      val = *reinterpret_cast<const uint4*>(src + tr * D + c0 + ch * EPC);
+      if (den) {
+        const float inv = 1.f / den[tr];
+        T* e = reinterpret_cast<T*>(&val);
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
+      }
+    }
+    *reinterpret_cast<uint4*>(Xs + row * XSP + ch * EPC) = val;
+  }
 }
 
-inline race_status causal_backward(const KernelSet&, const void*, const void*, const void*, const float*, float, int,
-                                   int, int64_t, int, int, int, int, int64_t, const void*, void*, void*, void*,
-                                   const void*, char*, hipStream_t, std::string* err) {
-  *err = "causal kernels are not built";
-  return RACE_ERR_UNSUPPORTED;
+// Features of one token row for the whole bucket bank, packed as K16 B frags.
+template <typename T, class G>
+__device__ __forceinline__ void features_packed(const typename Eng<T>::frag* __restrict__ Wf, const T* row,
+                                                float beta2, int L, typename Eng<T>::frag (&ph)[G::KL]) {
+  typename Eng<T>::frag xf[G::KD];
+  load_row_frags<T, G>(row, xf);
+  float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+  project<T, G>(Wf, xf, pre);
+  soft_assign<G>(pre, beta2, L, u, phi);
+  if (!row) {
+#pragma unroll
+    for (int i = 0; i < G::LRP / 2; ++i) phi[i] = 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < G::KL; ++q) ph[q] = tl_frag<T, G::LRP>(phi, q);
+}
+
+// ------------------------------------------------------------------ race_causal_readout
+// Unit = (segment, bh, value-column tile ct).  Bank slice S[lr][32 ct + n]
+// lives in accumulators st[at] (lane = column, registers over buckets).
+template <typename T, class G, bool REV, int MODE>
+__global__ __launch_bounds__(256) void race_causal_readout(CArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int NS = E::NSPLIT;
+  constexpr int TTP = CC + 8;
+  constexpr int XSP = 32 + 8;
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ T PhiT_all[4][G::LRP * TTP];
+  __shared__ T Xs_all[4][CC * XSP];
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  __syncthreads();
+
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
+  if (unit >= a.units) return;
+  T* PhiT = PhiT_all[w];
+  T* Xs = Xs_all[w];
+  constexpr int NU = (MODE == RO_DEN) ? 1 : G::CT;
+  const int ct = (MODE == RO_DEN) ? G::CT : (int)(unit % NU);
+  const int64_t seg = (unit / NU) % a.nseg;
+  const int64_t bh = unit / NU / a.nseg;
+  const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
+  const size_t rb = (size_t)bh * a.N;
+  const T* Ar = static_cast<const T*>(a.A_src) + rb * G::D;
+  const T* Br = static_cast<const T*>(a.B_src) + rb * G::D;
+
+  f32x16 st[G::AT];
+  {
+    const float* ss = a.seg_state + ((size_t)bh * a.nseg + seg) * G::LRP * (G::D + 1);
+    const int col = (MODE == RO_DEN) ? G::D : 32 * ct + n;
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        st[at][v] = ss[(size_t)lr * (G::D + 1) + col];
+      }
+  }
+  const float beta2 = 2.f * a.beta;
+  const int64_t nch = (s1 - s0 + CC - 1) / CC;
+  for (int64_t k = 0; k < nch; ++k) {
+    const int64_t t0 = s0 + (REV ? (nch - 1 - k) : k) * CC;
+    const int64_t tok = t0 + n;
+    const bool valid = tok < s1;
+    frag pa[G::KL], pb[G::KL];
+    features_packed<T, G>(Wf, valid ? Ar + tok * G::D : nullptr, beta2, a.L, pa);
+    features_packed<T, G>(Wf, valid ? Br + tok * G::D : nullptr, beta2, a.L, pb);
+    // transposed state-role features for the bank update
+#pragma unroll
+    for (int q = 0; q < G::KL; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) PhiT[kmap(q, h, i) * TTP + n] = pb[q][i];
+    if (MODE == RO_O || MODE == RO_H)
+      stage_cols<T, G::D, XSP>(static_cast<const T*>(a.X_src) + rb * G::D, t0, s1, 32 * ct, nullptr, Xs);
+    if (MODE == RO_DV)
+      stage_cols<T, G::D, XSP>(static_cast<const T*>(a.X_src) + rb * G::D, t0, s1, 32 * ct, a.den + rb, Xs);
+    wave_lds_sync();
+
+    // inter: bank before the chunk, read with the output-role features
+    f32x16 y = zero16();
+#pragma unroll
+    for (int q = 0; q < G::KL; ++q) {
+      float v8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v8[i] = st[q >> 1][8 * (q & 1) + i];
+      frag hi, lo;
+      E::split(v8, hi, lo);
+      E::mma(hi, pa[q], y);
+      if (NS == 2) E::mma(lo, pa[q], y);
+    }
+    // intra: masked kernel tile sc^T[tok_b][tok_a] = phi_B . phi_A
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int q = 0; q < G::KL; ++q) E::mma(pb[q], pa[q], sc);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
+      const bool keep = REV ? (tb >= n) : (tb <= n);
+      sc[v] = keep ? sc[v] : 0.f;
+    }
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      float s8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s8[i] = sc[8 * q2 + i];
+      const frag sb = E::pack(s8);
+      frag xa;
+      if (MODE == RO_DEN) {
+        xa = E::ones();
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[i] = Xs[kmap(q2, h, i) * XSP + n];
+      }
+      E::mma(xa, sb, y);
+    }
+    // epilogue: lane (tok, h) holds columns 32 ct + 8 j + 4 h + k
+    if (MODE == RO_DEN) {
+      if (valid && h == 0) a.den_out[rb + tok] = y[0];
+    } else if (MODE == RO_O || MODE == RO_DV) {
+      if (valid) {
+        const float inv = (MODE == RO_O) ? 1.f / a.den[rb + tok] : 1.f;
+        T* orow = static_cast<T*>(a.out) + (rb + tok) * G::D + 32 * ct + 4 * h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          typename E::vec4 o;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) o[kk] = (T)(y[4 * j + kk] * inv);
+          *reinterpret_cast<typename E::vec4*>(orow + 8 * j) = o;
+        }
+      }
+    } else {  // RO_H: partial dO . O over this column tile
+      float part = 0.f;
+      if (valid) {
+        const float inv = 1.f / a.den[rb + tok];
+        const T* drow = static_cast<const T*>(a.dO) + (rb + tok) * G::D + 32 * ct + 4 * h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const typename E::vec4 dv = *reinterpret_cast<const typename E::vec4*>(drow + 8 * j);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) part += (float)dv[kk] * (y[4 * j + kk] * inv);
+        }
+      }
+      part += xor32(part);
+      if (valid && h == 0) a.hpart[(rb + tok) * G::CT + ct] = part;
+    }
+    // bank update with the chunk's state-role keys and values
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const frag af = *reinterpret_cast<const frag*>(PhiT + (32 * at + n) * TTP + 16 * s + 8 * h);
+        frag bf;
+        if (MODE == RO_DEN) {
+          bf = E::ones();
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bf[i] = Xs[(16 * s + 8 * h + i) * XSP + n];
+        }
+        E::mma(af, bf, st[at]);
+      }
+    wave_lds_sync();
+  }
+}
+
+// ------------------------------------------------------------------ race_causal_transposed
+// Unit = (segment, bh, window TG of whole tables).  Bank rows of the window
+// live in acc[a][ct] as C[c][lr] tiles (lane = bucket row, registers over
+// value columns c; tile CT holds the mass / h column at c = d).
+// Forward walk (dPhi_Q): output role Q, state role K, X = [V | 1], U = [g | h].
+// Reverse walk (dPhi_K):  output role K, state role Q, X = [g | h], U = [V | 1].
+template <typename T, class G, bool REV, int TG>
+__device__ __forceinline__ void transposed_body(const CArgs& a, int64_t seg, int64_t bh,
+                                                const typename Eng<T>::frag* __restrict__ Wf, T* __restrict__ PhiT,
+                                                T* __restrict__ Xh, T* __restrict__ Xl) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int NS = E::NSPLIT;
+  constexpr int URP = G::R > 32 ? G::R : 32;
+  constexpr int ATU = URP / 32;
+  constexpr int R0 = TG * URP;
+  constexpr int TTP = CC + 8;
+  constexpr int XSP = G::D + 32 + 8;
+  constexpr int NC = G::CT + 1;          // column tiles incl. the mass / h tile
+  constexpr bool XEXACT = !REV;          // X = [V | 1] is exact in T; [g | h] is not
+  constexpr bool UEXACT = REV;           // U = [V | 1] exact; [g | h] not
+  constexpr bool USE_XL = !XEXACT && NS == 2;
+  const int lane = lane_id(), n = lane & 31, h = lane >> 5;
+  const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
+  const size_t rb = (size_t)bh * a.N;
+  const T* Ar = static_cast<const T*>(a.A_src) + rb * G::D;
+  const T* Br = static_cast<const T*>(a.B_src) + rb * G::D;
+  const T* Xr = static_cast<const T*>(a.X_src) + rb * G::D;
+  const T* Ur = static_cast<const T*>(a.U_src) + rb * G::D;
+  const float* den = a.den + rb;
+  const float* hv = a.hvec + rb;
+
+  f32x16 acc[ATU][NC];
+  {
+    const float* ss = a.seg_state + ((size_t)bh * a.nseg + seg) * G::LRP * (G::D + 1);
+#pragma unroll
+    for (int at = 0; at < ATU; ++at)
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * ct + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int lr = R0 + 32 * at + n;
+          acc[at][ct][v] = (c <= G::D) ? ss[(size_t)lr * (G::D + 1) + c] : 0.f;
+        }
+  }
+  // the mass-tile columns past c = d stay zero in the X tiles
+  for (int r = 0; r < CC; ++r) {
+    if (lane < 32) {
+      Xh[r * XSP + G::D + lane] = (T)0.f;
+      if (USE_XL) Xl[r * XSP + G::D + lane] = (T)0.f;
+    }
+  }
+  const float beta2 = 2.f * a.beta;
+  const int64_t nch = (s1 - s0 + CC - 1) / CC;
+  for (int64_t k = 0; k < nch; ++k) {
+    const int64_t t0 = s0 + (REV ? (nch - 1 - k) : k) * CC;
+    const int64_t tok = t0 + n;
+    const bool valid = tok < s1;
+    // output-role features of the window (float32, for the softmax backward)
+    float uA[G::NHP], phA[URP / 2];
+    {
+      frag xf[G::KD];
+      float pre[G::NHP];
+      load_row_frags<T, G>(valid ? Ar + tok * G::D : nullptr, xf);
+      project<T, G>(Wf, xf, pre);
+      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uA, phA);
+    }
+    // state-role features of the window, rounded, transposed into LDS
+    {
+      frag xf[G::KD];
+      float pre[G::NHP], uB[G::NHP], phB[URP / 2];
+      load_row_frags<T, G>(valid ? Br + tok * G::D : nullptr, xf);
+      project<T, G>(Wf, xf, pre);
+      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uB, phB);
+#pragma unroll
+      for (int at = 0; at < ATU; ++at)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+          PhiT[lr * TTP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
+        }
+    }
+    // output-role values U in TLAYOUT over columns (tile CT: c = d only)
+    float ut[NC * 16];
+    {
+      float tmp[G::D / 2];
+      if (valid) load_tl_row<T, G::D>(Ur + tok * G::D, tmp);
+      else {
+#pragma unroll
+        for (int i = 0; i < G::D / 2; ++i) tmp[i] = 0.f;
+      }
+      const float scale = (!REV && valid) ? 1.f / den[tok] : 1.f;
+#pragma unroll
+      for (int i = 0; i < G::D / 2; ++i) ut[i] = tmp[i] * scale;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ut[G::D / 2 + i] = 0.f;
+      const float extra = REV ? 1.f : (valid ? hv[tok] : 0.f);
+      if (h == 0) ut[G::D / 2] = valid ? extra : 0.f;
+    }
+    // state-role values X: rows t0..t0+31, columns 0..d (c = d: 1 or h)
+    {
+      constexpr int EPC = 16 / (int)sizeof(T);
+      constexpr int CPR = G::D / EPC;
+#pragma unroll
+      for (int it = 0; it < 32 * CPR / 64; ++it) {
+        const int flat = it * 64 + lane;
+        const int row = flat / CPR, ch = flat % CPR;
+        const int64_t tr = t0 + row;
+        float f[EPC];
+#pragma unroll
+        for (int kk = 0; kk < EPC; ++kk) f[kk] = 0.f;
+        if (tr < s1) {
+          const uint4 val = *reinterpret_cast<const uint4*>(Xr + tr * G::D + ch * EPC);
+          const T* e = reinterpret_cast<const T*>(&val);
+          const float sc = REV ? 1.f / den[tr] : 1.f;
+#pragma unroll
+          for (int kk = 0; kk < EPC; ++kk) f[kk] = (float)e[kk] * sc;
+        }
+#pragma unroll
+        for (int kk = 0; kk < EPC; ++kk) {
+          const T hi = (T)f[kk];
+          Xh[row * XSP + ch * EPC + kk] = hi;
+          if (USE_XL) Xl[row * XSP + ch * EPC + kk] = (T)(f[kk] - (float)hi);
+        }
+      }
+      if (h == 0) {
+        const float m = (!valid) ? 0.f : (REV ? hv[tok] : 1.f);
+        const T hi = (T)m;
+        Xh[n * XSP + G::D] = hi;
+        if (USE_XL) Xl[n * XSP + G::D] = (T)(m - (float)hi);
+      }
+    }
+    wave_lds_sync();
+
+    // dPhi of the output role, rows of the window: inter part from the bank
+    f32x16 dp[ATU];
+#pragma unroll
+    for (int at = 0; at < ATU; ++at) dp[at] = zero16();
+#pragma unroll
+    for (int q = 0; q < 2 * NC; ++q) {
+      frag uh, ul;
+      {
+        float u8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u8[i] = ut[8 * q + i];
+        E::split(u8, uh, ul);
+      }
+#pragma unroll
+      for (int at = 0; at < ATU; ++at) {
+        float v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = acc[at][q >> 1][8 * (q & 1) + i];
+        frag ah, al;
+        E::split(v8, ah, al);
+        E::mma(ah, uh, dp[at]);
+        if (NS == 2) {
+          if (!UEXACT) E::mma(ah, ul, dp[at]);
+          E::mma(al, uh, dp[at]);
+        }
+      }
+    }
+    // intra part: m^T[tok_b][tok_a] = X_b . U_a (masked), then Phi_B^T m^T
+    {
+      f32x16 mf = zero16();
+#pragma unroll
+      for (int q = 0; q < 2 * NC; ++q) {
+        frag uh, ul;
+        {
+          float u8[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u8[i] = ut[8 * q + i];
+          E::split(u8, uh, ul);
+        }
+        frag xh, xl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xh[i] = Xh[n * XSP + kmap(q, h, i)];
+        E::mma(xh, uh, mf);
+        if (NS == 2) {
+          if (!UEXACT) E::mma(xh, ul, mf);
+          if (USE_XL) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xl[i] = Xl[n * XSP + kmap(q, h, i)];
+            E::mma(xl, uh, mf);
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
+        const bool keep = REV ? (tb >= n) : (tb <= n);
+        mf[v] = keep ? mf[v] : 0.f;
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        float m8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m8[i] = mf[8 * q2 + i];
+        frag mh, ml;
+        E::split(m8, mh, ml);
+#pragma unroll
+        for (int at = 0; at < ATU; ++at) {
+          frag pf;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pf[i] = PhiT[(32 * at + n) * TTP + kmap(q2, h, i)];
+          E::mma(pf, mh, dp[at]);
+          if (NS == 2) E::mma(pf, ml, dp[at]);
+        }
+      }
+    }
+    // softmax, tanh backward of the window's tables -> dPre
+    {
+      float dphi[URP / 2];
+#pragma unroll
+      for (int at = 0; at < ATU; ++at)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dphi[16 * at + v] = dp[at][v];
+      float dpre[G::NHP];
+#pragma unroll
+      for (int i = 0; i < G::NHP; ++i) dpre[i] = 0.f;
+      assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre);
+      constexpr int L0 = R0 / G::R;
+      constexpr int L1 = cdiv(R0 + URP, G::R) < G::LMAX ? cdiv(R0 + URP, G::R) : G::LMAX;
+      if (valid && h == 0) {
+        float* dst = a.dpre_out + (rb + tok) * G::NHP;
+#pragma unroll
+        for (int hp = L0 * G::PE; hp < L1 * G::PE; ++hp) dst[hp] = dpre[hp];
+      }
+    }
+    // bank update: C[c][lr] += X^T[c][tok] Phi_B[tok][lr]
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      frag pfs[ATU];
+#pragma unroll
+      for (int at = 0; at < ATU; ++at)
+        pfs[at] = *reinterpret_cast<const frag*>(PhiT + (32 * at + n) * TTP + 16 * s + 8 * h);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        frag xh, xl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xh[i] = Xh[(16 * s + 8 * h + i) * XSP + 32 * ct + n];
+        if (USE_XL) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xl[i] = Xl[(16 * s + 8 * h + i) * XSP + 32 * ct + n];
+        }
+#pragma unroll
+        for (int at = 0; at < ATU; ++at) {
+          E::mma(xh, pfs[at], acc[at][ct]);
+          if (USE_XL) E::mma(xl, pfs[at], acc[at][ct]);
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
+template <typename T, class G, bool REV, int TG>
+__device__ __forceinline__ void transposed_dispatch(int tg, const CArgs& a, int64_t seg, int64_t bh,
+                                                    const typename Eng<T>::frag* Wf, T* PhiT, T* Xh, T* Xl) {
+  constexpr int URP = G::R > 32 ? G::R : 32;
+  if (tg == TG) {
+    transposed_body<T, G, REV, TG>(a, seg, bh, Wf, PhiT, Xh, Xl);
+  } else if constexpr ((TG + 1) * URP < G::LRP) {
+    transposed_dispatch<T, G, REV, TG + 1>(tg, a, seg, bh, Wf, PhiT, Xh, Xl);
+  }
+}
+
+template <typename T, class G, bool REV>
+__global__ __launch_bounds__(256) void race_causal_transposed(CArgs a) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  constexpr int URP = G::R > 32 ? G::R : 32;
+  constexpr int NTG = G::LRP / URP;
+  constexpr int TTP = CC + 8;
+  constexpr int XSP = G::D + 32 + 8;
+  constexpr bool USE_XL = REV && E::NSPLIT == 2;   // X = [g | h] needs hi + lo parts
+  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ T PhiT_all[4][URP * TTP];
+  __shared__ T Xh_all[4][CC * XSP];
+  __shared__ T Xl_all[USE_XL ? 4 : 1][CC * XSP];
+  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
+  if (unit >= a.units) return;
+  const int tg = (int)(unit % NTG);
+  const int64_t seg = (unit / NTG) % a.nseg;
+  const int64_t bh = unit / NTG / a.nseg;
+  transposed_dispatch<T, G, REV, 0>(tg, a, seg, bh, Wf, PhiT_all[w], Xh_all[w], Xl_all[USE_XL ? w : 0]);
+}
+
+// ------------------------------------------------------------------ dX = dPre . W
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_dx(const float* __restrict__ dpre, const float* __restrict__ W, int L,
+                                               int P, int64_t N, int64_t BH, void* __restrict__ outv) {
+  using E = Eng<T>;
+  using frag = typename E::frag;
+  __shared__ frag WTf[G::CT * G::NQS * 64];
+  build_wt_frags<T, G>(W, L, P, WTf);
+  __syncthreads();
+  const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
+  const int64_t total = BH * N;
+  T* out = static_cast<T*>(outv);
+  for (int64_t base = (int64_t)blockIdx.x * TT + 32 * w; base < total; base += (int64_t)gridDim.x * TT) {
+    const int64_t tok = base + n;
+    const bool valid = tok < total;
+    float dp[G::NHP];
+#pragma unroll
+    for (int i = 0; i < G::NHP; ++i) dp[i] = valid ? dpre[tok * G::NHP + i] : 0.f;
+    float dx[G::D / 2];
+    dx_mma<T, G>(WTf, dp, dx);
+    if (valid) store_tl_row<T, G::D>(out + tok * G::D, dx);
+  }
+}
+
+// ------------------------------------------------------------------ small kernels
+// Exclusive scan over segments (forward: banks before each segment; reverse:
+// banks after it), one thread per (bh, bank element).
+static __global__ void race_seg_scan(const float* __restrict__ part, float* __restrict__ out, int nseg, int per, int BH,
+                              int reverse) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)BH * per) return;
+  const int64_t bh = idx / per, rem = idx % per;
+  float run = 0.f;
+  for (int k = 0; k < nseg; ++k) {
+    const int s = reverse ? nseg - 1 - k : k;
+    const size_t o = ((size_t)bh * nseg + s) * per + rem;
+    const float v = part[o];
+    out[o] = run;
+    run += v;
+  }
+}
+
+// h_t = -(dO_t . O_t) / Den_t from the per-column-tile partial dot products.
+static __global__ void race_h_final(const float* __restrict__ hpart, const float* __restrict__ den, float* __restrict__ h,
+                             int64_t total, int ct) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  float s = 0.f;
+  for (int c = 0; c < ct; ++c) s += hpart[i * ct + c];
+  h[i] = -s / den[i];
 }
 
 }  // namespace race

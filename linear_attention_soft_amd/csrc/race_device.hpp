@@ -270,16 +270,20 @@ __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict_
 // Soft corner assignments in TLAYOUT (slides frame "Soft corner assignments
 // make hashing differentiable"; product-of-sigmoids form, reading notes
 // section 2.4): phi_r = prod_t sigma(2 beta u_t v_{r,t}), u = tanh(pre).
-// Lane half h owns the corners whose bit 2 equals h.  Rows of tables >= L
-// and padding rows are 0.
-template <class G>
-__device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float beta2, int L,
-                                            float (&u)[G::NHP], float (&phi)[G::LRP / 2]) {
+// Lane half h owns the corners whose bit 2 equals h.  Only bucket rows
+// [R0, R0 + NROWS) are produced (R0 and NROWS multiples of 32); rows of tables
+// >= L and padding rows are 0.  u receives tanh(pre) of every hyperplane slot.
+template <class G, int R0, int NROWS>
+__device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], float beta2, int L,
+                                                 float (&u)[G::NHP], float (&phi)[NROWS / 2]) {
+  static_assert(R0 % 32 == 0 && NROWS % 32 == 0 && R0 + NROWS <= G::LRP, "row window");
   const int h = lane_id() >> 5;
 #pragma unroll
   for (int hp = 0; hp < G::NHP; ++hp) u[hp] = tanh_f(pre[hp]);
+  constexpr int L0 = R0 / G::R;
+  constexpr int L1 = cdiv(R0 + NROWS, G::R) < G::LMAX ? cdiv(R0 + NROWS, G::R) : G::LMAX;
 #pragma unroll
-  for (int l = 0; l < G::LMAX; ++l) {
+  for (int l = L0; l < L1; ++l) {
     float sp[G::PE], sm[G::PE];
 #pragma unroll
     for (int t = 0; t < G::PE; ++t) sigmoid_pair(beta2 * u[l * G::PE + t], sp[t], sm[t]);
@@ -294,7 +298,6 @@ __device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float be
     hi[0] = 1.f;
 #pragma unroll
     for (int t = 3; t < G::PE; ++t) {
-      constexpr int dummy = 0; (void)dummy;
       const int half = 1 << (t - 3);
 #pragma unroll
       for (int x = 0; x < half; ++x) {
@@ -304,10 +307,10 @@ __device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float be
     }
     const bool live = l < L;
 #pragma unroll
-    for (int a = 0; a < G::AT; ++a) {
+    for (int a = 0; a < NROWS / 32; ++a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        const int lr0 = R0 + 32 * a + 8 * (v >> 2) + (v & 3);
         if (lr0 / G::R == l) {
           const int r0 = lr0 % G::R;
           phi[16 * a + v] = live ? g[r0 & 3] * hi[r0 >> 3] : 0.f;
@@ -316,10 +319,16 @@ __device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float be
     }
   }
 #pragma unroll
-  for (int a = 0; a < G::AT; ++a)
+  for (int a = 0; a < NROWS / 32; ++a)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      if ((32 * a + 8 * (v >> 2) + (v & 3)) / G::R >= G::LMAX) phi[16 * a + v] = 0.f;
+      if ((R0 + 32 * a + 8 * (v >> 2) + (v & 3)) / G::R >= G::LMAX) phi[16 * a + v] = 0.f;
+}
+
+template <class G>
+__device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float beta2, int L,
+                                            float (&u)[G::NHP], float (&phi)[G::LRP / 2]) {
+  soft_assign_rows<G, 0, G::LRP>(pre, beta2, L, u, phi);
 }
 
 // B operand of K16 step q from a TLAYOUT vector held in registers.
@@ -342,21 +351,25 @@ __device__ __forceinline__ void tl_frag_split(const float (&x)[M / 2], int q,
 
 // Backward through softmax, beta, corners and tanh for one token (TLAYOUT).
 // dLambda = phi * (dphi - sum_r phi dphi) per table; dU_t = beta sum_r dLambda_r v_{r,t};
-// dPre = dU * (1 - u^2).  Both lane halves end with every dPre value.
-template <class G>
-__device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], const float (&dphi)[G::LRP / 2],
-                                                const float (&u)[G::NHP], float beta,
-                                                float (&dpre)[G::NHP]) {
+// dPre = dU * (1 - u^2).  Both lane halves end with every dPre value.  Works on
+// bucket rows [R0, R0 + NROWS), which must hold whole tables; dPre slots of
+// tables outside the window are left untouched.
+template <class G, int R0, int NROWS>
+__device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 2], const float (&dphi)[NROWS / 2],
+                                                     const float (&u)[G::NHP], float beta,
+                                                     float (&dpre)[G::NHP]) {
   const int h = lane_id() >> 5;
   const float sgn2 = h ? 1.f : -1.f;
+  constexpr int L0 = R0 / G::R;
+  constexpr int L1 = cdiv(R0 + NROWS, G::R) < G::LMAX ? cdiv(R0 + NROWS, G::R) : G::LMAX;
 #pragma unroll
-  for (int l = 0; l < G::LMAX; ++l) {
+  for (int l = L0; l < L1; ++l) {
     float s = 0.f;
 #pragma unroll
-    for (int a = 0; a < G::AT; ++a)
+    for (int a = 0; a < NROWS / 32; ++a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        const int lr0 = R0 + 32 * a + 8 * (v >> 2) + (v & 3);
         if (lr0 / G::R == l) s += phi[16 * a + v] * dphi[16 * a + v];
       }
     s += xor32(s);
@@ -364,10 +377,10 @@ __device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], 
 #pragma unroll
     for (int t = 0; t < G::PE; ++t) du[t] = 0.f;
 #pragma unroll
-    for (int a = 0; a < G::AT; ++a)
+    for (int a = 0; a < NROWS / 32; ++a)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lr0 = 32 * a + 8 * (v >> 2) + (v & 3);
+        const int lr0 = R0 + 32 * a + 8 * (v >> 2) + (v & 3);
         if (lr0 / G::R == l) {
           const int r0 = lr0 % G::R;
           const float dl = phi[16 * a + v] * (dphi[16 * a + v] - s);
@@ -385,6 +398,21 @@ __device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], 
       dpre[l * G::PE + t] = beta * d * (1.f - uu * uu);
     }
   }
+}
+
+template <class G>
+__device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], const float (&dphi)[G::LRP / 2],
+                                                const float (&u)[G::NHP], float beta, float (&dpre)[G::NHP]) {
+  assign_backward_rows<G, 0, G::LRP>(phi, dphi, u, beta, dpre);
+}
+
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data (a wave issues LDS instructions in order; this stops the compiler
+// from moving them and waits for the writes to land).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 }
 
 // B operand of the dX contraction, step qs (entries e = 16 qs + 8 h + i).

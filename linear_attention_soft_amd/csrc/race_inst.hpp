@@ -1,5 +1,6 @@
 // Launchers of one kernel instance; included by the per-dtype instance files.
 #pragma once
+#include "race_causal.hpp"
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
 
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, const
 template <typename T, int D, int PE, int LRP>
 struct Inst {
   using G = Geo<T, D, PE, LRP>;
+  static unsigned blocks4(int64_t units) { return (unsigned)((units + 3) / 4); }
   static void reduce(const NCArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_bucket_reduce<T, G>), g, dim3(256), 0, s, a);
   }
@@ -58,11 +60,39 @@ struct Inst {
                   dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, out);
   }
+  static void c_den(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_DEN>), g, dim3(256), 0, s, a);
+  }
+  static void c_o(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_O>), g, dim3(256), 0, s, a);
+  }
+  static void c_h(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_H>), g, dim3(256), 0, s, a);
+  }
+  static void c_dv(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_readout<T, G, true, RO_DV>), g, dim3(256), 0, s, a);
+  }
+  static void c_dq(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_transposed<T, G, false>), g, dim3(256), 0, s, a);
+  }
+  static void c_dk(const CArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_causal_transposed<T, G, true>), g, dim3(256), 0, s, a);
+  }
+  static void dx(const float* dpre, const float* W, int L, int P, int64_t N, int64_t BH, void* out, dim3 g,
+                 hipStream_t s) {
+    hipLaunchKernelGGL((race_dx<T, G>), g, dim3(256), 0, s, dpre, W, L, P, N, BH, out);
+  }
+  // nc: compile the non-causal kernels; causal: compile the causal ones
+  template <bool NC, bool CAUSAL>
   static KernelSet set(int dtype) {
     KernelSet k{};
     k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP;
-    k.reduce = reduce; k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv;
+    k.reduce = reduce;
     k.softbucket_dbg = dbg;
+    if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
+    if constexpr (CAUSAL) {
+      k.c_den = c_den; k.c_o = c_o; k.c_h = c_h; k.c_dv = c_dv; k.c_dq = c_dq; k.c_dk = c_dk; k.dx = dx;
+    }
     return k;
   }
 };

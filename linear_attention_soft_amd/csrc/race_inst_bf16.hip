@@ -4,9 +4,10 @@
 namespace race {
 const KernelSet* kernel_sets_bf16(int* count) {
   static const KernelSet sets[] = {
-      Inst<bf16, 64, 3, 32>::set(1),
-      Inst<bf16, 64, 4, 64>::set(1),
-      Inst<bf16, 128, 4, 32>::set(1),
+      Inst<bf16, 64, 3, 32>::template set<true, true>(1),
+      Inst<bf16, 64, 4, 64>::template set<true, true>(1),
+      Inst<bf16, 128, 4, 32>::template set<true, true>(1),
+      Inst<bf16, 128, 6, 256>::template set<false, true>(1),
   };
   *count = (int)(sizeof(sets) / sizeof(sets[0]));
   return sets;

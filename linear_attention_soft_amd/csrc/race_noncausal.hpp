@@ -34,8 +34,13 @@ struct NCArgs {
   float beta;
   int L, P;
   int64_t N;
-  int64_t chunk_tokens;     // tokens per workgroup, multiple of 128
+  int64_t chunk_tokens;     // tokens per workgroup
   int nchunk;
+  // race_bucket_reduce only: when tok_den is set, the value rows Y are divided by
+  // tok_den[token] (g = dO / Den) and the extra column holds tok_extra[token]
+  // instead of ones (the causal backward's gradient sums Phi_Q^T [g | h]).
+  const float* tok_den;
+  const float* tok_extra;
 };
 
 constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
@@ -217,6 +222,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   __shared__ frag Wf[G::NPT * G::KD * 64];
   __shared__ T PhiT[G::LRP * TTP];
   __shared__ T Bs[TT * BSP];
+  __shared__ float hsv[TT];
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
@@ -251,17 +257,28 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
       }
     // value rows of the wave's 32 tokens, 16 bytes per lane per step
     constexpr int CPR = G::D * (int)sizeof(T) / 16;      // 16-byte chunks per row
+    constexpr int EPC = 16 / (int)sizeof(T);              // elements per chunk
+    const float* den = a.tok_den ? a.tok_den + (size_t)bh * a.N : nullptr;
 #pragma unroll
     for (int it = 0; it < 32 * CPR / 64; ++it) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const int64_t trow = base + 32 * w + row;
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (trow < t_end) val = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
+      if (trow < t_end) {
+        val = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
+        if (den) {
+          const float inv = 1.f / den[trow];
+          T* e = reinterpret_cast<T*>(&val);
+#pragma unroll
+          for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
+        }
+      }
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
     }
+    if (a.tok_extra && h == 0) hsv[tl] = valid ? a.tok_extra[(size_t)bh * a.N + tok] : 0.f;
     __syncthreads();
-    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, nullptr, acc);
+    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, a.tok_extra ? hsv : nullptr, acc);
     __syncthreads();
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), acc);

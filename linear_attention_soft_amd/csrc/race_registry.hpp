@@ -12,13 +12,18 @@ typedef void (*nc_launch_fn)(const NCArgs&, dim3 grid, hipStream_t);
 typedef void (*c_launch_fn)(const CArgs&, dim3 grid, hipStream_t);
 typedef void (*dbg_launch_fn)(const void* X, const float* W, float beta, int L, int P, int64_t N,
                               float* out, dim3 grid, hipStream_t);
+typedef void (*dx_launch_fn)(const float* dpre, const float* W, int L, int P, int64_t N, int64_t BH, void* out,
+                             dim3 grid, hipStream_t);
 
 struct KernelSet {
   int dtype;   // race_dtype
   int D, PE, LRP;
-  nc_launch_fn reduce, readout, bwd_q, bwd_kv;
+  nc_launch_fn reduce;                     // bank / segment sums (both variants)
+  nc_launch_fn readout, bwd_q, bwd_kv;     // non-causal; null when not compiled
   dbg_launch_fn softbucket_dbg;
-  c_launch_fn causal_fwd, causal_bwd_q, causal_bwd_kv;   // may be null
+  // causal; null when not compiled
+  c_launch_fn c_den, c_o, c_h, c_dv, c_dq, c_dk;
+  dx_launch_fn dx;
 };
 
 const KernelSet* kernel_sets_f32(int* count);
