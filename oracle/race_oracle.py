@@ -54,6 +54,9 @@ __all__ = [
     "forward",
     "backward",
     "state_head",
+    "query_grads",
+    "grad_banks",
+    "key_grads",
 ]
 
 
@@ -77,7 +80,7 @@ def _projected(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     """
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
-    pre = np.einsum("nd,lpd->lnp", X, W)
+    pre = np.matmul(X[None], W.transpose(0, 2, 1))
     return np.tanh(pre)
 
 
@@ -91,7 +94,7 @@ def soft_assign(X: np.ndarray, W: np.ndarray, beta: float) -> np.ndarray:
     """
     U = _projected(X, W)                       # (L, N, P)
     C = corners(W.shape[1])                    # (R, P)
-    logits = float(beta) * np.einsum("lnp,rp->lnr", U, C)
+    logits = float(beta) * np.matmul(U, C.T)
     logits = logits - logits.max(axis=-1, keepdims=True)
     E = np.exp(logits)
     return E / E.sum(axis=-1, keepdims=True)
@@ -120,7 +123,7 @@ def bucket_stats(Phi_K: np.ndarray, V: np.ndarray):
     """
     Phi_K = np.asarray(Phi_K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
-    content = np.einsum("lnr,nc->lrc", Phi_K, V)
+    content = np.matmul(Phi_K.transpose(0, 2, 1), V)
     mass = Phi_K.sum(axis=1)
     return content, mass
 
@@ -133,8 +136,8 @@ def readout(Phi_Q: np.ndarray, content: np.ndarray, mass: np.ndarray):
     tables"; reading notes section 2.5).  Returns (O, Num, Den).
     """
     Phi_Q = np.asarray(Phi_Q, dtype=np.float64)
-    Num = np.einsum("lnr,lrc->nc", Phi_Q, content)
-    Den = np.einsum("lnr,lr->n", Phi_Q, mass)
+    Num = np.matmul(Phi_Q, content).sum(axis=0)
+    Den = np.matmul(Phi_Q, mass[:, :, None]).sum(axis=0)[:, 0]
     return Num / Den[:, None], Num, Den
 
 
@@ -184,13 +187,15 @@ def _prefix_states(Phi_K, V, t0, t1, content0, mass0):
     return content0[:, None] + pc, mass0[:, None] + pm
 
 
-def causal_forward_head(Q, K, V, W, beta, block=256, return_den=False):
+def causal_forward_head(Q, K, V, W, beta, block=256, return_den=False, content0=None, mass0=None):
     """Causal RACE output of one head through inclusive prefix sums.
 
     Same quantities as ``causal_forward_head_loop``; the running sums
     content_t = sum_{j<=t} phi(K_j) V_j^T and mass_t = sum_{j<=t} phi(K_j)
     are formed with cumulative sums, ``block`` tokens at a time only to bound
-    memory (the sums themselves are the plain prefix sums).
+    memory (the sums themselves are the plain prefix sums).  ``content0`` and
+    ``mass0`` (default zero) are the bank of keys that precede this block of
+    the sequence, so a long sequence can be evaluated piece by piece.
     """
     Phi_Q = soft_assign(Q, W, beta)
     Phi_K = soft_assign(K, W, beta)
@@ -199,8 +204,8 @@ def causal_forward_head(Q, K, V, W, beta, block=256, return_den=False):
     dv = V.shape[1]
     O = np.empty((N, dv))
     Den = np.empty(N)
-    c0 = np.zeros((L, R, dv))
-    m0 = np.zeros((L, R))
+    c0 = np.zeros((L, R, dv)) if content0 is None else np.array(content0, dtype=np.float64)
+    m0 = np.zeros((L, R)) if mass0 is None else np.array(mass0, dtype=np.float64)
     for t0 in range(0, N, block):
         t1 = min(N, t0 + block)
         pc, pm = _prefix_states(Phi_K, V, t0, t1, c0, m0)
@@ -238,12 +243,43 @@ def _assign_backward(X, W, beta, Phi, dPhi):
     U = _projected(X, W)                                   # (L, N, P)
     C = corners(W.shape[1])
     dLam = Phi * (dPhi - np.sum(Phi * dPhi, axis=-1, keepdims=True))
-    dU = float(beta) * np.einsum("lnr,rp->lnp", dLam, C)
+    dU = float(beta) * np.matmul(dLam, C)
     dPre = dU * (1.0 - U * U)
-    return np.einsum("lnp,lpd->nd", dPre, np.asarray(W, dtype=np.float64))
+    return np.matmul(dPre, np.asarray(W, dtype=np.float64)).sum(axis=0)
 
 
-def backward_head(Q, K, V, W, beta, dO, causal=False):
+def query_grads(Q, dO, W, beta, content, mass):
+    """Query-side gradient of sum(O * dO) for rows that read the bank
+    (content, mass): g = dO / Den, h = -rowdot(dO, O) / Den,
+    dPhi_Q = g content^T + h mass^T, then softmax / tanh / projection backward.
+    Returns (dQ, O, Den, g, h)."""
+    Phi_Q = soft_assign(Q, W, beta)
+    O, _, Den = readout(Phi_Q, content, mass)
+    dO = np.asarray(dO, dtype=np.float64)
+    g = dO / Den[:, None]
+    h = -np.sum(dO * O, axis=1) / Den
+    dPhi_Q = np.matmul(g[None], content.transpose(0, 2, 1)) + h[None, :, None] * mass[:, None, :]
+    return _assign_backward(Q, W, beta, Phi_Q, dPhi_Q), O, Den, g, h
+
+
+def grad_banks(Q, W, beta, g, h):
+    """Gradient banks dcontent = Phi_Q^T g (L, R, d) and dmass = Phi_Q^T h (L, R)
+    summed over the given query rows."""
+    Phi_Q = soft_assign(Q, W, beta)
+    return np.matmul(Phi_Q.transpose(0, 2, 1), g), np.matmul(Phi_Q.transpose(0, 2, 1), h[:, None])[:, :, 0]
+
+
+def key_grads(K, V, W, beta, dcontent, dmass):
+    """Key-side gradients for rows that wrote the bank: dV = sum_l Phi_K dcontent,
+    dPhi_K = V dcontent^T + 1 dmass^T, then softmax / tanh / projection backward."""
+    Phi_K = soft_assign(K, W, beta)
+    V = np.asarray(V, dtype=np.float64)
+    dV = np.matmul(Phi_K, dcontent).sum(axis=0)
+    dPhi_K = np.matmul(V[None], dcontent.transpose(0, 2, 1)) + dmass[:, None, :]
+    return _assign_backward(K, W, beta, Phi_K, dPhi_K), dV
+
+
+def backward_head(Q, K, V, W, beta, dO, causal=False, content0=None, mass0=None):
     """Exact gradient (dQ, dK, dV) of sum(O * dO) for one head.
 
     With g = dO / Den and h = -rowdot(dO, O) / Den:
@@ -252,54 +288,52 @@ def backward_head(Q, K, V, W, beta, dO, causal=False):
     1 dmass^T.  Causal: the contents/masses read by query t are the prefix
     sums at t, and the gradients reaching key j are the suffix sums over
     t >= j.  Then softmax, tanh and projection backward on both sides.
+    Causal only: content0 / mass0 are the bank of earlier keys (the rows are
+    then the last block of a longer sequence; gradients of the earlier keys
+    are not returned).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     dO = np.asarray(dO, dtype=np.float64)
+    if not causal:
+        content, mass = state_head(K, V, W, beta)
+        dQ, _, _, g, h = query_grads(Q, dO, W, beta, content, mass)
+        dcontent, dmass = grad_banks(Q, W, beta, g, h)
+        dK, dV = key_grads(K, V, W, beta, dcontent, dmass)
+        return dQ, dK, dV
     Phi_Q = soft_assign(Q, W, beta)
     Phi_K = soft_assign(K, W, beta)
     L, N, R = Phi_Q.shape
     dv = V.shape[1]
-    if not causal:
-        content, mass = bucket_stats(Phi_K, V)
-        O, _, Den = readout(Phi_Q, content, mass)
-        g = dO / Den[:, None]
-        h = -np.sum(dO * O, axis=1) / Den
-        dPhi_Q = np.einsum("nc,lrc->lnr", g, content) + h[None, :, None] * mass[:, None, :]
-        dcontent = np.einsum("lnr,nc->lrc", Phi_Q, g)
-        dmass = np.einsum("lnr,n->lr", Phi_Q, h)
-        dV = np.einsum("lnr,lrc->nc", Phi_K, dcontent)
-        dPhi_K = np.einsum("nc,lrc->lnr", V, dcontent) + dmass[:, None, :]
-    else:
-        O, Den = causal_forward_head(Q, K, V, W, beta, return_den=True)
-        g = dO / Den[:, None]
-        h = -np.sum(dO * O, axis=1) / Den
-        dPhi_Q = np.empty((L, N, R))
-        dPhi_K = np.empty((L, N, R))
-        dV = np.empty((N, dv))
-        block = 256
-        # Prefix sums (read by each query).
-        c0 = np.zeros((L, R, dv))
-        m0 = np.zeros((L, R))
-        for t0 in range(0, N, block):
-            t1 = min(N, t0 + block)
-            pc, pm = _prefix_states(Phi_K, V, t0, t1, c0, m0)
-            dPhi_Q[:, t0:t1] = (np.einsum("nc,lnrc->lnr", g[t0:t1], pc)
-                                + h[None, t0:t1, None] * pm)
-            c0, m0 = pc[:, -1], pm[:, -1]
-        # Suffix sums D_j = sum_{t>=j} phi(Q_t) g_t^T, E_j = sum_{t>=j} phi(Q_t) h_t.
-        Dn = np.zeros((L, R, dv))
-        En = np.zeros((L, R))
-        for t1 in range(N, 0, -block):
-            t0 = max(0, t1 - block)
-            outer = Phi_Q[:, t0:t1, :, None] * g[None, t0:t1, None, :]
-            sD = np.cumsum(outer[:, ::-1], axis=1)[:, ::-1] + Dn[:, None]
-            sE = np.cumsum(Phi_Q[:, t0:t1][:, ::-1] * h[None, t0:t1][:, ::-1, None],
-                           axis=1)[:, ::-1] + En[:, None]
-            dV[t0:t1] = np.einsum("lnr,lnrc->nc", Phi_K[:, t0:t1], sD)
-            dPhi_K[:, t0:t1] = np.einsum("nc,lnrc->lnr", V[t0:t1], sD) + sE
-            Dn, En = sD[:, 0], sE[:, 0]
+    O, Den = causal_forward_head(Q, K, V, W, beta, return_den=True, content0=content0, mass0=mass0)
+    g = dO / Den[:, None]
+    h = -np.sum(dO * O, axis=1) / Den
+    dPhi_Q = np.empty((L, N, R))
+    dPhi_K = np.empty((L, N, R))
+    dV = np.empty((N, dv))
+    block = 256
+    # Prefix sums (read by each query).
+    c0 = np.zeros((L, R, dv)) if content0 is None else np.array(content0, dtype=np.float64)
+    m0 = np.zeros((L, R)) if mass0 is None else np.array(mass0, dtype=np.float64)
+    for t0 in range(0, N, block):
+        t1 = min(N, t0 + block)
+        pc, pm = _prefix_states(Phi_K, V, t0, t1, c0, m0)
+        dPhi_Q[:, t0:t1] = (np.einsum("nc,lnrc->lnr", g[t0:t1], pc)
+                            + h[None, t0:t1, None] * pm)
+        c0, m0 = pc[:, -1], pm[:, -1]
+    # Suffix sums D_j = sum_{t>=j} phi(Q_t) g_t^T, E_j = sum_{t>=j} phi(Q_t) h_t.
+    Dn = np.zeros((L, R, dv))
+    En = np.zeros((L, R))
+    for t1 in range(N, 0, -block):
+        t0 = max(0, t1 - block)
+        outer = Phi_Q[:, t0:t1, :, None] * g[None, t0:t1, None, :]
+        sD = np.cumsum(outer[:, ::-1], axis=1)[:, ::-1] + Dn[:, None]
+        sE = np.cumsum(Phi_Q[:, t0:t1][:, ::-1] * h[None, t0:t1][:, ::-1, None],
+                       axis=1)[:, ::-1] + En[:, None]
+        dV[t0:t1] = np.einsum("lnr,lnrc->nc", Phi_K[:, t0:t1], sD)
+        dPhi_K[:, t0:t1] = np.einsum("nc,lnrc->lnr", V[t0:t1], sD) + sE
+        Dn, En = sD[:, 0], sE[:, 0]
     dQ = _assign_backward(Q, W, beta, Phi_Q, dPhi_Q)
     dK = _assign_backward(K, W, beta, Phi_K, dPhi_K)
     return dQ, dK, dV

@@ -424,3 +424,38 @@ def test_backward_causal_equals_masked_brute_force_gradient():
             lm = loss(*a)
             num[idx] = (lp - lm) / (2 * eps)
         assert np.abs(num - G).max() <= 1e-6 * max(1.0, np.abs(G).max())
+
+
+def test_causal_blocks_with_initial_bank_equal_whole_sequence():
+    """Evaluating the tail of a causal sequence from the bank of its prefix
+    gives the same outputs and gradients of the tail as the whole sequence."""
+    rng = np.random.default_rng(60)
+    N, d, L, P, beta, cut = 90, 5, 2, 3, 3.0, 57
+    Q, K, V, W = _rand_head(rng, N, d, L, P)
+    dO = rng.standard_normal((N, d))
+    O = orc.causal_forward_head(Q, K, V, W, beta)
+    dQ, dK, dV = orc.backward_head(Q, K, V, W, beta, dO, True)
+    c0, m0 = orc.state_head(K[:cut], V[:cut], W, beta)
+    Ot = orc.causal_forward_head(Q[cut:], K[cut:], V[cut:], W, beta, content0=c0, mass0=m0)
+    np.testing.assert_allclose(Ot, O[cut:], rtol=1e-12, atol=1e-13)
+    tq, tk, tv = orc.backward_head(Q[cut:], K[cut:], V[cut:], W, beta, dO[cut:], True, content0=c0, mass0=m0)
+    for a, b in ((tq, dQ[cut:]), (tk, dK[cut:]), (tv, dV[cut:])):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * np.abs(b).max())
+
+
+def test_bank_level_pieces_compose_to_backward():
+    """query_grads / grad_banks / key_grads evaluated in two halves and summed
+    give the single-call gradients (bank sums are additive over rows)."""
+    rng = np.random.default_rng(61)
+    Q, K, V, W = _rand_head(rng, 70, 6, 2, 3)
+    dO = rng.standard_normal((70, 6))
+    dQ, dK, dV = orc.backward_head(Q, K, V, W, 2.0, dO, False)
+    content, mass = orc.state_head(K, V, W, 2.0)
+    parts = [orc.query_grads(Q[s], dO[s], W, 2.0, content, mass) for s in (slice(0, 30), slice(30, 70))]
+    np.testing.assert_allclose(np.concatenate([p[0] for p in parts]), dQ, rtol=1e-12, atol=1e-14)
+    banks = [orc.grad_banks(Q[s], W, 2.0, p[3], p[4]) for s, p in zip((slice(0, 30), slice(30, 70)), parts)]
+    dc = banks[0][0] + banks[1][0]
+    dm = banks[0][1] + banks[1][1]
+    gk, gv = orc.key_grads(K, V, W, 2.0, dc, dm)
+    np.testing.assert_allclose(gk, dK, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(gv, dV, rtol=1e-11, atol=1e-13)
