@@ -38,10 +38,15 @@ ROW_PASSES = {
     "race_readout_norm": 2,    # read Q, write O
     "race_bwd_q": 3,           # read Q, dO, write dQ
     "race_bwd_kv": 4,          # read K, V, write dK, dV
-    "race_causal_fwd": 4,      # read Q, K, V, write O
-    "race_causal_bwd_q": 5,    # read Q, K, V, dO, write dQ
-    "race_causal_bwd_kv": 6,   # read Q, K, V, dO, write dK, dV
     "race_causal_segsum": 2,   # read K, V
+    "race_causal_den": 2,      # read Q, K
+    "race_causal_fwd": 4,      # read Q, K, V, write O
+    "race_causal_h": 4,        # read Q, K, V, dO
+    "race_causal_gradsum": 2,  # read Q, dO
+    "race_causal_dv": 4,       # read K, Q, dO, write dV
+    "race_causal_dphi_q": 4,   # read Q, K, V, dO
+    "race_causal_dphi_k": 4,   # read K, Q, dO, V
+    "race_causal_dx": 2,       # write dQ and dK
 }
 
 

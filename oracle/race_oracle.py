@@ -55,6 +55,7 @@ __all__ = [
     "backward",
     "state_head",
     "query_grads",
+    "query_terms",
     "grad_banks",
     "key_grads",
 ]
@@ -136,8 +137,10 @@ def readout(Phi_Q: np.ndarray, content: np.ndarray, mass: np.ndarray):
     tables"; reading notes section 2.5).  Returns (O, Num, Den).
     """
     Phi_Q = np.asarray(Phi_Q, dtype=np.float64)
-    Num = np.matmul(Phi_Q, content).sum(axis=0)
-    Den = np.matmul(Phi_Q, mass[:, :, None]).sum(axis=0)[:, 0]
+    L, N, R = Phi_Q.shape
+    F = Phi_Q.transpose(1, 0, 2).reshape(N, L * R)        # tables side by side
+    Num = F @ np.asarray(content, dtype=np.float64).reshape(L * R, -1)
+    Den = F @ np.asarray(mass, dtype=np.float64).reshape(L * R)
     return Num / Den[:, None], Num, Den
 
 
@@ -248,24 +251,31 @@ def _assign_backward(X, W, beta, Phi, dPhi):
     return np.matmul(dPre, np.asarray(W, dtype=np.float64)).sum(axis=0)
 
 
-def query_grads(Q, dO, W, beta, content, mass):
-    """Query-side gradient of sum(O * dO) for rows that read the bank
-    (content, mass): g = dO / Den, h = -rowdot(dO, O) / Den,
-    dPhi_Q = g content^T + h mass^T, then softmax / tanh / projection backward.
-    Returns (dQ, O, Den, g, h)."""
+def query_terms(Q, dO, W, beta, content, mass):
+    """For query rows that read the bank (content, mass): Phi_Q, O, Den and the
+    upstream terms g = dO / Den, h = -rowdot(dO, O) / Den."""
     Phi_Q = soft_assign(Q, W, beta)
     O, _, Den = readout(Phi_Q, content, mass)
     dO = np.asarray(dO, dtype=np.float64)
     g = dO / Den[:, None]
-    h = -np.sum(dO * O, axis=1) / Den
+    h = -np.einsum("nc,nc->n", dO, O) / Den
+    return Phi_Q, O, Den, g, h
+
+
+def query_grads(Q, dO, W, beta, content, mass):
+    """Query-side gradient of sum(O * dO) for rows that read the bank
+    (content, mass): dPhi_Q = g content^T + h mass^T, then softmax / tanh /
+    projection backward.  Returns (dQ, O, Den, g, h)."""
+    Phi_Q, O, Den, g, h = query_terms(Q, dO, W, beta, content, mass)
     dPhi_Q = np.matmul(g[None], content.transpose(0, 2, 1)) + h[None, :, None] * mass[:, None, :]
     return _assign_backward(Q, W, beta, Phi_Q, dPhi_Q), O, Den, g, h
 
 
-def grad_banks(Q, W, beta, g, h):
+def grad_banks(Q, W, beta, g, h, Phi_Q=None):
     """Gradient banks dcontent = Phi_Q^T g (L, R, d) and dmass = Phi_Q^T h (L, R)
-    summed over the given query rows."""
-    Phi_Q = soft_assign(Q, W, beta)
+    summed over the given query rows (Phi_Q may be passed in when known)."""
+    if Phi_Q is None:
+        Phi_Q = soft_assign(Q, W, beta)
     return np.matmul(Phi_Q.transpose(0, 2, 1), g), np.matmul(Phi_Q.transpose(0, 2, 1), h[:, None])[:, :, 0]
 
 
