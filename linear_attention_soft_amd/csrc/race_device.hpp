@@ -228,7 +228,21 @@ __device__ void build_wt_frags(const float* __restrict__ W, int L, int P,
   }
 }
 
+__device__ __forceinline__ void wave_lds_sync();
+
 // ---------------------------------------------------------------- per-token front end
+// Branch-free load of a token row's projection B operand.  Callers clamp the
+// row to a valid one and discard or zero the features of tokens past the end,
+// so prefetched loads never sit behind a data-dependent branch (which would
+// make the compiler wait for them early).
+template <typename T, class G>
+__device__ __forceinline__ void load_row_frags_nb(const T* __restrict__ x, typename Eng<T>::frag (&xf)[G::KD]) {
+  using E = Eng<T>;
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int q = 0; q < G::KD; ++q) xf[q] = *reinterpret_cast<const typename E::frag*>(x + 16 * q + 8 * h);
+}
+
 // Load the B operand of the projection for token row `x` (nullptr -> zeros).
 template <typename T, class G>
 __device__ __forceinline__ void load_row_frags(const T* __restrict__ x, typename Eng<T>::frag (&xf)[G::KD]) {
@@ -459,6 +473,54 @@ __device__ __forceinline__ void store_tl_row(T* __restrict__ row, const float (&
       *reinterpret_cast<typename Eng<T>::vec4*>(row + 32 * mt + 8 * j + 4 * h) = w;
     }
 }
+
+// Store one 32-column tile (accumulator of a C^T[c][tok] MFMA) of a token row.
+template <typename T>
+__device__ __forceinline__ void store_tl_tile(T* __restrict__ row, int ct, const f32x16& acc, float scale) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    typename Eng<T>::vec4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = (T)(acc[4 * j + k] * scale);
+    *reinterpret_cast<typename Eng<T>::vec4*>(row + 32 * ct + 8 * j + 4 * h) = w;
+  }
+}
+
+// Output staging: a wave writes its 32 x D output tile into LDS (row stride
+// D + 8 elements) from TLAYOUT accumulators, then stores whole rows with
+// 16-byte lanes (four 256-byte rows per instruction at d = 128).
+template <int D, typename T>
+struct OutStage {
+  static constexpr int SP = D + 8;
+  static constexpr int ELEMS = 32 * SP;
+  __device__ __forceinline__ static void put(T* __restrict__ st, int ct, const f32x16& acc, float scale) {
+    const int lane = lane_id(), n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typename Eng<T>::vec4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (T)(acc[4 * j + k] * scale);
+      *reinterpret_cast<typename Eng<T>::vec4*>(st + n * SP + 32 * ct + 8 * j + 4 * h) = w;
+    }
+  }
+  // rows t0 .. t0+31 of out (only rows < t_end are written)
+  __device__ __forceinline__ static void flush(const T* __restrict__ st, T* __restrict__ out, int64_t t0,
+                                               int64_t t_end) {
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int CPR = D / EPC;
+    const int lane = lane_id();
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+      const int flat = it * 64 + lane;
+      const int row = flat / CPR, ch = flat % CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + row * SP + ch * EPC);
+      if (t0 + row < t_end) *reinterpret_cast<uint4*>(out + (t0 + row) * D + ch * EPC) = v;
+    }
+    wave_lds_sync();
+  }
+};
 
 template <typename T, int D>
 __device__ __forceinline__ void load_tl_row(const T* __restrict__ row, float (&x)[D / 2]) {

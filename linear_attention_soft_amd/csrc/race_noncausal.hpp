@@ -158,6 +158,24 @@ __device__ __forceinline__ void dx_mma(const typename Eng<T>::frag* __restrict__
   }
 }
 
+// dX = dPre . W for the wave's 32 tokens, written into the staging tile.
+template <typename T, class G>
+__device__ __forceinline__ void dx_mma_stage(const typename Eng<T>::frag* __restrict__ WTf,
+                                             const float (&dpre)[G::NHP], T* __restrict__ st) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+  typename E::frag bq[G::NQS];
+#pragma unroll
+  for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dpre, qs);
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int qs = 0; qs < G::NQS; ++qs) E::mma(WTf[(ct * G::NQS + qs) * 64 + lane], bq[qs], acc);
+    OutStage<G::D, T>::put(st, ct, acc, 1.f);
+  }
+}
+
 // Cooperative bucket reduction of one 128-token tile: acc[j] (tile w + 4 j of
 // the (AT) x (CT + 1) grid) += PhiT[lr][tok] * [B | extra][tok][c].
 // The extra column tile is all ones (mass) or hs[tok] (gradient mass).
@@ -239,14 +257,29 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
 #pragma unroll
   for (int j = 0; j < NTW; ++j) acc[j] = zero16();
 
-  for (int64_t base = t_begin; base < t_end; base += TT) {
-    const int tl = 32 * w + n;
+  constexpr int CPR = G::D * (int)sizeof(T) / 16;      // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);              // elements per chunk
+  constexpr int NCH = 32 * CPR / 64;                    // chunks per lane per tile
+  const float* den = a.tok_den ? a.tok_den + (size_t)bh * a.N : nullptr;
+  const int tl = 32 * w + n;
+  const int64_t last = t_end - 1;
+  // rows of the wave's 32 tokens: key rows as projection operands, value rows
+  // as 16-byte chunks (row = flat / CPR) for the LDS tile
+  auto load_tile = [&](int64_t b, frag (&xf)[G::KD], uint4 (&yv)[NCH]) {
+    load_row_frags_nb<T, G>(X + min(b + tl, last) * G::D, xf);
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      const int flat = it * 64 + lane;
+      const int row = flat / CPR, ch = flat % CPR;
+      const int64_t trow = min(b + 32 * w + row, last);
+      yv[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
+    }
+  };
+  auto tile = [&](const frag (&cx)[G::KD], const uint4 (&cy)[NCH], int64_t base) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
-    frag xf[G::KD];
-    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, xf, pre);
+    project<T, G>(Wf, cx, pre);
     soft_assign<G>(pre, beta2, a.L, u, phi);
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
@@ -255,24 +288,17 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
         const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
         PhiT[lr * TTP + tl] = valid ? (T)phi[16 * at + v] : (T)0.f;
       }
-    // value rows of the wave's 32 tokens, 16 bytes per lane per step
-    constexpr int CPR = G::D * (int)sizeof(T) / 16;      // 16-byte chunks per row
-    constexpr int EPC = 16 / (int)sizeof(T);              // elements per chunk
-    const float* den = a.tok_den ? a.tok_den + (size_t)bh * a.N : nullptr;
 #pragma unroll
-    for (int it = 0; it < 32 * CPR / 64; ++it) {
+    for (int it = 0; it < NCH; ++it) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const int64_t trow = base + 32 * w + row;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (trow < t_end) {
-        val = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
-        if (den) {
-          const float inv = 1.f / den[trow];
-          T* e = reinterpret_cast<T*>(&val);
+      uint4 val = trow < t_end ? cy[it] : make_uint4(0, 0, 0, 0);
+      if (den && trow < t_end) {
+        const float inv = 1.f / den[trow];
+        T* e = reinterpret_cast<T*>(&val);
 #pragma unroll
-          for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
-        }
+        for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
       }
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
     }
@@ -280,6 +306,21 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
     __syncthreads();
     reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, a.tok_extra ? hsv : nullptr, acc);
     __syncthreads();
+  };
+  frag xa[G::KD], xb[G::KD];
+  uint4 ya[NCH], yb[NCH];
+  int64_t base = t_begin;
+  load_tile(base, xa, ya);
+  while (base < t_end) {
+    load_tile(base + TT, xb, yb);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xa, ya, base);
+    base += TT;
+    if (base >= t_end) break;
+    load_tile(base + TT, xa, ya);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xb, yb, base);
+    base += TT;
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), acc);
 }
@@ -291,6 +332,7 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   using frag = typename E::frag;
   __shared__ frag Wf[G::NPT * G::KD * 64];
   __shared__ frag RF[(G::CT + 1) * G::KL * E::NSPLIT * 64];
+  __shared__ T OS[4][OutStage<G::D, T>::ELEMS];
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
   build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
@@ -303,27 +345,45 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
   const float beta2 = 2.f * a.beta;
 
-  for (int64_t base = t_begin + 32 * w; base < t_end; base += TT) {
+  const int64_t last = t_end - 1;
+  // one 32-token tile: rows in cx (loaded one tile ahead)
+  auto tile = [&](const frag (&cx)[G::KD], int64_t base) {
     const int64_t tok = base + n;
     const bool valid = tok < t_end;
-    frag xf[G::KD];
-    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, xf, pre);
+    project<T, G>(Wf, cx, pre);
     soft_assign<G>(pre, beta2, a.L, u, phi);
     f32x16 acc[G::CT + 1];
     readout_mma<T, G>(RF, phi, acc);
     const float inv = 1.f / acc[G::CT][0];
-    float o[G::D / 2];
+    (void)valid;
 #pragma unroll
-    for (int mt = 0; mt < G::CT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[16 * mt + v] = acc[mt][v] * inv;
-    if (valid) store_tl_row<T, G::D>(O + tok * G::D, o);
+    for (int mt = 0; mt < G::CT; ++mt) OutStage<G::D, T>::put(OS[w], mt, acc[mt], inv);
+    OutStage<G::D, T>::flush(OS[w], O, base, t_end);
+  };
+  // double-buffered rows: each half prefetches into the set the other half uses
+  frag xa[G::KD], xb[G::KD];
+  int64_t base = t_begin + 32 * w;
+  load_row_frags_nb<T, G>(X + min(base + n, last) * G::D, xa);
+  while (base < t_end) {
+    load_row_frags_nb<T, G>(X + min(base + TT + n, last) * G::D, xb);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this tile's work
+    tile(xa, base);
+    base += TT;
+    if (base >= t_end) break;
+    load_row_frags_nb<T, G>(X + min(base + TT + n, last) * G::D, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xb, base);
+    base += TT;
   }
 }
 
 // ------------------------------------------------------------------ race_bwd_q
+// Per token (Den from float32 Phi_Q):
+//   A[lr]   = content[lr] . dO          (bank hi + lo times the exact dO row)
+//   h       = -(dO . Num) / Den^2 = -(sum_lr phi[lr] A[lr]) / Den^2
+//   dPhi_Q  = A / Den + mass h
+// and the gradient bank is (Phi_Q / Den)^T dO with mass column -(dO . O).
 template <typename T, class G>
 __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
   using E = Eng<T>;
@@ -333,21 +393,20 @@ __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
   constexpr int BSP = G::D + Pad<T>::v;
   constexpr int NTW = cdiv(G::AT * (G::CT + 1), 4);
   __shared__ frag Wf[G::NPT * G::KD * 64];
-  __shared__ frag RF[(G::CT + 1) * G::KL * NS * 64];
   __shared__ frag DF[G::AT * G::KD * NS * 64];
   __shared__ frag WTf[G::CT * G::NQS * 64];
   __shared__ float massL[G::LRP];
   __shared__ T PhiT[G::LRP * TTP];
   __shared__ T Bs[TT * BSP];
   __shared__ float hs[TT];
+  static_assert(BSP == OutStage<G::D, T>::SP, "dQ is staged in the wave's rows of Bs");
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const float* content = a.st_content + (size_t)bh * G::LRP * G::D;
   const float* mass = a.st_mass + (size_t)bh * G::LRP;
   build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
-  build_readout_frags<T, G>(content, mass, RF);
-  build_bank_rows_frags<T, G, true>(content, DF);
+  build_bank_rows_frags<T, G, false>(content, DF);
   build_wt_frags<T, G>(a.W, a.L, a.P, WTf);
   for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) massL[i] = mass[i];
   __syncthreads();
@@ -363,87 +422,100 @@ __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
 #pragma unroll
   for (int j = 0; j < NTW; ++j) racc[j] = zero16();
 
-  for (int64_t base = t_begin; base < t_end; base += TT) {
-    const int tl = 32 * w + n;
+  const int tl = 32 * w + n;
+  const int64_t last = t_end - 1;
+  auto tile = [&](const frag (&cx)[G::KD], const frag (&yy)[G::KD], int64_t base) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
-    frag xf[G::KD];
-    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+    frag cy[G::KD];
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) cy[q] = valid ? yy[q] : E::zero();
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, xf, pre);
+    project<T, G>(Wf, cx, pre);
     soft_assign<G>(pre, beta2, a.L, u, phi);
     if (!valid) {
 #pragma unroll
       for (int i = 0; i < G::LRP / 2; ++i) phi[i] = 0.f;
     }
-    f32x16 acc[G::CT + 1];
-    readout_mma<T, G>(RF, phi, acc);
-    const float den = valid ? acc[G::CT][0] : 1.f;
-    const float inv = 1.f / den;
-    float g[G::D / 2];
-    if (valid) load_tl_row<T, G::D>(dO + tok * G::D, g);
-    else {
+    // Den = sum_lr phi mass;  A = content . dO
+    float den = 0.f;
 #pragma unroll
-      for (int i = 0; i < G::D / 2; ++i) g[i] = 0.f;
-    }
-    float hd = 0.f;
+    for (int at = 0; at < G::AT; ++at)
 #pragma unroll
-    for (int mt = 0; mt < G::CT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hd += g[16 * mt + v] * acc[mt][v];
-    hd += xor32(hd);
-    const float hval = -hd * inv * inv;        // -(dO . O) / Den with O = Num / Den
-#pragma unroll
-    for (int i = 0; i < G::D / 2; ++i) g[i] *= inv;
-
-    // dPhi_Q[lr] = content[lr] . g + mass[lr] h
-    float dphi[G::LRP / 2];
+      for (int v = 0; v < 16; ++v) den += phi[16 * at + v] * massL[32 * at + 8 * (v >> 2) + 4 * h + (v & 3)];
+    den += xor32(den);
+    const float inv = valid ? 1.f / den : 0.f;
+    float av[G::LRP / 2];
 #pragma unroll
     for (int at = 0; at < G::AT; ++at) {
       f32x16 d = zero16();
 #pragma unroll
-      for (int q = 0; q < G::KD; ++q) {
-        frag gh, gl;
-        tl_frag_split<T, G::D>(g, q, gh, gl);
-        E::mma(DF[((at * G::KD + q) * NS + 0) * 64 + lane], gh, d);
-        if (NS == 2) {
-          E::mma(DF[((at * G::KD + q) * NS + 0) * 64 + lane], gl, d);
-          E::mma(DF[((at * G::KD + q) * NS + (NS - 1)) * 64 + lane], gh, d);
-        }
-      }
+      for (int q = 0; q < G::KD; ++q)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-        dphi[16 * at + v] = d[v] + massL[lr] * hval;
-      }
+        for (int sp = 0; sp < NS; ++sp) E::mma(DF[((at * G::KD + q) * NS + sp) * 64 + lane], cy[q], d);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) av[16 * at + v] = d[v];
     }
-    float dpre[G::NHP];
-    assign_backward<G>(phi, dphi, u, a.beta, dpre);
-    float dx[G::D / 2];
-    dx_mma<T, G>(WTf, dpre, dx);
-    if (valid) store_tl_row<T, G::D>(dQ + tok * G::D, dx);
-
-    // stage Phi_Q^T, g, h for dcontent = Phi_Q^T g, dmass = Phi_Q^T h
+    float hd = 0.f;
+#pragma unroll
+    for (int i = 0; i < G::LRP / 2; ++i) hd += phi[i] * av[i];
+    hd += xor32(hd);                           // dO . Num
+    const float hval = -hd * inv * inv;        // h = -(dO . O) / Den
+    float dphi[G::LRP / 2];
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-        PhiT[lr * TTP + tl] = (T)phi[16 * at + v];
+        dphi[16 * at + v] = av[16 * at + v] * inv + massL[lr] * hval;
+      }
+    float dpre[G::NHP];
+    assign_backward<G>(phi, dphi, u, a.beta, dpre);
+    // the wave's 32 rows of Bs are free until the dO rows are staged below
+    dx_mma_stage<T, G>(WTf, dpre, Bs + 32 * w * BSP);
+    OutStage<G::D, T>::flush(Bs + 32 * w * BSP, dQ, base + 32 * w, t_end);
+
+    // stage (Phi_Q / Den)^T, dO rows and -(dO . O) for the gradient bank
+#pragma unroll
+    for (int at = 0; at < G::AT; ++at)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+        PhiT[lr * TTP + tl] = (T)(phi[16 * at + v] * inv);
       }
 #pragma unroll
-    for (int mt = 0; mt < G::CT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typename E::vec4 wv;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = (T)g[16 * mt + 4 * j + k];
-        *reinterpret_cast<typename E::vec4*>(Bs + tl * BSP + 32 * mt + 8 * j + 4 * h) = wv;
-      }
-    if (h == 0) hs[tl] = valid ? hval : 0.f;
+    for (int q = 0; q < G::KD; ++q)
+      *reinterpret_cast<frag*>(Bs + tl * BSP + 16 * q + 8 * h) = cy[q];
+    if (h == 0) hs[tl] = valid ? -hd * inv : 0.f;
     __syncthreads();
     reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, hs, racc);
     __syncthreads();
+  };
+  frag xa[G::KD], ya[G::KD], xb[G::KD], yb[G::KD];
+  int64_t base = t_begin;
+  {
+    const int64_t r = min(base + tl, last);
+    load_row_frags_nb<T, G>(X + r * G::D, xa);
+    load_row_frags_nb<T, G>(dO + r * G::D, ya);
+  }
+  while (base < t_end) {
+    {
+      const int64_t r = min(base + TT + tl, last);
+      load_row_frags_nb<T, G>(X + r * G::D, xb);
+      load_row_frags_nb<T, G>(dO + r * G::D, yb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xa, ya, base);
+    base += TT;
+    if (base >= t_end) break;
+    {
+      const int64_t r = min(base + TT + tl, last);
+      load_row_frags_nb<T, G>(X + r * G::D, xa);
+      load_row_frags_nb<T, G>(dO + r * G::D, ya);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xb, yb, base);
+    base += TT;
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), racc);
 }
@@ -459,6 +531,7 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   __shared__ frag KF[G::AT * G::KD * NS * 64];
   __shared__ frag WTf[G::CT * G::NQS * 64];
   __shared__ float dmassL[G::LRP];
+  __shared__ T OS[4][OutStage<G::D, T>::ELEMS];
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
@@ -479,32 +552,28 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
   const float beta2 = 2.f * a.beta;
 
-  for (int64_t base = t_begin + 32 * w; base < t_end; base += TT) {
+  const int64_t last = t_end - 1;
+  auto tile = [&](const frag (&cx)[G::KD], const frag (&cy)[G::KD], int64_t base) {
     const int64_t tok = base + n;
     const bool valid = tok < t_end;
-    frag xf[G::KD];
-    load_row_frags<T, G>(valid ? Kx + tok * G::D : nullptr, xf);
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, xf, pre);
+    project<T, G>(Wf, cx, pre);
     soft_assign<G>(pre, beta2, a.L, u, phi);
     // dV = sum_l Phi_K dcontent
-    float dv[G::D / 2];
+    frag pb[G::KL];
+#pragma unroll
+    for (int q = 0; q < G::KL; ++q) pb[q] = tl_frag<T, G::LRP>(phi, q);
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) {
       f32x16 acc = zero16();
 #pragma unroll
-      for (int q = 0; q < G::KL; ++q) {
-        const frag b = tl_frag<T, G::LRP>(phi, q);
+      for (int q = 0; q < G::KL; ++q)
 #pragma unroll
-        for (int sp = 0; sp < NS; ++sp) E::mma(VF[((ct * G::KL + q) * NS + sp) * 64 + lane], b, acc);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dv[16 * ct + v] = acc[v];
+        for (int sp = 0; sp < NS; ++sp) E::mma(VF[((ct * G::KL + q) * NS + sp) * 64 + lane], pb[q], acc);
+      OutStage<G::D, T>::put(OS[w], ct, acc, 1.f);
     }
-    if (valid) store_tl_row<T, G::D>(dV + tok * G::D, dv);
+    OutStage<G::D, T>::flush(OS[w], dV, base, t_end);
     // dPhi_K[lr] = dcontent[lr] . V + dmass[lr]
-    frag yf[G::KD];
-    load_row_frags<T, G>(valid ? Vx + tok * G::D : nullptr, yf);
     float dphi[G::LRP / 2];
 #pragma unroll
     for (int at = 0; at < G::AT; ++at) {
@@ -512,7 +581,7 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
 #pragma unroll
       for (int q = 0; q < G::KD; ++q)
 #pragma unroll
-        for (int sp = 0; sp < NS; ++sp) E::mma(KF[((at * G::KD + q) * NS + sp) * 64 + lane], yf[q], d);
+        for (int sp = 0; sp < NS; ++sp) E::mma(KF[((at * G::KD + q) * NS + sp) * 64 + lane], cy[q], d);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -521,9 +590,35 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
     }
     float dpre[G::NHP];
     assign_backward<G>(phi, dphi, u, a.beta, dpre);
-    float dx[G::D / 2];
-    dx_mma<T, G>(WTf, dpre, dx);
-    if (valid) store_tl_row<T, G::D>(dK + tok * G::D, dx);
+    dx_mma_stage<T, G>(WTf, dpre, OS[w]);
+    OutStage<G::D, T>::flush(OS[w], dK, base, t_end);
+    (void)valid;
+  };
+  frag xa[G::KD], ya[G::KD], xb[G::KD], yb[G::KD];
+  int64_t base = t_begin + 32 * w;
+  {
+    const int64_t r = min(base + n, last);
+    load_row_frags_nb<T, G>(Kx + r * G::D, xa);
+    load_row_frags_nb<T, G>(Vx + r * G::D, ya);
+  }
+  while (base < t_end) {
+    {
+      const int64_t r = min(base + TT + n, last);
+      load_row_frags_nb<T, G>(Kx + r * G::D, xb);
+      load_row_frags_nb<T, G>(Vx + r * G::D, yb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xa, ya, base);
+    base += TT;
+    if (base >= t_end) break;
+    {
+      const int64_t r = min(base + TT + n, last);
+      load_row_frags_nb<T, G>(Kx + r * G::D, xa);
+      load_row_frags_nb<T, G>(Vx + r * G::D, ya);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tile(xb, yb, base);
+    base += TT;
   }
 }
 
