@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 18)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 22)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 1 GiB once (reference kernel for rocprofv3 byte counters)")
     return ap.parse_args()
