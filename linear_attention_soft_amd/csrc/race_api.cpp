@@ -16,6 +16,7 @@
 #include "race_causal.hpp"
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
+#include "race_walk.hpp"
 
 namespace race {
 // ------------------------------------------------------------------ fixed-order chunk sums
@@ -109,7 +110,7 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
   for (int i = 0; i < count; ++i) {
     const race::KernelSet& k = sets[i];
     if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
-    if (causal && !k.c_o) continue;
+    if (causal && !k.w_fwd) continue;
     if (!causal && !k.readout) continue;
     if (!best || k.LRP < best->LRP) best = &k;
   }
@@ -175,16 +176,15 @@ int nhp_of(const Plan& p) {
   return lmax * p.PE;
 }
 
-// Causal backward workspace: h partials [BH][N][d/32], h [BH][N], gradient
+// Causal backward workspace: h [BH][N], gradient
 // segment sums and their reverse scan [BH][nseg][LRP][d+1] each, dPre of Q
 // and of K [BH][N][NHP] each.
 struct CausalBwdWs {
-  size_t hpart, h, gpart, gsuf, dpq, dpk, total;
+  size_t h, gpart, gsuf, dpq, dpk, total;
 };
 CausalBwdWs causal_bwd_ws(const Plan& p) {
   CausalBwdWs w{};
   size_t off = 0;
-  w.hpart = off; off += align256((size_t)p.BH * p.N * (p.D / 32) * sizeof(float));
   w.h = off;     off += align256(tok_bytes(p));
   w.gpart = off; off += align256(seg_bank_bytes(p));
   w.gsuf = off;  off += align256(seg_bank_bytes(p));
@@ -231,42 +231,44 @@ void launch_finalize(const float* part, int nchunk, const Plan& p, float* conten
 
 
 // ---- causal sequences
+race::WArgs walk_args(const Plan& p, const float* W, float beta) {
+  race::WArgs w{};
+  w.W = W; w.beta = beta; w.L = p.L; w.P = p.P; w.N = p.N; w.seg_tokens = p.seg_tokens; w.nseg = p.nseg;
+  return w;
+}
+
+void launch_seg_scan(const Plan& p, const float* part, float* out, int reverse, hipStream_t s) {
+  const int per = p.LRP * (int)(p.D + 1);
+  const int64_t tot = p.BH * (int64_t)per;
+  hipLaunchKernelGGL(race::race_seg_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, part, out, p.nseg,
+                     per, (int)p.BH, reverse);
+}
+
 race_status causal_forward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
                            void* O, void* state, char* ws, hipStream_t s) {
   race_status st;
-  const int per = p.LRP * (int)(p.D + 1);
   float* part = reinterpret_cast<float*>(ws);
   char* sbase = state ? static_cast<char*>(state) : ws + align256(seg_bank_bytes(p));
   float* prefix = reinterpret_cast<float*>(sbase);
   float* den = reinterpret_cast<float*>(sbase + align256(seg_bank_bytes(p)));
-  race::NCArgs r{};
-  r.X = K; r.Y = V; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
-  r.chunk_tokens = p.seg_tokens; r.nchunk = p.nseg; r.part = part;
+  const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
+  race::WArgs w = walk_args(p, W, beta);
+  w.B_src = K; w.X_src = V; w.bank_out = part;
   {
     ProfScope ps(s, "race_causal_segsum");
-    p.ks->reduce(r, dim3(p.nseg, (unsigned)p.BH), s);
+    p.ks->w_segsum(w, grid, s);
   }
   if ((st = check_launch("race_causal_segsum")) != RACE_OK) return st;
   {
     ProfScope ps(s, "race_seg_scan");
-    const int64_t tot = p.BH * (int64_t)per;
-    hipLaunchKernelGGL(race::race_seg_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, part, prefix,
-                       p.nseg, per, (int)p.BH, 0);
+    launch_seg_scan(p, part, prefix, 0, s);
   }
   if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
-  race::CArgs c{};
-  c.A_src = Q; c.B_src = K; c.X_src = V; c.W = W; c.seg_state = prefix; c.den = den; c.den_out = den; c.out = O;
-  c.beta = beta; c.L = p.L; c.P = p.P; c.N = p.N; c.seg_tokens = p.seg_tokens; c.nseg = p.nseg;
-  c.units = (int64_t)p.nseg * p.BH;
-  {
-    ProfScope ps(s, "race_causal_den");
-    p.ks->c_den(c, dim3((unsigned)((c.units + 3) / 4)), s);
-  }
-  if ((st = check_launch("race_causal_den")) != RACE_OK) return st;
-  c.units = (int64_t)p.nseg * p.BH * (p.D / 32);
+  w = walk_args(p, W, beta);
+  w.A_src = Q; w.B_src = K; w.X_src = V; w.out = O; w.bank_in = prefix; w.den_out = den;
   {
     ProfScope ps(s, "race_causal_fwd");
-    p.ks->c_o(c, dim3((unsigned)((c.units + 3) / 4)), s);
+    p.ks->w_fwd(w, grid, s);
   }
   return check_launch("race_causal_fwd");
 }
@@ -275,12 +277,9 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
                             const void* dO, void* dQ, void* dK, void* dV, const void* state, char* ws,
                             hipStream_t s) {
   race_status st;
-  const int per = p.LRP * (int)(p.D + 1);
-  const int CT = (int)(p.D / 32);
   const float* prefix = static_cast<const float*>(state);
   const float* den = reinterpret_cast<const float*>(static_cast<const char*>(state) + align256(seg_bank_bytes(p)));
   const CausalBwdWs L = causal_bwd_ws(p);
-  float* hpart = reinterpret_cast<float*>(ws + L.hpart);
   float* h = reinterpret_cast<float*>(ws + L.h);
   float* gpart = reinterpret_cast<float*>(ws + L.gpart);
   float* gsuf = reinterpret_cast<float*>(ws + L.gsuf);
@@ -289,48 +288,37 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   const int R = 1 << p.PE;
   const int URP = R > 32 ? R : 32;
   const int NTG = p.LRP / URP;
+  const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
 
+  // 1. h = -(dO . O) / Den from a readout walk (O itself is not needed)
+  race::WArgs w = walk_args(p, W, beta);
+  w.A_src = Q; w.B_src = K; w.X_src = V; w.dO = dO; w.bank_in = prefix; w.den = den; w.h_out = h;
+  {
+    ProfScope ps(s, "race_causal_h");
+    p.ks->w_h(w, grid, s);
+  }
+  if ((st = check_launch("race_causal_h")) != RACE_OK) return st;
+  // 2. gradient segment sums Phi_Q^T [g | h], reverse exclusive scan
+  w = walk_args(p, W, beta);
+  w.B_src = Q; w.X_src = dO; w.den = den; w.hvec = h; w.bank_out = gpart;
+  {
+    ProfScope ps(s, "race_causal_gradsum");
+    p.ks->w_gsum(w, grid, s);
+  }
+  if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
+  launch_seg_scan(p, gpart, gsuf, 1, s);
+  if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
+  // 3. dV: reverse walk with Phi_K as output role, Phi_Q as state role, g as values
+  w = walk_args(p, W, beta);
+  w.A_src = K; w.B_src = Q; w.X_src = dO; w.den = den; w.bank_in = gsuf; w.out = dV;
+  {
+    ProfScope ps(s, "race_causal_dv");
+    p.ks->w_dv(w, grid, s);
+  }
+  if ((st = check_launch("race_causal_dv")) != RACE_OK) return st;
   race::CArgs c{};
   c.W = W; c.beta = beta; c.L = p.L; c.P = p.P; c.N = p.N; c.seg_tokens = p.seg_tokens; c.nseg = p.nseg;
   c.den = den;
-  // 1. per-column-tile partial dO . O, then h = -(dO . O) / Den
-  c.A_src = Q; c.B_src = K; c.X_src = V; c.dO = dO; c.hpart = hpart; c.seg_state = prefix;
-  c.units = (int64_t)p.nseg * p.BH * CT;
-  {
-    ProfScope ps(s, "race_causal_h");
-    p.ks->c_h(c, dim3((unsigned)((c.units + 3) / 4)), s);
-  }
-  if ((st = check_launch("race_causal_h")) != RACE_OK) return st;
-  {
-    const int64_t tot = p.BH * p.N;
-    hipLaunchKernelGGL(race::race_h_final, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, hpart, den, h, tot,
-                       CT);
-  }
-  if ((st = check_launch("race_h_final")) != RACE_OK) return st;
-  // 2. gradient segment sums Phi_Q^T [g | h], reverse exclusive scan
-  race::NCArgs r{};
-  r.X = Q; r.Y = dO; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
-  r.chunk_tokens = p.seg_tokens; r.nchunk = p.nseg; r.part = gpart; r.tok_den = den; r.tok_extra = h;
-  {
-    ProfScope ps(s, "race_causal_gradsum");
-    p.ks->reduce(r, dim3(p.nseg, (unsigned)p.BH), s);
-  }
-  if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
-  {
-    const int64_t tot = p.BH * (int64_t)per;
-    hipLaunchKernelGGL(race::race_seg_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, gpart, gsuf,
-                       p.nseg, per, (int)p.BH, 1);
-  }
-  if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
-  // 3. dV: reverse walk of the readout with Phi_K as query, Phi_Q as key, g as value
-  race::CArgs v = c;
-  v.A_src = K; v.B_src = Q; v.X_src = dO; v.out = dV; v.seg_state = gsuf;
-  v.units = (int64_t)p.nseg * p.BH * CT;
-  {
-    ProfScope ps(s, "race_causal_dv");
-    p.ks->c_dv(v, dim3((unsigned)((v.units + 3) / 4)), s);
-  }
-  if ((st = check_launch("race_causal_dv")) != RACE_OK) return st;
   // 4. dPhi_Q (forward walk) and dPhi_K (reverse walk) -> dPre
   race::CArgs q = c;
   q.A_src = Q; q.B_src = K; q.X_src = V; q.U_src = dO; q.hvec = h; q.seg_state = prefix; q.dpre_out = dpq;

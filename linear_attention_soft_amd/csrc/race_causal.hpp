@@ -3,26 +3,19 @@
 // reading notes section 2.6).  The key at position t is added before the
 // query at t reads, so token t sees keys j <= t.
 //
-// The sequence of every (batch, head) is cut into segments.  One wave walks
-// a segment in 32-token chunks and carries the running bucket bank in MFMA
-// accumulators; the bank at each segment start comes from a segment-sum
-// reduce plus an exclusive scan over segments.  Inside a chunk the bank
-// before the chunk is read with Phi_Q (inter part) and the chunk's own keys
-// enter through the masked 32x32 kernel tile Phi_Q Phi_K^T (intra part).
-//
-// A bank of L*R rows x (d+1) columns is too large for one wave at the wide
-// settings (L = 4, P = 6: 256 x 129 floats), so waves split it:
-//   race_causal_readout     one wave per 32-column slice of the values:
-//                           contracts the bank over buckets (O, Den, dV).
+// The sequence of every (batch, head) is cut into segments; the bank at each
+// segment start comes from a segment-sum walk plus an exclusive scan over
+// segments.  Contractions of the bank over buckets (O, den, h, dV) run in the
+// cooperative readout-layout walks of race_walk.hpp.  This file holds the
+// walks that contract the bank over value columns:
 //   race_causal_transposed  one wave per window of whole tables (bucket
-//                           rows): contracts the bank over value columns
-//                           (dPhi_Q, dPhi_K), then softmax, tanh and
-//                           projection backward of those tables.
+//                           rows): dPhi_Q on a forward walk, dPhi_K on a
+//                           reverse walk, then softmax, tanh and projection
+//                           backward of those tables.
 // Backward (exact gradient of the causal forward map, W and beta fixed):
 //   g_t = dO_t / Den_t,  h_t = -(dO_t . O_t) / Den_t
-//   dPhi_Q,t = sum_{j<=t} phi_K,j (V_j . g_t + h_t)          (transposed, forward walk)
-//   dPhi_K,j = sum_{t>=j} phi_Q,t (g_t . V_j + h_t)          (transposed, reverse walk)
-//   dV_j     = sum_{t>=j} (phi_K,j . phi_Q,t) g_t             (readout, reverse walk)
+//   dPhi_Q,t = sum_{j<=t} phi_K,j (V_j . g_t + h_t)          (forward walk)
+//   dPhi_K,j = sum_{t>=j} phi_Q,t (g_t . V_j + h_t)          (reverse walk)
 // and dQ, dK = dPre . W.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -43,14 +36,10 @@ struct CArgs {
   const void* B_src;      // rows whose features take the state (key) role
   const void* X_src;      // value rows of the state role (V; or dO, divided by Den)
   const void* U_src;      // value rows of the output role (transposed kernel: dO or V)
-  const void* dO;         // readout in h mode
-  void* out;              // readout: O or dV rows
   float* dpre_out;        // transposed: [BH][N][NHP] dPre of the output role
   const float* W;
   const float* seg_state; // [BH][nseg][LRP][d+1]: bank before (forward walk) / after (reverse walk) the segment
   const float* den;       // [BH][N]
-  float* den_out;         // [BH][N]
-  float* hpart;           // [BH][N][d/32]
   const float* hvec;      // [BH][N]
   float beta;
   int L, P;
@@ -60,9 +49,8 @@ struct CArgs {
   int64_t units;
 };
 
-enum { RO_O = 0, RO_DEN = 1, RO_H = 2, RO_DV = 3 };
-
-// Segments: about 4096 waves of work over the whole problem, 64-token multiples.
+// Segments: about 1024 (segment, batch x head) units over the whole problem,
+// 64-token multiples.
 inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_tokens) {
   int64_t want = (1024 + BH - 1) / BH;
   const int64_t tiles = (N + 63) / 64;
@@ -71,198 +59,6 @@ inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_t
   const int64_t per = (tiles + want - 1) / want;
   *seg_tokens = per * 64;
   *nseg = (int)((N + *seg_tokens - 1) / *seg_tokens);
-}
-
-// Load a 32-token x 32-column slice of value rows into an LDS tile (row
-// stride XSP), optionally divided by den[token]; rows past s1 are zero.
-template <typename T, int D, int XSP>
-__device__ __forceinline__ void stage_cols(const T* __restrict__ src, int64_t t0, int64_t s1, int c0,
-                                           const float* __restrict__ den, T* __restrict__ Xs) {
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = 32 / EPC;
-  const int lane = lane_id();
-#pragma unroll
-  for (int it = 0; it < 32 * CPR / 64; ++it) {
-    const int flat = it * 64 + lane;
-    const int row = flat / CPR, ch = flat % CPR;
-    const int64_t tr = t0 + row;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (tr < s1) {
-      val = *reinterpret_cast<const uint4*>(src + tr * D + c0 + ch * EPC);
-      if (den) {
-        const float inv = 1.f / den[tr];
-        T* e = reinterpret_cast<T*>(&val);
-#pragma unroll
-        for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
-      }
-    }
-    *reinterpret_cast<uint4*>(Xs + row * XSP + ch * EPC) = val;
-  }
-}
-
-// Features of one token row for the whole bucket bank, packed as K16 B frags.
-template <typename T, class G>
-__device__ __forceinline__ void features_packed(const typename Eng<T>::frag* __restrict__ Wf, const T* row,
-                                                float beta2, int L, typename Eng<T>::frag (&ph)[G::KL]) {
-  typename Eng<T>::frag xf[G::KD];
-  load_row_frags<T, G>(row, xf);
-  float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-  project<T, G>(Wf, xf, pre);
-  soft_assign<G>(pre, beta2, L, u, phi);
-  if (!row) {
-#pragma unroll
-    for (int i = 0; i < G::LRP / 2; ++i) phi[i] = 0.f;
-  }
-#pragma unroll
-  for (int q = 0; q < G::KL; ++q) ph[q] = tl_frag<T, G::LRP>(phi, q);
-}
-
-// ------------------------------------------------------------------ race_causal_readout
-// Unit = (segment, bh, value-column tile ct).  Bank slice S[lr][32 ct + n]
-// lives in accumulators st[at] (lane = column, registers over buckets).
-template <typename T, class G, bool REV, int MODE>
-__global__ __launch_bounds__(256) void race_causal_readout(CArgs a) {
-  using E = Eng<T>;
-  using frag = typename E::frag;
-  constexpr int NS = E::NSPLIT;
-  constexpr int TTP = CC + 8;
-  constexpr int XSP = 32 + 8;
-  __shared__ frag Wf[G::NPT * G::KD * 64];
-  __shared__ T PhiT_all[4][G::LRP * TTP];
-  __shared__ T Xs_all[4][CC * XSP];
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
-  __syncthreads();
-
-  const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
-  if (unit >= a.units) return;
-  T* PhiT = PhiT_all[w];
-  T* Xs = Xs_all[w];
-  constexpr int NU = (MODE == RO_DEN) ? 1 : G::CT;
-  const int ct = (MODE == RO_DEN) ? G::CT : (int)(unit % NU);
-  const int64_t seg = (unit / NU) % a.nseg;
-  const int64_t bh = unit / NU / a.nseg;
-  const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
-  const size_t rb = (size_t)bh * a.N;
-  const T* Ar = static_cast<const T*>(a.A_src) + rb * G::D;
-  const T* Br = static_cast<const T*>(a.B_src) + rb * G::D;
-
-  f32x16 st[G::AT];
-  {
-    const float* ss = a.seg_state + ((size_t)bh * a.nseg + seg) * G::LRP * (G::D + 1);
-    const int col = (MODE == RO_DEN) ? G::D : 32 * ct + n;
-#pragma unroll
-    for (int at = 0; at < G::AT; ++at)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-        st[at][v] = ss[(size_t)lr * (G::D + 1) + col];
-      }
-  }
-  const float beta2 = 2.f * a.beta;
-  const int64_t nch = (s1 - s0 + CC - 1) / CC;
-  for (int64_t k = 0; k < nch; ++k) {
-    const int64_t t0 = s0 + (REV ? (nch - 1 - k) : k) * CC;
-    const int64_t tok = t0 + n;
-    const bool valid = tok < s1;
-    frag pa[G::KL], pb[G::KL];
-    features_packed<T, G>(Wf, valid ? Ar + tok * G::D : nullptr, beta2, a.L, pa);
-    features_packed<T, G>(Wf, valid ? Br + tok * G::D : nullptr, beta2, a.L, pb);
-    // transposed state-role features for the bank update
-#pragma unroll
-    for (int q = 0; q < G::KL; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) PhiT[kmap(q, h, i) * TTP + n] = pb[q][i];
-    if (MODE == RO_O || MODE == RO_H)
-      stage_cols<T, G::D, XSP>(static_cast<const T*>(a.X_src) + rb * G::D, t0, s1, 32 * ct, nullptr, Xs);
-    if (MODE == RO_DV)
-      stage_cols<T, G::D, XSP>(static_cast<const T*>(a.X_src) + rb * G::D, t0, s1, 32 * ct, a.den + rb, Xs);
-    wave_lds_sync();
-
-    // inter: bank before the chunk, read with the output-role features
-    f32x16 y = zero16();
-#pragma unroll
-    for (int q = 0; q < G::KL; ++q) {
-      float v8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v8[i] = st[q >> 1][8 * (q & 1) + i];
-      frag hi, lo;
-      E::split(v8, hi, lo);
-      E::mma(hi, pa[q], y);
-      if (NS == 2) E::mma(lo, pa[q], y);
-    }
-    // intra: masked kernel tile sc^T[tok_b][tok_a] = phi_B . phi_A
-    f32x16 sc = zero16();
-#pragma unroll
-    for (int q = 0; q < G::KL; ++q) E::mma(pb[q], pa[q], sc);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
-      const bool keep = REV ? (tb >= n) : (tb <= n);
-      sc[v] = keep ? sc[v] : 0.f;
-    }
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      float s8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s8[i] = sc[8 * q2 + i];
-      const frag sb = E::pack(s8);
-      frag xa;
-      if (MODE == RO_DEN) {
-        xa = E::ones();
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xa[i] = Xs[kmap(q2, h, i) * XSP + n];
-      }
-      E::mma(xa, sb, y);
-    }
-    // epilogue: lane (tok, h) holds columns 32 ct + 8 j + 4 h + k
-    if (MODE == RO_DEN) {
-      if (valid && h == 0) a.den_out[rb + tok] = y[0];
-    } else if (MODE == RO_O || MODE == RO_DV) {
-      if (valid) {
-        const float inv = (MODE == RO_O) ? 1.f / a.den[rb + tok] : 1.f;
-        T* orow = static_cast<T*>(a.out) + (rb + tok) * G::D + 32 * ct + 4 * h;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          typename E::vec4 o;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) o[kk] = (T)(y[4 * j + kk] * inv);
-          *reinterpret_cast<typename E::vec4*>(orow + 8 * j) = o;
-        }
-      }
-    } else {  // RO_H: partial dO . O over this column tile
-      float part = 0.f;
-      if (valid) {
-        const float inv = 1.f / a.den[rb + tok];
-        const T* drow = static_cast<const T*>(a.dO) + (rb + tok) * G::D + 32 * ct + 4 * h;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const typename E::vec4 dv = *reinterpret_cast<const typename E::vec4*>(drow + 8 * j);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) part += (float)dv[kk] * (y[4 * j + kk] * inv);
-        }
-      }
-      part += xor32(part);
-      if (valid && h == 0) a.hpart[(rb + tok) * G::CT + ct] = part;
-    }
-    // bank update with the chunk's state-role keys and values
-#pragma unroll
-    for (int at = 0; at < G::AT; ++at)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const frag af = *reinterpret_cast<const frag*>(PhiT + (32 * at + n) * TTP + 16 * s + 8 * h);
-        frag bf;
-        if (MODE == RO_DEN) {
-          bf = E::ones();
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bf[i] = Xs[(16 * s + 8 * h + i) * XSP + n];
-        }
-        E::mma(af, bf, st[at]);
-      }
-    wave_lds_sync();
-  }
 }
 
 // ------------------------------------------------------------------ race_causal_transposed
@@ -596,16 +392,6 @@ static __global__ void race_seg_scan(const float* __restrict__ part, float* __re
     out[o] = run;
     run += v;
   }
-}
-
-// h_t = -(dO_t . O_t) / Den_t from the per-column-tile partial dot products.
-static __global__ void race_h_final(const float* __restrict__ hpart, const float* __restrict__ den, float* __restrict__ h,
-                             int64_t total, int ct) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  float s = 0.f;
-  for (int c = 0; c < ct; ++c) s += hpart[i * ct + c];
-  h[i] = -s / den[i];
 }
 
 }  // namespace race

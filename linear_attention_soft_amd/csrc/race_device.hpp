@@ -257,6 +257,43 @@ __device__ __forceinline__ void load_row_frags(const T* __restrict__ x, typename
   }
 }
 
+// Projection tiles [PT0, PT1) that hold the hyperplanes of the tables
+// overlapping bucket rows [R0, R0 + NROWS).
+template <class G, int R0, int NROWS>
+struct WinTiles {
+  static constexpr int L0 = R0 / G::R;
+  static constexpr int L1 = cdiv(R0 + NROWS, G::R) < G::LMAX ? cdiv(R0 + NROWS, G::R) : G::LMAX;
+  static constexpr int PT0 = L1 > L0 ? L0 * G::PE / G::HPT : 0;
+  static constexpr int PT1 = L1 > L0 ? cdiv(L1 * G::PE, G::HPT) : 0;
+};
+
+// pre[hp] = W_hp . x for the hyperplane slots of projection tiles [PT0, PT1)
+// of the lane's token; other slots are 0.
+template <typename T, class G, int PT0, int PT1>
+__device__ __forceinline__ void project_tiles(const typename Eng<T>::frag* __restrict__ Wf,
+                                              const typename Eng<T>::frag (&xf)[G::KD],
+                                              float (&pre)[G::NHP]) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+#pragma unroll
+  for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
+#pragma unroll
+  for (int pt = PT0; pt < PT1; ++pt) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) E::mma(Wf[(pt * G::KD + q) * 64 + lane], xf[q], acc);
+    if (E::NSPLIT == 2) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        if (8 * pt + v < G::NHP) pre[8 * pt + v] = acc[v] + acc[v + 8];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (16 * pt + v < G::NHP) pre[16 * pt + v] = acc[v];
+    }
+  }
+}
+
 // pre[hp] = W_hp . x for every hyperplane slot of the lane's token.
 template <typename T, class G>
 __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict__ Wf,

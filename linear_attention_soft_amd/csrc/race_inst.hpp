@@ -3,6 +3,7 @@
 #include "race_causal.hpp"
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
+#include "race_walk.hpp"
 
 namespace race {
 
@@ -60,17 +61,9 @@ struct Inst {
                   dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, out);
   }
-  static void c_den(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_DEN>), g, dim3(256), 0, s, a);
-  }
-  static void c_o(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_O>), g, dim3(256), 0, s, a);
-  }
-  static void c_h(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_readout<T, G, false, RO_H>), g, dim3(256), 0, s, a);
-  }
-  static void c_dv(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_readout<T, G, true, RO_DV>), g, dim3(256), 0, s, a);
+  template <int MODE>
+  static void walk(const WArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_walk_rw<T, G, MODE>), g, dim3(RWCfg<T, G, MODE>::NT), 0, s, a);
   }
   static void c_dq(const CArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_causal_transposed<T, G, false>), g, dim3(256), 0, s, a);
@@ -91,7 +84,9 @@ struct Inst {
     k.softbucket_dbg = dbg;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
-      k.c_den = c_den; k.c_o = c_o; k.c_h = c_h; k.c_dv = c_dv; k.c_dq = c_dq; k.c_dk = c_dk; k.dx = dx;
+      k.c_dq = c_dq; k.c_dk = c_dk; k.dx = dx;
+      k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>; k.w_fwd = walk<W_FWD>; k.w_h = walk<W_H>;
+      k.w_dv = walk<W_DV>;
     }
     return k;
   }
