@@ -110,7 +110,7 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
   for (int i = 0; i < count; ++i) {
     const race::KernelSet& k = sets[i];
     if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
-    if (causal && !k.w_fwd) continue;
+    if (causal && (!k.w_fwd || !k.tw_dq)) continue;
     if (!causal && !k.readout) continue;
     if (!best || k.LRP < best->LRP) best = &k;
   }
@@ -170,17 +170,11 @@ size_t state_bytes(const Plan& p) {
   return align256(seg_bank_bytes(p)) + align256(tok_bytes(p));
 }
 
-int nhp_of(const Plan& p) {
-  const int R = 1 << p.PE;
-  const int lmax = p.LRP / R > 0 ? p.LRP / R : 1;
-  return lmax * p.PE;
-}
 
-// Causal backward workspace: h [BH][N], gradient
-// segment sums and their reverse scan [BH][nseg][LRP][d+1] each, dPre of Q
-// and of K [BH][N][NHP] each.
+// Causal backward workspace: h [BH][N], gradient segment sums and their
+// reverse scan [BH][nseg][LRP][d+1] each.
 struct CausalBwdWs {
-  size_t h, gpart, gsuf, dpq, dpk, total;
+  size_t h, gpart, gsuf, total;
 };
 CausalBwdWs causal_bwd_ws(const Plan& p) {
   CausalBwdWs w{};
@@ -188,8 +182,6 @@ CausalBwdWs causal_bwd_ws(const Plan& p) {
   w.h = off;     off += align256(tok_bytes(p));
   w.gpart = off; off += align256(seg_bank_bytes(p));
   w.gsuf = off;  off += align256(seg_bank_bytes(p));
-  w.dpq = off;   off += align256((size_t)p.BH * p.N * nhp_of(p) * sizeof(float));
-  w.dpk = off;   off += align256((size_t)p.BH * p.N * nhp_of(p) * sizeof(float));
   w.total = off;
   return w;
 }
@@ -283,11 +275,6 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   float* h = reinterpret_cast<float*>(ws + L.h);
   float* gpart = reinterpret_cast<float*>(ws + L.gpart);
   float* gsuf = reinterpret_cast<float*>(ws + L.gsuf);
-  float* dpq = reinterpret_cast<float*>(ws + L.dpq);
-  float* dpk = reinterpret_cast<float*>(ws + L.dpk);
-  const int R = 1 << p.PE;
-  const int URP = R > 32 ? R : 32;
-  const int NTG = p.LRP / URP;
   const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
 
   // 1. h = -(dO . O) / Den from a readout walk (O itself is not needed)
@@ -316,35 +303,23 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
     p.ks->w_dv(w, grid, s);
   }
   if ((st = check_launch("race_causal_dv")) != RACE_OK) return st;
-  race::CArgs c{};
-  c.W = W; c.beta = beta; c.L = p.L; c.P = p.P; c.N = p.N; c.seg_tokens = p.seg_tokens; c.nseg = p.nseg;
-  c.den = den;
-  // 4. dPhi_Q (forward walk) and dPhi_K (reverse walk) -> dPre
-  race::CArgs q = c;
-  q.A_src = Q; q.B_src = K; q.X_src = V; q.U_src = dO; q.hvec = h; q.seg_state = prefix; q.dpre_out = dpq;
-  q.units = (int64_t)p.nseg * p.BH * NTG;
+  // 4. dQ: forward transposed walk (dPhi_Q, softmax / tanh / projection backward)
+  race::TWArgs t{};
+  t.W = W; t.beta = beta; t.L = p.L; t.P = p.P; t.N = p.N; t.seg_tokens = p.seg_tokens; t.nseg = p.nseg;
+  t.den = den; t.hvec = h;
+  t.A_src = Q; t.B_src = K; t.X_src = V; t.U_src = dO; t.bank_in = prefix; t.dX = dQ;
   {
-    ProfScope ps(s, "race_causal_dphi_q");
-    p.ks->c_dq(q, dim3((unsigned)((q.units + 3) / 4)), s);
+    ProfScope ps(s, "race_causal_dq");
+    p.ks->tw_dq(t, grid, s);
   }
-  if ((st = check_launch("race_causal_dphi_q")) != RACE_OK) return st;
-  race::CArgs k = c;
-  k.A_src = K; k.B_src = Q; k.X_src = dO; k.U_src = V; k.hvec = h; k.seg_state = gsuf; k.dpre_out = dpk;
-  k.units = (int64_t)p.nseg * p.BH * NTG;
+  if ((st = check_launch("race_causal_dq")) != RACE_OK) return st;
+  // 5. dK: reverse transposed walk (dPhi_K) from the gradient suffix banks
+  t.A_src = K; t.B_src = Q; t.X_src = dO; t.U_src = V; t.bank_in = gsuf; t.dX = dK;
   {
-    ProfScope ps(s, "race_causal_dphi_k");
-    p.ks->c_dk(k, dim3((unsigned)((k.units + 3) / 4)), s);
+    ProfScope ps(s, "race_causal_dk");
+    p.ks->tw_dk(t, grid, s);
   }
-  if ((st = check_launch("race_causal_dphi_k")) != RACE_OK) return st;
-  // 5. dQ, dK = dPre . W
-  {
-    const int64_t tiles = (p.BH * p.N + race::TT - 1) / race::TT;
-    const unsigned blocks = (unsigned)(tiles < 8192 ? tiles : 8192);
-    ProfScope ps(s, "race_causal_dx");
-    p.ks->dx(dpq, W, p.L, p.P, p.N, p.BH, dQ, dim3(blocks), s);
-    p.ks->dx(dpk, W, p.L, p.P, p.N, p.BH, dK, dim3(blocks), s);
-  }
-  return check_launch("race_causal_dx");
+  return check_launch("race_causal_dk");
 }
 
 }  // namespace

@@ -8,10 +8,10 @@
 // segments.  Contractions of the bank over buckets (O, den, h, dV) run in the
 // cooperative readout-layout walks of race_walk.hpp.  This file holds the
 // walks that contract the bank over value columns:
-//   race_causal_transposed  one wave per window of whole tables (bucket
-//                           rows): dPhi_Q on a forward walk, dPhi_K on a
-//                           reverse walk, then softmax, tanh and projection
-//                           backward of those tables.
+//   race_walk_tw  one wave per window of whole tables (bucket rows), the
+//                 workgroup walking one (segment, batch x head): dPhi_Q on a
+//                 forward walk, dPhi_K on a reverse walk, then softmax, tanh
+//                 and projection backward of those tables and dX = dPre . W.
 // Backward (exact gradient of the causal forward map, W and beta fixed):
 //   g_t = dO_t / Den_t,  h_t = -(dO_t . O_t) / Den_t
 //   dPhi_Q,t = sum_{j<=t} phi_K,j (V_j . g_t + h_t)          (forward walk)
@@ -26,28 +26,9 @@
 #include "../../include/race_attn.h"
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
+#include "race_walk.hpp"
 
 namespace race {
-
-constexpr int CC = 32;   // tokens per causal chunk
-
-struct CArgs {
-  const void* A_src;      // rows whose features take the output (query) role
-  const void* B_src;      // rows whose features take the state (key) role
-  const void* X_src;      // value rows of the state role (V; or dO, divided by Den)
-  const void* U_src;      // value rows of the output role (transposed kernel: dO or V)
-  float* dpre_out;        // transposed: [BH][N][NHP] dPre of the output role
-  const float* W;
-  const float* seg_state; // [BH][nseg][LRP][d+1]: bank before (forward walk) / after (reverse walk) the segment
-  const float* den;       // [BH][N]
-  const float* hvec;      // [BH][N]
-  float beta;
-  int L, P;
-  int64_t N;
-  int64_t seg_tokens;
-  int nseg;
-  int64_t units;
-};
 
 // Segments: about 1024 (segment, batch x head) units over the whole problem,
 // 64-token multiples.
@@ -61,319 +42,442 @@ inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_t
   *nseg = (int)((N + *seg_tokens - 1) / *seg_tokens);
 }
 
-// ------------------------------------------------------------------ race_causal_transposed
-// Unit = (segment, bh, window TG of whole tables).  Bank rows of the window
-// live in acc[a][ct] as C[c][lr] tiles (lane = bucket row, registers over
-// value columns c; tile CT holds the mass / h column at c = d).
-// Forward walk (dPhi_Q): output role Q, state role K, X = [V | 1], U = [g | h].
-// Reverse walk (dPhi_K):  output role K, state role Q, X = [g | h], U = [V | 1].
+struct TWArgs {
+  const void* A_src;      // output-role rows (forward walk: Q; reverse walk: K)
+  const void* B_src;      // state-role rows (forward: K; reverse: Q)
+  const void* X_src;      // state-role values: forward V; reverse dO (divided by den: g)
+  const void* U_src;      // output-role values: forward dO; reverse V
+  void* dX;               // dQ (forward) or dK (reverse)
+  const float* bank_in;   // [BH][nseg][LRP][d+1]: bank before (forward) / after (reverse) the segment
+  const float* den;       // [BH][N]
+  const float* hvec;      // [BH][N]
+  const float* W;
+  float beta;
+  int L, P;
+  int64_t N;
+  int64_t seg_tokens;
+  int nseg;
+};
+
+// One wave per window of URP bucket rows (whole tables); the workgroup walks
+// one (segment, batch x head).
+template <typename T, class G, bool REV>
+struct TWCfg {
+  static constexpr int URP = G::R > 32 ? G::R : 32;
+  static constexpr int NM = G::LRP / URP;             // waves
+  static constexpr int ATU = URP / 32;                // 32-row tiles per wave
+  static constexpr int NT = 64 * NM;
+  static constexpr bool XSPLIT = REV && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
+  static constexpr int NXS = XSPLIT ? 2 : 1;
+  static constexpr int FS = G::D + 16 / (int)sizeof(T);   // staged row (elements)
+  static constexpr int TSP = WC + 8;                  // Phi_B^T row (elements)
+  static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
+  static constexpr int NPS = cdiv(WC * CPR, NT);      // staged chunks per thread
+  // The float32 bank enters the contraction over value columns as bf16
+  // hi + lo parts (the softmax backward that follows subtracts nearly equal
+  // terms).
+  static constexpr bool BANK_LO = true;
+  static_assert(G::LRP % URP == 0, "windows of whole tables");
+};
+
+template <typename T, class G, bool REV>
+struct TWLds {
+  using C = TWCfg<T, G, REV>;
+  typename Eng<T>::frag Wf[G::NPT * G::KD * 64];   // projection operands
+  alignas(16) T PhiBT[C::NM][C::URP * C::TSP];   // wave-private Phi_B^T of the current chunk
+  alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
+  alignas(16) T AR[2][WC * C::FS];               // output-role rows (projection operands)
+  alignas(16) T BR[2][WC * C::FS];               // state-role rows
+  alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
+  alignas(16) T XF[2][C::NXS][WC * C::FS];       // X rows, kmap frag order (hi, lo)
+  alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
+  alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
+};
+
+// W^T frags of the dX contraction for column tile ct, built into registers
+// (same entries as build_wt_frags).
+template <typename T, class G>
+__device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int L, int P, int ct,
+                                             typename Eng<T>::frag (&wt)[G::NQS]) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+  const int c = 32 * ct + (lane & 31), h = lane >> 5;
+#pragma unroll
+  for (int qs = 0; qs < G::NQS; ++qs) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 16 * qs + 8 * h + i;
+      float w = 0.f;
+      if (e < G::NE && ct < G::CT) {
+        const int hp = e % G::NHP, which = e / G::NHP;
+        const int l = hp / G::PE, t = hp % G::PE;
+        if (l < L && t < P) {
+          const float x = W[(size_t)(l * P + t) * G::D + c];
+          const float xh = E::round(x);
+          w = (E::NSPLIT == 2 && which == 2) ? (x - xh) : (E::NSPLIT == 2 ? xh : x);
+        }
+      }
+      v[i] = w;
+    }
+    wt[qs] = E::pack(v);
+  }
+}
+
+// ------------------------------------------------------------------ race_walk_tw
+// Per chunk, wave w (bucket rows [R0, R0 + URP)), with the bank B[c][lr] of
+// its rows (columns of the state-role values X, plus the mass column kept as
+// a vector m) in registers:
+//   dphi[lr][a] = sum_c B[lr][c] U_a[c] + m[lr] ue_a                       (inter)
+//               + sum_{b in chunk, masked} phi_B,b[lr] (X_b . U_a + xe_b ue_a)  (intra)
+//   forward walk (dPhi_Q): U = dO, ue = h den, xe = 1, then dphi /= den_a
+//   reverse walk (dPhi_K): U = V,  ue = 1,     xe = h, X = g = dO / den
+//   softmax, tanh backward of the wave's tables -> dPre (to LDS)
+//   B[c][lr] += sum_b X_b[c] phi_B,b[lr],  m[lr] += sum_b phi_B,b[lr] xe_b
+// and, one chunk behind, dX = dPre . W for the wave's column tiles.  Rows of
+// the next chunk are staged into double-buffered LDS by the whole workgroup
+// (one barrier per chunk); X^T tiles for the bank update come out of an MFMA
+// with an identity operand.
 template <typename T, class G, bool REV, int TG>
-__device__ __forceinline__ void transposed_body(const CArgs& a, int64_t seg, int64_t bh,
-                                                const typename Eng<T>::frag* __restrict__ Wf, T* __restrict__ PhiT,
-                                                T* __restrict__ Xh, T* __restrict__ Xl) {
+__device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
+  using C = TWCfg<T, G, REV>;
   using E = Eng<T>;
   using frag = typename E::frag;
-  constexpr int NS = E::NSPLIT;
-  constexpr int URP = G::R > 32 ? G::R : 32;
-  constexpr int ATU = URP / 32;
-  constexpr int R0 = TG * URP;
-  constexpr int TTP = CC + 8;
-  constexpr int XSP = G::D + 32 + 8;
-  constexpr int NC = G::CT + 1;          // column tiles incl. the mass / h tile
-  constexpr bool XEXACT = !REV;          // X = [V | 1] is exact in T; [g | h] is not
-  constexpr bool UEXACT = REV;           // U = [V | 1] exact; [g | h] not
-  constexpr bool USE_XL = !XEXACT && NS == 2;
+  constexpr int R0 = TG * C::URP;
+  constexpr int URP = C::URP, ATU = C::ATU;
+  constexpr int DP1 = G::D + 1;
+  constexpr int FS = C::FS, TSP = C::TSP;
+  constexpr int EPC = C::EPC, CPR = C::CPR;
+  using WT = WinTiles<G, R0, URP>;
+  typedef T T4 __attribute__((ext_vector_type(4)));
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
+  const int w = TG;
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x, bh = blockIdx.y;
   const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
+  const int64_t nch = (s1 - s0 + WC - 1) / WC;
   const size_t rb = (size_t)bh * a.N;
-  const T* Ar = static_cast<const T*>(a.A_src) + rb * G::D;
-  const T* Br = static_cast<const T*>(a.B_src) + rb * G::D;
-  const T* Xr = static_cast<const T*>(a.X_src) + rb * G::D;
-  const T* Ur = static_cast<const T*>(a.U_src) + rb * G::D;
+  const size_t bank_off = ((size_t)bh * a.nseg + seg) * G::LRP * DP1;
+  const T* Ag = static_cast<const T*>(a.A_src) + rb * G::D;
+  const T* Bg = static_cast<const T*>(a.B_src) + rb * G::D;
+  const T* Xg = static_cast<const T*>(a.X_src) + rb * G::D;
+  const T* Ug = static_cast<const T*>(a.U_src) + rb * G::D;
   const float* den = a.den + rb;
   const float* hv = a.hvec + rb;
-
-  f32x16 acc[ATU][NC];
-  {
-    const float* ss = a.seg_state + ((size_t)bh * a.nseg + seg) * G::LRP * (G::D + 1);
-#pragma unroll
-    for (int at = 0; at < ATU; ++at)
-#pragma unroll
-      for (int ct = 0; ct < NC; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 32 * ct + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int lr = R0 + 32 * at + n;
-          acc[at][ct][v] = (c <= G::D) ? ss[(size_t)lr * (G::D + 1) + c] : 0.f;
-        }
-  }
-  // the mass-tile columns past c = d stay zero in the X tiles
-  for (int r = 0; r < CC; ++r) {
-    if (lane < 32) {
-      Xh[r * XSP + G::D + lane] = (T)0.f;
-      if (USE_XL) Xl[r * XSP + G::D + lane] = (T)0.f;
-    }
-  }
+  T* dXg = static_cast<T*>(a.dX) + rb * G::D;
   const float beta2 = 2.f * a.beta;
-  const int64_t nch = (s1 - s0 + CC - 1) / CC;
+
+  frag wt[C::NCTW][G::NQS];
+#pragma unroll
+  for (int j = 0; j < C::NCTW; ++j) wt_frags_reg<T, G>(a.W, a.L, a.P, w + C::NM * j, wt[j]);
+  // identity operands: lane (c, h), element i is 1 where kmap(s, h, i) == c
+  frag idn[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = kmap(s, h, i) == n ? 1.f : 0.f;
+    idn[s] = E::pack(v);
+  }
+
+  f32x16 acc[ATU][G::CT];
+#pragma unroll
+  for (int at = 0; at < ATU; ++at) {
+    const size_t rowo = bank_off + (size_t)(R0 + 32 * at + n) * DP1;
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[at][ct][v] = a.bank_in[rowo + 32 * ct + 8 * (v >> 2) + 4 * h + (v & 3)];
+    if (h == 0) S.Mw[w][32 * at + n] = a.bank_in[rowo + G::D];
+  }
+
+  // ---- staging loads (chunk index clamped: loads never sit behind a branch)
+  uint4 px[C::NPS], pu[C::NPS], pa[C::NPS], pb[C::NPS];
+  float pd[C::NPS];
+  float tk_h = 0.f, tk_d = 1.f;
+  auto load_stage = [&](int64_t k) {
+    const int64_t t0 = chunk_t0<REV>(s0, nch, k < nch ? k : nch - 1);
+#pragma unroll
+    for (int i = 0; i < C::NPS; ++i) {
+      const int idx = min(tid + C::NT * i, WC * CPR - 1);
+      const int64_t row = min(t0 + idx / CPR, s1 - 1);
+      const int cc = idx % CPR;
+      px[i] = *reinterpret_cast<const uint4*>(Xg + row * G::D + cc * EPC);
+      pu[i] = *reinterpret_cast<const uint4*>(Ug + row * G::D + cc * EPC);
+      pa[i] = *reinterpret_cast<const uint4*>(Ag + row * G::D + cc * EPC);
+      pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
+      pd[i] = den[row];
+    }
+    const int64_t row = min(t0 + n, s1 - 1);
+    tk_h = hv[row];
+    tk_d = den[row];
+  };
+  // ---- write the staged chunk k into buffer bb
+  auto stage = [&](int64_t k, int bb) {
+    const int64_t t0 = chunk_t0<REV>(s0, nch, k);
+#pragma unroll
+    for (int i = 0; i < C::NPS; ++i) {
+      const int idx = tid + C::NT * i;
+      if (idx < WC * CPR) {
+        const int r = idx / CPR, cc = idx % CPR;
+        const bool ok = t0 + r < s1;
+        *reinterpret_cast<uint4*>(&S.AR[bb][r * FS + cc * EPC]) = pa[i];
+        *reinterpret_cast<uint4*>(&S.BR[bb][r * FS + cc * EPC]) = pb[i];
+        const T* xe8 = reinterpret_cast<const T*>(&px[i]);
+        const T* ue8 = reinterpret_cast<const T*>(&pu[i]);
+        const float sc = REV ? 1.f / pd[i] : 1.f;
+        // kmap frag order: column 16 q + 8 hh + e sits at 16 q + 8 (e / 4) + 4 hh + e % 4,
+        // so a 16-byte chunk of bf16 goes out as two 8-byte halves
+        T xh[EPC], xl[EPC], uu[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const float f = ok ? (float)xe8[e] * sc : 0.f;
+          xh[e] = (T)f;
+          xl[e] = (T)(f - (float)xh[e]);
+          uu[e] = ok ? ue8[e] : (T)0.f;
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < EPC / 4; ++g4) {
+          const int col = cc * EPC + 4 * g4;
+          const int q = col >> 4, o = col & 15, hh = o >> 3, ee = o & 7;
+          const int pos = r * FS + 16 * q + 8 * (ee >> 2) + 4 * hh;
+          *reinterpret_cast<T4*>(&S.UF[bb][pos]) = *reinterpret_cast<const T4*>(&uu[4 * g4]);
+          *reinterpret_cast<T4*>(&S.XF[bb][0][pos]) = *reinterpret_cast<const T4*>(&xh[4 * g4]);
+          if (C::XSPLIT) *reinterpret_cast<T4*>(&S.XF[bb][1][pos]) = *reinterpret_cast<const T4*>(&xl[4 * g4]);
+        }
+      }
+    }
+    if (tid < WC) {
+      const bool ok = t0 + tid < s1;
+      S.TK[bb][0][tid] = ok ? (REV ? tk_h : 1.f) : 0.f;        // xe
+      S.TK[bb][1][tid] = ok ? (REV ? 1.f : tk_h * tk_d) : 0.f; // ue
+      S.TK[bb][2][tid] = ok ? 1.f / tk_d : 0.f;                 // 1 / den
+    }
+  };
+  // ---- dX = dPre . W for chunk k (from DP[bb]), this wave's column tiles
+  auto dx_out = [&](int64_t k, int bb) {
+    const int64_t t0 = chunk_t0<REV>(s0, nch, k);
+    float dp[G::NHP];
+#pragma unroll
+    for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * G::NHP + i];
+    frag bq[G::NQS];
+#pragma unroll
+    for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dp, qs);
+#pragma unroll
+    for (int j = 0; j < C::NCTW; ++j) {
+      const int ct = w + C::NM * j;
+      if (ct < G::CT) {
+        f32x16 o = zero16();
+#pragma unroll
+        for (int qs = 0; qs < G::NQS; ++qs) E::mma(wt[j][qs], bq[qs], o);
+        if (t0 + n < s1) store_tl_tile<T>(dXg + (t0 + n) * G::D, ct, o, 1.f);
+      }
+    }
+  };
+
+  build_proj_frags<T, G>(a.W, a.L, a.P, S.Wf);
+  load_stage(0);
+  stage(0, 0);
+  __syncthreads();
+
   for (int64_t k = 0; k < nch; ++k) {
-    const int64_t t0 = s0 + (REV ? (nch - 1 - k) : k) * CC;
-    const int64_t tok = t0 + n;
-    const bool valid = tok < s1;
-    // output-role features of the window (float32, for the softmax backward)
+    const int bb = (int)(k & 1);
+    const int64_t t0 = chunk_t0<REV>(s0, nch, k);
+    const bool valid = t0 + n < s1;
+    load_stage(k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
     float uA[G::NHP], phA[URP / 2];
     {
-      frag xf[G::KD];
+      frag xa[G::KD];
+#pragma unroll
+      for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[bb][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP];
-      load_row_frags<T, G>(valid ? Ar + tok * G::D : nullptr, xf);
-      project<T, G>(Wf, xf, pre);
+      project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, pre);
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uA, phA);
     }
-    // state-role features of the window, rounded, transposed into LDS
     {
-      frag xf[G::KD];
+      frag xb[G::KD];
+#pragma unroll
+      for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[bb][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP], uB[G::NHP], phB[URP / 2];
-      load_row_frags<T, G>(valid ? Br + tok * G::D : nullptr, xf);
-      project<T, G>(Wf, xf, pre);
+      project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uB, phB);
+      T* pt = S.PhiBT[w];
 #pragma unroll
       for (int at = 0; at < ATU; ++at)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-          PhiT[lr * TTP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
+          pt[lr * TSP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
         }
-    }
-    // output-role values U in TLAYOUT over columns (tile CT: c = d only)
-    float ut[NC * 16];
-    {
-      float tmp[G::D / 2];
-      if (valid) load_tl_row<T, G::D>(Ur + tok * G::D, tmp);
-      else {
-#pragma unroll
-        for (int i = 0; i < G::D / 2; ++i) tmp[i] = 0.f;
-      }
-      const float scale = (!REV && valid) ? 1.f / den[tok] : 1.f;
-#pragma unroll
-      for (int i = 0; i < G::D / 2; ++i) ut[i] = tmp[i] * scale;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ut[G::D / 2 + i] = 0.f;
-      const float extra = REV ? 1.f : (valid ? hv[tok] : 0.f);
-      if (h == 0) ut[G::D / 2] = valid ? extra : 0.f;
-    }
-    // state-role values X: rows t0..t0+31, columns 0..d (c = d: 1 or h)
-    {
-      constexpr int EPC = 16 / (int)sizeof(T);
-      constexpr int CPR = G::D / EPC;
-#pragma unroll
-      for (int it = 0; it < 32 * CPR / 64; ++it) {
-        const int flat = it * 64 + lane;
-        const int row = flat / CPR, ch = flat % CPR;
-        const int64_t tr = t0 + row;
-        float f[EPC];
-#pragma unroll
-        for (int kk = 0; kk < EPC; ++kk) f[kk] = 0.f;
-        if (tr < s1) {
-          const uint4 val = *reinterpret_cast<const uint4*>(Xr + tr * G::D + ch * EPC);
-          const T* e = reinterpret_cast<const T*>(&val);
-          const float sc = REV ? 1.f / den[tr] : 1.f;
-#pragma unroll
-          for (int kk = 0; kk < EPC; ++kk) f[kk] = (float)e[kk] * sc;
-        }
-#pragma unroll
-        for (int kk = 0; kk < EPC; ++kk) {
-          const T hi = (T)f[kk];
-          Xh[row * XSP + ch * EPC + kk] = hi;
-          if (USE_XL) Xl[row * XSP + ch * EPC + kk] = (T)(f[kk] - (float)hi);
-        }
-      }
-      if (h == 0) {
-        const float m = (!valid) ? 0.f : (REV ? hv[tok] : 1.f);
-        const T hi = (T)m;
-        Xh[n * XSP + G::D] = hi;
-        if (USE_XL) Xl[n * XSP + G::D] = (T)(m - (float)hi);
-      }
     }
     wave_lds_sync();
 
-    // dPhi of the output role, rows of the window: inter part from the bank
+    // inter: bank . U_a (U exact in T)
     f32x16 dp[ATU];
 #pragma unroll
     for (int at = 0; at < ATU; ++at) dp[at] = zero16();
-#pragma unroll
-    for (int q = 0; q < 2 * NC; ++q) {
-      frag uh, ul;
-      {
-        float u8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u8[i] = ut[8 * q + i];
-        E::split(u8, uh, ul);
-      }
-#pragma unroll
-      for (int at = 0; at < ATU; ++at) {
-        float v8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = acc[at][q >> 1][8 * (q & 1) + i];
-        frag ah, al;
-        E::split(v8, ah, al);
-        E::mma(ah, uh, dp[at]);
-        if (NS == 2) {
-          if (!UEXACT) E::mma(ah, ul, dp[at]);
-          E::mma(al, uh, dp[at]);
-        }
-      }
-    }
-    // intra part: m^T[tok_b][tok_a] = X_b . U_a (masked), then Phi_B^T m^T
     {
-      f32x16 mf = zero16();
+      const T* uf = S.UF[bb] + n * FS + 8 * h;
 #pragma unroll
-      for (int q = 0; q < 2 * NC; ++q) {
-        frag uh, ul;
-        {
-          float u8[8];
+      for (int q = 0; q < G::KD; ++q) {
+        const frag ub = *reinterpret_cast<const frag*>(uf + 16 * q);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) u8[i] = ut[8 * q + i];
-          E::split(u8, uh, ul);
-        }
-        frag xh, xl;
+        for (int at = 0; at < ATU; ++at) {
+          float v8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xh[i] = Xh[n * XSP + kmap(q, h, i)];
-        E::mma(xh, uh, mf);
-        if (NS == 2) {
-          if (!UEXACT) E::mma(xh, ul, mf);
-          if (USE_XL) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xl[i] = Xl[n * XSP + kmap(q, h, i)];
-            E::mma(xl, uh, mf);
+          for (int i = 0; i < 8; ++i) v8[i] = acc[at][q >> 1][8 * (q & 1) + i];
+          if (C::BANK_LO && E::NSPLIT == 2) {
+            frag hi, lo;
+            E::split(v8, hi, lo);
+            E::mma(hi, ub, dp[at]);
+            E::mma(lo, ub, dp[at]);
+          } else {
+            E::mma(E::pack(v8), ub, dp[at]);
           }
         }
       }
+    }
+    // intra scores mf[b][a] = X_b . U_a + xe_b ue_a, masked (b <= a forward, b >= a reverse)
+    f32x16 mf = zero16();
+    {
+      const T* uf = S.UF[bb] + n * FS + 8 * h;
+      const T* xf = S.XF[bb][0] + n * FS + 8 * h;
+      const T* xl = S.XF[bb][C::NXS - 1] + n * FS + 8 * h;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool keep = REV ? (tb >= n) : (tb <= n);
-        mf[v] = keep ? mf[v] : 0.f;
+      for (int q = 0; q < G::KD; ++q) {
+        const frag ub = *reinterpret_cast<const frag*>(uf + 16 * q);
+        E::mma(*reinterpret_cast<const frag*>(xf + 16 * q), ub, mf);
+        if (C::XSPLIT) E::mma(*reinterpret_cast<const frag*>(xl + 16 * q), ub, mf);
+      }
+    }
+    const float ue = S.TK[bb][1][n];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
+      const bool keep = REV ? (tb >= n) : (tb <= n);
+      mf[v] = keep ? mf[v] + S.TK[bb][0][tb] * ue : 0.f;
+    }
+    // mass term and intra part: dp[lr][a] += m[lr] ue_a + sum_b phi_B,b[lr] mf[b][a]
+    {
+      const T* pt = S.PhiBT[w];
+#pragma unroll
+      for (int at = 0; at < ATU; ++at) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dp[at][v] += S.Mw[w][32 * at + 8 * (v >> 2) + 4 * h + (v & 3)] * ue;
       }
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
+      for (int s = 0; s < 2; ++s) {
         float m8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m8[i] = mf[8 * q2 + i];
+        for (int i = 0; i < 8; ++i) m8[i] = mf[8 * s + i];
         frag mh, ml;
         E::split(m8, mh, ml);
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
-          frag pf;
+          const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
+          const T4 lo4 = *reinterpret_cast<const T4*>(r);
+          const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
+          frag af;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pf[i] = PhiT[(32 * at + n) * TTP + kmap(q2, h, i)];
-          E::mma(pf, mh, dp[at]);
-          if (NS == 2) E::mma(pf, ml, dp[at]);
+          for (int i = 0; i < 4; ++i) {
+            af[i] = lo4[i];
+            af[4 + i] = hi4[i];
+          }
+          E::mma(af, mh, dp[at]);
+          if (E::NSPLIT == 2) E::mma(af, ml, dp[at]);
         }
       }
     }
-    // softmax, tanh backward of the window's tables -> dPre
+    // softmax, tanh backward of the wave's tables -> dPre (forward walk: dphi = dp / den)
     {
+      const float sc = REV ? 1.f : S.TK[bb][2][n];
       float dphi[URP / 2];
 #pragma unroll
       for (int at = 0; at < ATU; ++at)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dphi[16 * at + v] = dp[at][v];
+        for (int v = 0; v < 16; ++v) dphi[16 * at + v] = dp[at][v] * sc;
       float dpre[G::NHP];
 #pragma unroll
       for (int i = 0; i < G::NHP; ++i) dpre[i] = 0.f;
       assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre);
-      constexpr int L0 = R0 / G::R;
-      constexpr int L1 = cdiv(R0 + URP, G::R) < G::LMAX ? cdiv(R0 + URP, G::R) : G::LMAX;
-      if (valid && h == 0) {
-        float* dst = a.dpre_out + (rb + tok) * G::NHP;
+      if (h == 0) {
 #pragma unroll
-        for (int hp = L0 * G::PE; hp < L1 * G::PE; ++hp) dst[hp] = dpre[hp];
+        for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
       }
     }
-    // bank update: C[c][lr] += X^T[c][tok] Phi_B[tok][lr]
+    // bank update: B[c][lr] += sum_b X_b[c] phi_B,b[lr]; X^T tiles (lane = column,
+    // registers = tokens in kmap order) from X rows times the identity
+    {
+      const T* pt = S.PhiBT[w];
+      frag pb[2][ATU];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      frag pfs[ATU];
-#pragma unroll
-      for (int at = 0; at < ATU; ++at)
-        pfs[at] = *reinterpret_cast<const frag*>(PhiT + (32 * at + n) * TTP + 16 * s + 8 * h);
-#pragma unroll
-      for (int ct = 0; ct < NC; ++ct) {
-        frag xh, xl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xh[i] = Xh[(16 * s + 8 * h + i) * XSP + 32 * ct + n];
-        if (USE_XL) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xl[i] = Xl[(16 * s + 8 * h + i) * XSP + 32 * ct + n];
-        }
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
-          E::mma(xh, pfs[at], acc[at][ct]);
-          if (USE_XL) E::mma(xl, pfs[at], acc[at][ct]);
+          const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
+          const T4 lo4 = *reinterpret_cast<const T4*>(r);
+          const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pb[s][at][i] = lo4[i];
+            pb[s][at][4 + i] = hi4[i];
+          }
+        }
+#pragma unroll
+      for (int sp = 0; sp < C::NXS; ++sp) {
+        const T* xf = S.XF[bb][sp] + n * FS + 8 * h;
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          f32x16 xt = zero16();
+          E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct)), idn[0], xt);
+          E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct + 1)), idn[1], xt);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float x8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x8[i] = xt[8 * s + i];
+            const frag xa = E::pack(x8);
+#pragma unroll
+            for (int at = 0; at < ATU; ++at) E::mma(xa, pb[s][at], acc[at][ct]);
+          }
         }
       }
+      // mass: lane half h sums tokens 16 h .. 16 h + 15 of row 32 at + n
+#pragma unroll
+      for (int at = 0; at < ATU; ++at) {
+        const T* r = pt + (32 * at + n) * TSP + 16 * h;
+        float sm = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sm += (float)r[t] * S.TK[bb][0][16 * h + t];
+        sm += xor32(sm);
+        if (h == 0) S.Mw[w][32 * at + n] += sm;
+      }
     }
-    wave_lds_sync();
+    // staging of chunk k + 1, dX of chunk k - 1
+    if (k + 1 < nch) stage(k + 1, bb ^ 1);
+    if (k > 0) dx_out(k - 1, bb ^ 1);
+    __syncthreads();
   }
+  dx_out(nch - 1, (int)((nch - 1) & 1));
 }
 
 template <typename T, class G, bool REV, int TG>
-__device__ __forceinline__ void transposed_dispatch(int tg, const CArgs& a, int64_t seg, int64_t bh,
-                                                    const typename Eng<T>::frag* Wf, T* PhiT, T* Xh, T* Xl) {
-  constexpr int URP = G::R > 32 ? G::R : 32;
-  if (tg == TG) {
-    transposed_body<T, G, REV, TG>(a, seg, bh, Wf, PhiT, Xh, Xl);
-  } else if constexpr ((TG + 1) * URP < G::LRP) {
-    transposed_dispatch<T, G, REV, TG + 1>(tg, a, seg, bh, Wf, PhiT, Xh, Xl);
+__device__ __forceinline__ void tw_dispatch(int w, const TWArgs& a, TWLds<T, G, REV>& S) {
+  if (w == TG) {
+    tw_body<T, G, REV, TG>(a, S);
+  } else if constexpr (TG + 1 < TWCfg<T, G, REV>::NM) {
+    tw_dispatch<T, G, REV, TG + 1>(w, a, S);
   }
 }
 
 template <typename T, class G, bool REV>
-__global__ __launch_bounds__(256) void race_causal_transposed(CArgs a) {
-  using E = Eng<T>;
-  using frag = typename E::frag;
-  constexpr int URP = G::R > 32 ? G::R : 32;
-  constexpr int NTG = G::LRP / URP;
-  constexpr int TTP = CC + 8;
-  constexpr int XSP = G::D + 32 + 8;
-  constexpr bool USE_XL = REV && E::NSPLIT == 2;   // X = [g | h] needs hi + lo parts
-  __shared__ frag Wf[G::NPT * G::KD * 64];
-  __shared__ T PhiT_all[4][URP * TTP];
-  __shared__ T Xh_all[4][CC * XSP];
-  __shared__ T Xl_all[USE_XL ? 4 : 1][CC * XSP];
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
-  __syncthreads();
-  const int w = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + w;
-  if (unit >= a.units) return;
-  const int tg = (int)(unit % NTG);
-  const int64_t seg = (unit / NTG) % a.nseg;
-  const int64_t bh = unit / NTG / a.nseg;
-  transposed_dispatch<T, G, REV, 0>(tg, a, seg, bh, Wf, PhiT_all[w], Xh_all[w], Xl_all[USE_XL ? w : 0]);
-}
-
-// ------------------------------------------------------------------ dX = dPre . W
-template <typename T, class G>
-__global__ __launch_bounds__(256) void race_dx(const float* __restrict__ dpre, const float* __restrict__ W, int L,
-                                               int P, int64_t N, int64_t BH, void* __restrict__ outv) {
-  using E = Eng<T>;
-  using frag = typename E::frag;
-  __shared__ frag WTf[G::CT * G::NQS * 64];
-  build_wt_frags<T, G>(W, L, P, WTf);
-  __syncthreads();
-  const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
-  const int64_t total = BH * N;
-  T* out = static_cast<T*>(outv);
-  for (int64_t base = (int64_t)blockIdx.x * TT + 32 * w; base < total; base += (int64_t)gridDim.x * TT) {
-    const int64_t tok = base + n;
-    const bool valid = tok < total;
-    float dp[G::NHP];
-#pragma unroll
-    for (int i = 0; i < G::NHP; ++i) dp[i] = valid ? dpre[tok * G::NHP + i] : 0.f;
-    float dx[G::D / 2];
-    dx_mma<T, G>(WTf, dp, dx);
-    if (valid) store_tl_row<T, G::D>(out + tok * G::D, dx);
-  }
+__global__ __launch_bounds__((TWCfg<T, G, REV>::NT)) void race_walk_tw(TWArgs a) {
+  __shared__ TWLds<T, G, REV> S;
+  tw_dispatch<T, G, REV, 0>(threadIdx.x >> 6, a, S);
 }
 
 // ------------------------------------------------------------------ small kernels

@@ -49,6 +49,11 @@ template <> struct Eng<bf16> {
   __device__ __forceinline__ static void mma(const frag& a, const frag& b, f32x16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // 16x16 tile, K32 step: lane l holds k = 8*(l/16) + i of row / column l%16;
+  // the accumulator holds element (m, n) in lane n + 16*(m/4), register m%4.
+  __device__ __forceinline__ static void mma16(const frag& a, const frag& b, f32x4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ __forceinline__ static frag pack(const float* v) {
     frag f;
 #pragma unroll
@@ -86,6 +91,11 @@ template <> struct Eng<float> {
   __device__ __forceinline__ static void mma(const frag& a, const frag& b, f32x16& c) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+  }
+  // 16x16 tile, K32 step (eight K4 MFMAs; element i of lane l is k = 8*(l/16) + i).
+  __device__ __forceinline__ static void mma16(const frag& a, const frag& b, f32x4& c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
   }
   __device__ __forceinline__ static frag pack(const float* v) {
     frag f;

@@ -65,15 +65,9 @@ struct Inst {
   static void walk(const WArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_walk_rw<T, G, MODE>), g, dim3(RWCfg<T, G, MODE>::NT), 0, s, a);
   }
-  static void c_dq(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_transposed<T, G, false>), g, dim3(256), 0, s, a);
-  }
-  static void c_dk(const CArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_causal_transposed<T, G, true>), g, dim3(256), 0, s, a);
-  }
-  static void dx(const float* dpre, const float* W, int L, int P, int64_t N, int64_t BH, void* out, dim3 g,
-                 hipStream_t s) {
-    hipLaunchKernelGGL((race_dx<T, G>), g, dim3(256), 0, s, dpre, W, L, P, N, BH, out);
+  template <bool REV>
+  static void tw(const TWArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_walk_tw<T, G, REV>), g, dim3(TWCfg<T, G, REV>::NT), 0, s, a);
   }
   // nc: compile the non-causal kernels; causal: compile the causal ones
   template <bool NC, bool CAUSAL>
@@ -84,7 +78,7 @@ struct Inst {
     k.softbucket_dbg = dbg;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
-      k.c_dq = c_dq; k.c_dk = c_dk; k.dx = dx;
+      k.tw_dq = tw<false>; k.tw_dk = tw<true>;
       k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>; k.w_fwd = walk<W_FWD>; k.w_h = walk<W_H>;
       k.w_dv = walk<W_DV>;
     }

@@ -6,16 +6,14 @@
 namespace race {
 
 struct NCArgs;
-struct CArgs;
 struct WArgs;
+struct TWArgs;
 
 typedef void (*nc_launch_fn)(const NCArgs&, dim3 grid, hipStream_t);
-typedef void (*c_launch_fn)(const CArgs&, dim3 grid, hipStream_t);
+typedef void (*tw_launch_fn)(const TWArgs&, dim3 grid, hipStream_t);
 typedef void (*w_launch_fn)(const WArgs&, dim3 grid, hipStream_t);
 typedef void (*dbg_launch_fn)(const void* X, const float* W, float beta, int L, int P, int64_t N,
                               float* out, dim3 grid, hipStream_t);
-typedef void (*dx_launch_fn)(const float* dpre, const float* W, int L, int P, int64_t N, int64_t BH, void* out,
-                             dim3 grid, hipStream_t);
 
 struct KernelSet {
   int dtype;   // race_dtype
@@ -24,10 +22,9 @@ struct KernelSet {
   nc_launch_fn readout, bwd_q, bwd_kv;     // non-causal; null when not compiled
   dbg_launch_fn softbucket_dbg;
   // causal; null when not compiled
-  c_launch_fn c_dq, c_dk;
-  dx_launch_fn dx;
-  // causal readout-layout walks (grid: segments x BH)
+  // causal walks (grid: segments x BH): readout layout, then transposed layout
   w_launch_fn w_segsum, w_gsum, w_fwd, w_h, w_dv;
+  tw_launch_fn tw_dq, tw_dk;
 };
 
 const KernelSet* kernel_sets_f32(int* count);
