@@ -39,14 +39,13 @@ ROW_PASSES = {
     "race_bwd_q": 3,           # read Q, dO, write dQ
     "race_bwd_kv": 4,          # read K, V, write dK, dV
     "race_causal_segsum": 2,   # read K, V
-    "race_causal_den": 2,      # read Q, K
     "race_causal_fwd": 4,      # read Q, K, V, write O
-    "race_causal_h": 4,        # read Q, K, V, dO
+    "race_causal_h": 4,        # read Q, K, V, dO (backward without O)
+    "race_causal_h_from_o": 2, # read dO, O
     "race_causal_gradsum": 2,  # read Q, dO
     "race_causal_dv": 4,       # read K, Q, dO, write dV
-    "race_causal_dphi_q": 4,   # read Q, K, V, dO
-    "race_causal_dphi_k": 4,   # read K, Q, dO, V
-    "race_causal_dx": 2,       # write dQ and dK
+    "race_causal_dq": 5,       # read Q, K, V, dO, write dQ
+    "race_causal_dk": 5,       # read K, Q, dO, V, write dK
 }
 
 
@@ -138,7 +137,7 @@ def main():
 
     def step():
         race.race_attn_fwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, O=O, state=st, workspace=wsf)
-        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, dQ=dQ, dK=dK, dV=dV, workspace=wsb)
+        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV, workspace=wsb)
 
     for _ in range(args.warmup):
         step()

@@ -86,9 +86,11 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
 
 /* Backward pass: the exact gradients dQ, dK, dV of sum(O * dO) with W and
  * beta held fixed (softmax, tanh and projection backward on both sides).
- * state must be the one written by race_attn_fwd on the same inputs; O may be
- * NULL (it is recomputed, not read).  workspace must hold
- * race_attn_workspace_bytes(..., 1). */
+ * state must be the one written by race_attn_fwd on the same inputs.  O is
+ * the forward output or NULL: the non-causal backward never reads it; the
+ * causal backward takes h = -(dO . O) / Den from it elementwise when given,
+ * and rebuilds Den O with one more walk over Q, K, V when it is NULL.
+ * workspace must hold race_attn_workspace_bytes(..., 1). */
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W,
                           float beta, int P, int L, int causal, const void* O,
                           const void* dO, void* dQ, void* dK, void* dV,

@@ -266,8 +266,8 @@ race_status causal_forward(const Plan& p, const void* Q, const void* K, const vo
 }
 
 race_status causal_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
-                            const void* dO, void* dQ, void* dK, void* dV, const void* state, char* ws,
-                            hipStream_t s) {
+                            const void* O, const void* dO, void* dQ, void* dK, void* dV, const void* state,
+                            char* ws, hipStream_t s) {
   race_status st;
   const float* prefix = static_cast<const float*>(state);
   const float* den = reinterpret_cast<const float*>(static_cast<const char*>(state) + align256(seg_bank_bytes(p)));
@@ -277,10 +277,14 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   float* gsuf = reinterpret_cast<float*>(ws + L.gsuf);
   const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
 
-  // 1. h = -(dO . O) / Den from a readout walk (O itself is not needed)
+  // 1. h = -(dO . O) / Den: elementwise from O when the caller has it, else
+  //    from a readout walk that rebuilds Den O without writing O
   race::WArgs w = walk_args(p, W, beta);
-  w.A_src = Q; w.B_src = K; w.X_src = V; w.dO = dO; w.bank_in = prefix; w.den = den; w.h_out = h;
-  {
+  if (O) {
+    ProfScope ps(s, "race_causal_h_from_o");
+    p.ks->h_from_o(dO, O, den, h, p.BH * p.N, s);
+  } else {
+    w.A_src = Q; w.B_src = K; w.X_src = V; w.dO = dO; w.bank_in = prefix; w.den = den; w.h_out = h;
     ProfScope ps(s, "race_causal_h");
     p.ks->w_h(w, grid, s);
   }
@@ -402,7 +406,6 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
                           int causal, const void* O, const void* dO, void* dQ, void* dK, void* dV,
                           const race_shape* shape, const void* state, size_t state_bytes_in, void* workspace,
                           size_t workspace_bytes_in, race_stream_t stream) {
-  (void)O;
   g_last_error.clear();
   Plan p;
   race_status st = make_plan(shape, P, L, causal, &p, true);
@@ -412,10 +415,12 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
   if (!state) return fail(RACE_ERR_INVALID_ARG, "state from race_attn_fwd is required");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(dO) || !aligned16(dQ) ||
-      !aligned16(dK) || !aligned16(dV) || !aligned16(state) || (workspace && !aligned16(workspace)))
+      !aligned16(dK) || !aligned16(dV) || !aligned16(state) || (O && !aligned16(O)) ||
+      (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
-  const void* ins[] = {Q, K, V, dO};
+  if (!p.causal) O = nullptr;   // the non-causal backward never reads O
+  const void* ins[] = {Q, K, V, dO, O};
   void* outs[] = {dQ, dK, dV};
   for (void* o : outs) {
     for (const void* i : ins)
@@ -432,7 +437,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  if (p.causal) return causal_backward(p, Q, K, V, W, beta, dO, dQ, dK, dV, state, ws, s);
+  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, state, ws, s);
 
   const float* content = static_cast<const float*>(state);
   const float* mass = content + (size_t)p.BH * p.LRP * p.D;

@@ -78,7 +78,7 @@ struct TWCfg {
   // The float32 bank enters the contraction over value columns as bf16
   // hi + lo parts (the softmax backward that follows subtracts nearly equal
   // terms).
-  static constexpr bool BANK_LO = true;
+  static constexpr bool BANK_LO = false;
   static_assert(G::LRP % URP == 0, "windows of whole tables");
 };
 
@@ -481,6 +481,32 @@ __global__ __launch_bounds__((TWCfg<T, G, REV>::NT)) void race_walk_tw(TWArgs a)
 }
 
 // ------------------------------------------------------------------ small kernels
+// h_t = -(dO_t . O_t) / den_t for every token when the caller hands over O:
+// 16 lanes per token row, one 16-byte chunk each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void race_h_from_o(const T* __restrict__ dO, const T* __restrict__ O,
+                                                     const float* __restrict__ den, float* __restrict__ h,
+                                                     int64_t total) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int LPT = D / EPC;   // lanes per token (16 bf16 / 32 f32 for d = 128)
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tok = gid / LPT;
+  const int part = (int)(gid % LPT);
+  float s = 0.f;
+  if (tok < total) {
+    const uint4 a = *reinterpret_cast<const uint4*>(dO + tok * D + part * EPC);
+    const uint4 b = *reinterpret_cast<const uint4*>(O + tok * D + part * EPC);
+    const T* x = reinterpret_cast<const T*>(&a);
+    const T* y = reinterpret_cast<const T*>(&b);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s += (float)x[e] * (float)y[e];
+  }
+#pragma unroll
+  for (int m = LPT / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (tok < total && part == 0) h[tok] = -s / den[tok];
+}
+
+
 // Exclusive scan over segments (forward: banks before each segment; reverse:
 // banks after it), one thread per (bh, bank element).
 static __global__ void race_seg_scan(const float* __restrict__ part, float* __restrict__ out, int nseg, int per, int BH,

@@ -69,6 +69,12 @@ struct Inst {
   static void tw(const TWArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_walk_tw<T, G, REV>), g, dim3(TWCfg<T, G, REV>::NT), 0, s, a);
   }
+  static void h_from_o(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t s) {
+    constexpr int LPT = D / (16 / (int)sizeof(T));
+    const int64_t threads = total * LPT;
+    hipLaunchKernelGGL((race_h_from_o<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const T*>(dO), static_cast<const T*>(O), den, h, total);
+  }
   // nc: compile the non-causal kernels; causal: compile the causal ones
   template <bool NC, bool CAUSAL>
   static KernelSet set(int dtype) {
@@ -78,7 +84,7 @@ struct Inst {
     k.softbucket_dbg = dbg;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
-      k.tw_dq = tw<false>; k.tw_dk = tw<true>;
+      k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;
       k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>; k.w_fwd = walk<W_FWD>; k.w_h = walk<W_H>;
       k.w_dv = walk<W_DV>;
     }

@@ -25,6 +25,7 @@ struct KernelSet {
   // causal walks (grid: segments x BH): readout layout, then transposed layout
   w_launch_fn w_segsum, w_gsum, w_fwd, w_h, w_dv;
   tw_launch_fn tw_dq, tw_dk;
+  void (*h_from_o)(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t);
 };
 
 const KernelSet* kernel_sets_f32(int* count);

@@ -122,3 +122,22 @@ def test_causal_deterministic():
         outs.append((O, st) + tuple(g))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("key,N,B,H,dtype", [(2, 700, 1, 2, "f32"), (5, 4133, 1, 2, "bf16")])
+def test_causal_backward_given_O(key, N, B, H, dtype):
+    """With the forward output handed over, h = -(dO . O) / Den comes from O
+    elementwise instead of a rebuilding walk: same oracle bar, and agreement
+    with the path that rebuilds Den O (fp32 I/O: to rounding; bf16 I/O: O is
+    rounded to bf16 before it is read, so to the bf16 bar)."""
+    w, inp, dev = _case(key, N, B, H, dtype)
+    say(f"causal bwd given O key={key} N={N} H={H} dtype={dtype}")
+    O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, True)
+    g_o = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, True, dev["dO"], state, O=O)
+    g_n = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, True, dev["dO"], state)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    for name, got, ref in zip(("dQ", "dK", "dV"), g_o, oracle_bwd(inp, True)):
+        check(name, got, ref, tol)
+    for name, a, b in zip(("dQ", "dK", "dV"), g_o, g_n):
+        check(name + " (O given vs rebuilt)", a, to64(b), tol)

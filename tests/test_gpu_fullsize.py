@@ -41,7 +41,8 @@ def _run(w):
     inp = ri.make_inputs(w, device="cuda")
     Wd = inp["W"].cuda()
     O, state = race.race_attn_fwd(inp["Q"], inp["K"], inp["V"], Wd, w.beta, w.P, w.L, w.causal)
-    dQ, dK, dV = race.race_attn_bwd(inp["Q"], inp["K"], inp["V"], Wd, w.beta, w.P, w.L, w.causal, inp["dO"], state)
+    dQ, dK, dV = race.race_attn_bwd(inp["Q"], inp["K"], inp["V"], Wd, w.beta, w.P, w.L, w.causal, inp["dO"], state,
+                                    O=O)
     torch.cuda.synchronize()
     say("  GPU forward + backward done")
     return inp, O, state, dQ, dK, dV
