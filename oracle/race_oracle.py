@@ -30,7 +30,8 @@ Conventions (readings where the pages are silent):
 * No epsilon is added to the denominator; all features are positive.
 * W has shape (L, P, d) and is shared by every batch row and head.
 * The backward pass is the exact gradient of the forward map with W and beta
-  held fixed.
+  held fixed; ``dbeta_head`` adds the gradient with respect to beta, the
+  inverse temperature the pages train (logits beta * u . v_r).
 
 Everything is float64 numpy.  Arrays for one head are (N, d); batched
 arrays are (B, H, N, d).
@@ -58,6 +59,9 @@ __all__ = [
     "query_terms",
     "grad_banks",
     "key_grads",
+    "beta_terms",
+    "dbeta_head",
+    "dbeta",
 ]
 
 
@@ -249,6 +253,61 @@ def _assign_backward(X, W, beta, Phi, dPhi):
     dU = float(beta) * np.matmul(dLam, C)
     dPre = dU * (1.0 - U * U)
     return np.matmul(dPre, np.asarray(W, dtype=np.float64)).sum(axis=0)
+
+
+def beta_terms(X, W, beta, Phi, dPhi):
+    """Per-row contribution to dL/dbeta of the soft assignments Phi(X).
+
+    The logits are Lambda_r = beta (u . v_r) (slides, frame "Soft corner
+    assignments make hashing differentiable"), so with the softmax backward
+    dLambda = Phi * (dPhi - rowsum(Phi * dPhi)) each row contributes
+    sum_l sum_r dLambda_r (u . v_r).  Returns an (N,) array.
+    """
+    U = _projected(X, W)                                   # (L, N, P)
+    C = corners(W.shape[1])
+    dLam = Phi * (dPhi - np.sum(Phi * dPhi, axis=-1, keepdims=True))
+    return np.sum(dLam * np.matmul(U, C.T), axis=(0, 2))
+
+
+def dbeta_head(Q, K, V, W, beta, dO, causal=False):
+    """dL/dbeta of L = sum(O * dO) for one head, as per-row terms of the
+    query side and of the key side: returns (terms_Q, terms_K), each (N,);
+    dbeta is their total.  The dPhi of each side are those of backward_head."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    Phi_Q = soft_assign(Q, W, beta)
+    Phi_K = soft_assign(K, W, beta)
+    if not causal:
+        content, mass = state_head(K, V, W, beta)
+        _, O, Den, g, h = query_terms(Q, dO, W, beta, content, mass)
+        dPhi_Q = np.matmul(g[None], content.transpose(0, 2, 1)) + h[None, :, None] * mass[:, None, :]
+        dcontent, dmass = grad_banks(Q, W, beta, g, h, Phi_Q)
+        dPhi_K = np.matmul(V[None], dcontent.transpose(0, 2, 1)) + dmass[:, None, :]
+    else:
+        L, N, R = Phi_Q.shape
+        O, Den = causal_forward_head(Q, K, V, W, beta, return_den=True)
+        g = dO / Den[:, None]
+        h = -np.sum(dO * O, axis=1) / Den
+        # prefix sums read by query t, suffix sums reaching key j (inclusive)
+        pc = np.cumsum(Phi_K[:, :, :, None] * V[None, :, None, :], axis=1)
+        pm = np.cumsum(Phi_K, axis=1)
+        dPhi_Q = np.einsum("nc,lnrc->lnr", g, pc) + h[None, :, None] * pm
+        sD = np.cumsum((Phi_Q[:, :, :, None] * g[None, :, None, :])[:, ::-1], axis=1)[:, ::-1]
+        sE = np.cumsum((Phi_Q * h[None, :, None])[:, ::-1], axis=1)[:, ::-1]
+        dPhi_K = np.einsum("nc,lnrc->lnr", V, sD) + sE
+    return beta_terms(Q, W, beta, Phi_Q, dPhi_Q), beta_terms(K, W, beta, Phi_K, dPhi_K)
+
+
+def dbeta(Q, K, V, W, beta, dO, causal=False):
+    """Batched dL/dbeta over (B, H, N, d) arrays (one beta for every head)."""
+    tot = 0.0
+    for b in range(np.asarray(Q).shape[0]):
+        for hh in range(np.asarray(Q).shape[1]):
+            tq, tk = dbeta_head(Q[b, hh], K[b, hh], V[b, hh], W, beta, dO[b, hh], causal)
+            tot += float(tq.sum() + tk.sum())
+    return tot
 
 
 def query_terms(Q, dO, W, beta, content, mass):

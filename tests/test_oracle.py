@@ -459,3 +459,38 @@ def test_bank_level_pieces_compose_to_backward():
     gk, gv = orc.key_grads(K, V, W, 2.0, dc, dm)
     np.testing.assert_allclose(gk, dK, rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(gv, dV, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("beta", [0.7, 4.0])
+def test_dbeta_finite_differences(causal, beta):
+    """dL/dbeta (query-side plus key-side terms) equals the central finite
+    difference of sum(O * dO) in beta (logits beta * u . v_r)."""
+    rng = np.random.default_rng(60 + 2 * causal + int(beta))
+    N, d, L, P = 9, 5, 2, 3
+    Q, K, V, W = _rand_head(rng, N, d, L, P)
+    dO = rng.standard_normal((N, d))
+    tq, tk = orc.dbeta_head(Q, K, V, W, beta, dO, causal)
+    eps = 1e-6
+    num = (_loss(Q, K, V, W, beta + eps, dO, causal) - _loss(Q, K, V, W, beta - eps, dO, causal)) / (2 * eps)
+    got = tq.sum() + tk.sum()
+    assert abs(got - num) <= 1e-7 * max(1.0, np.abs(tq).sum() + np.abs(tk).sum()), (causal, beta, got, num)
+    # the batched wrapper adds the same terms
+    assert abs(orc.dbeta(Q[None, None], K[None, None], V[None, None], W, beta, dO[None, None], causal) - got) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dbeta_invariants(causal):
+    """Constant V makes O independent of beta, so dbeta = 0; V -> V + c
+    shifts O by c and leaves dbeta unchanged."""
+    rng = np.random.default_rng(70 + causal)
+    N, d, L, P, beta = 200, 6, 3, 3, 2.5
+    Q, K, V, W = _rand_head(rng, N, d, L, P)
+    dO = rng.standard_normal((N, d))
+    tq, tk = orc.dbeta_head(Q, K, V, W, beta, dO, causal)
+    scale = np.abs(tq).sum() + np.abs(tk).sum()
+    c = rng.standard_normal(d)
+    tq2, tk2 = orc.dbeta_head(Q, K, V + c, W, beta, dO, causal)
+    assert abs((tq2.sum() + tk2.sum()) - (tq.sum() + tk.sum())) < 1e-10 * scale
+    tqc, tkc = orc.dbeta_head(Q, K, np.tile(c, (N, 1)), W, beta, dO, causal)
+    assert abs(tqc.sum() + tkc.sum()) < 1e-11 * scale
