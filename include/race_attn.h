@@ -84,8 +84,13 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
                           const race_shape* shape, void* state, size_t state_bytes,
                           void* workspace, size_t workspace_bytes, race_stream_t stream);
 
-/* Backward pass: the exact gradients dQ, dK, dV of sum(O * dO) with W and
- * beta held fixed (softmax, tanh and projection backward on both sides).
+/* Backward pass: the exact gradients dQ, dK, dV of sum(O * dO) with W
+ * held fixed (softmax, tanh and projection backward on both sides), and,
+ * when dbeta (a device pointer to one float, 4-byte aligned) is not NULL,
+ * dL/dbeta: beta multiplies the corner logits u . v_r (slides, frame "Soft
+ * corner assignments make hashing differentiable"), one beta for every
+ * batch row and head, so dbeta sums over both sides, every head, table and
+ * token; it is summed in a fixed order (same bits on every run).
  * state must be the one written by race_attn_fwd on the same inputs.  O is
  * the forward output or NULL: the non-causal backward never reads it; the
  * causal backward takes h = -(dO . O) / Den from it elementwise when given,
@@ -93,7 +98,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
  * workspace must hold race_attn_workspace_bytes(..., 1). */
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W,
                           float beta, int P, int L, int causal, const void* O,
-                          const void* dO, void* dQ, void* dK, void* dV,
+                          const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
                           const race_shape* shape, const void* state, size_t state_bytes,
                           void* workspace, size_t workspace_bytes, race_stream_t stream);
 

@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
         L.race_attn_workspace_bytes.restype = sz
         L.race_attn_fwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, sp, vp, sz, vp, sz, vp]
         L.race_attn_fwd.restype = i32
-        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp, vp, sp, vp, sz, vp, sz, vp]
+        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sp, vp, sz, vp, sz, vp]
         L.race_attn_bwd.restype = i32
         L.race_softbucket_debug.argtypes = [vp, vp, f32, i32, i32, sp, vp, vp]
         L.race_softbucket_debug.restype = i32
@@ -153,23 +153,31 @@ def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, work
 
 
 def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK=None, dV=None,
-                  workspace=None, stream=None):
-    """Exact gradients of sum(O * dO).  Returns (dQ, dK, dV)."""
+                  dbeta=None, workspace=None, stream=None):
+    """Exact gradients of sum(O * dO).  Returns (dQ, dK, dV), or (dQ, dK, dV,
+    dbeta) when dbeta is True (a new float32 tensor of one element) or a
+    float32 device tensor to write dL/dbeta into."""
     shape = _shape_of(Q)
     dQ = torch.empty_like(Q) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
     dV = torch.empty_like(V) if dV is None else dV
+    want_dbeta = dbeta is not None and dbeta is not False
+    if dbeta is True:
+        dbeta = torch.zeros(1, dtype=torch.float32, device=Q.device)
+    if want_dbeta and (dbeta.dtype != torch.float32 or not dbeta.is_cuda or dbeta.numel() < 1):
+        raise ValueError("dbeta must be a float32 device tensor with at least one element")
     wb = race_attn_workspace_bytes(shape, P, L, causal, True)
     if wb == 0:
         _check(lib().race_attn_bwd(None, None, None, None, float(beta), P, L, int(causal), None, None, None, None,
-                                   None, ctypes.byref(shape), None, 0, None, 0, None))
+                                   None, None, ctypes.byref(shape), None, 0, None, 0, None))
     workspace = _buffer(wb, Q.device, workspace)
     _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
                                int(L), int(causal), O.data_ptr() if O is not None else None, _dev(dO, "dO"),
-                               _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"), ctypes.byref(shape),
+                               _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
+                               dbeta.data_ptr() if want_dbeta else None, ctypes.byref(shape),
                                _dev(state, "state"), _bytes(state), _dev(workspace, "workspace"),
                                _bytes(workspace), _stream(stream)))
-    return dQ, dK, dV
+    return (dQ, dK, dV, dbeta) if want_dbeta else (dQ, dK, dV)
 
 
 def profile_enable(on: bool = True):

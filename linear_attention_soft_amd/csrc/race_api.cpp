@@ -173,8 +173,19 @@ size_t state_bytes(const Plan& p) {
 
 // Causal backward workspace: h [BH][N], gradient segment sums and their
 // reverse scan [BH][nseg][LRP][d+1] each.
+// Per-wave shares of dL/dbeta: query side then key side.  Non-causal: 4
+// waves per (chunk, head); causal: one wave per table window per (segment,
+// head).
+int64_t dbeta_parts_per_side(const Plan& p) {
+  if (!p.causal) return (int64_t)p.BH * p.nchunk * 4;
+  const int R = 1 << p.PE;
+  const int URP = R > 32 ? R : 32;
+  return (int64_t)p.BH * p.nseg * (p.LRP / URP);
+}
+size_t dbeta_bytes(const Plan& p) { return align256(2 * (size_t)dbeta_parts_per_side(p) * sizeof(float)); }
+
 struct CausalBwdWs {
-  size_t h, gpart, gsuf, total;
+  size_t h, gpart, gsuf, dbeta, total;
 };
 CausalBwdWs causal_bwd_ws(const Plan& p) {
   CausalBwdWs w{};
@@ -182,6 +193,7 @@ CausalBwdWs causal_bwd_ws(const Plan& p) {
   w.h = off;     off += align256(tok_bytes(p));
   w.gpart = off; off += align256(seg_bank_bytes(p));
   w.gsuf = off;  off += align256(seg_bank_bytes(p));
+  w.dbeta = off; off += dbeta_bytes(p);
   w.total = off;
   return w;
 }
@@ -190,7 +202,7 @@ size_t workspace_bytes(const Plan& p, bool bwd) {
   if (!p.causal) {
     size_t w = align256(part_bytes(p));
     if (!bwd) w += align256(bank_bytes(p));          // bank when no state buffer is given
-    else w += align256(bank_bytes(p));               // gradient bank dcontent, dmass
+    else w += align256(bank_bytes(p)) + dbeta_bytes(p);   // gradient bank dcontent, dmass; dbeta shares
     return w;
   }
   // forward: segment sums, and (when no state buffer is given) the segment
@@ -227,6 +239,10 @@ race::WArgs walk_args(const Plan& p, const float* W, float beta) {
   race::WArgs w{};
   w.W = W; w.beta = beta; w.L = p.L; w.P = p.P; w.N = p.N; w.seg_tokens = p.seg_tokens; w.nseg = p.nseg;
   return w;
+}
+
+void launch_dbeta_finalize(const Plan& p, const float* parts, float* dbeta, hipStream_t s) {
+  hipLaunchKernelGGL(race::race_dbeta_finalize, dim3(1), dim3(256), 0, s, parts, 2 * dbeta_parts_per_side(p), dbeta);
 }
 
 void launch_seg_scan(const Plan& p, const float* part, float* out, int reverse, hipStream_t s) {
@@ -266,8 +282,8 @@ race_status causal_forward(const Plan& p, const void* Q, const void* K, const vo
 }
 
 race_status causal_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
-                            const void* O, const void* dO, void* dQ, void* dK, void* dV, const void* state,
-                            char* ws, hipStream_t s) {
+                            const void* O, const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
+                            const void* state, char* ws, hipStream_t s) {
   race_status st;
   const float* prefix = static_cast<const float*>(state);
   const float* den = reinterpret_cast<const float*>(static_cast<const char*>(state) + align256(seg_bank_bytes(p)));
@@ -311,7 +327,8 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   race::TWArgs t{};
   t.W = W; t.beta = beta; t.L = p.L; t.P = p.P; t.N = p.N; t.seg_tokens = p.seg_tokens; t.nseg = p.nseg;
   t.den = den; t.hvec = h;
-  t.A_src = Q; t.B_src = K; t.X_src = V; t.U_src = dO; t.bank_in = prefix; t.dX = dQ;
+  float* bparts = dbeta ? reinterpret_cast<float*>(ws + L.dbeta) : nullptr;
+  t.A_src = Q; t.B_src = K; t.X_src = V; t.U_src = dO; t.bank_in = prefix; t.dX = dQ; t.dbeta_part = bparts;
   {
     ProfScope ps(s, "race_causal_dq");
     p.ks->tw_dq(t, grid, s);
@@ -319,11 +336,17 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   if ((st = check_launch("race_causal_dq")) != RACE_OK) return st;
   // 5. dK: reverse transposed walk (dPhi_K) from the gradient suffix banks
   t.A_src = K; t.B_src = Q; t.X_src = dO; t.U_src = V; t.bank_in = gsuf; t.dX = dK;
+  t.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
   {
     ProfScope ps(s, "race_causal_dk");
     p.ks->tw_dk(t, grid, s);
   }
-  return check_launch("race_causal_dk");
+  if ((st = check_launch("race_causal_dk")) != RACE_OK) return st;
+  if (dbeta) {
+    ProfScope ps(s, "race_dbeta_finalize");
+    launch_dbeta_finalize(p, bparts, dbeta, s);
+  }
+  return check_launch("race_dbeta_finalize");
 }
 
 }  // namespace
@@ -403,7 +426,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
 }
 
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
-                          int causal, const void* O, const void* dO, void* dQ, void* dK, void* dV,
+                          int causal, const void* O, const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
                           const race_shape* shape, const void* state, size_t state_bytes_in, void* workspace,
                           size_t workspace_bytes_in, race_stream_t stream) {
   g_last_error.clear();
@@ -418,6 +441,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
       !aligned16(dK) || !aligned16(dV) || !aligned16(state) || (O && !aligned16(O)) ||
       (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  if (dbeta && ((uintptr_t)dbeta & 3u)) return fail(RACE_ERR_INVALID_ARG, "dbeta must be 4-byte aligned");
   const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
   if (!p.causal) O = nullptr;   // the non-causal backward never reads O
   const void* ins[] = {Q, K, V, dO, O};
@@ -427,7 +451,10 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
       if (overlaps(o, tbytes, i, tbytes)) return fail(RACE_ERR_INVALID_ARG, "an output overlaps an input");
     for (void* o2 : outs)
       if (o2 != o && overlaps(o, tbytes, o2, tbytes)) return fail(RACE_ERR_INVALID_ARG, "outputs overlap");
+    if (overlaps(o, tbytes, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dbeta overlaps an output");
   }
+  for (const void* i : ins)
+    if (overlaps(i, tbytes, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dbeta overlaps an input");
   const size_t need_state = state_bytes(p);
   if (state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
@@ -437,7 +464,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, state, ws, s);
+  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, state, ws, s);
 
   const float* content = static_cast<const float*>(state);
   const float* mass = content + (size_t)p.BH * p.LRP * p.D;
@@ -445,11 +472,12 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   float* dbank = reinterpret_cast<float*>(ws + align256(part_bytes(p)));
   float* dcontent = dbank;
   float* dmass = dbank + (size_t)p.BH * p.LRP * p.D;
+  float* bparts = dbeta ? reinterpret_cast<float*>(ws + align256(part_bytes(p)) + align256(bank_bytes(p))) : nullptr;
 
   race::NCArgs a{};
   a.X = Q; a.Y = dO; a.out0 = dQ; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.st_content = content; a.st_mass = mass; a.part = part;
-  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
+  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.dbeta_part = bparts;
   {
     ProfScope ps(s, "race_bwd_q");
     p.ks->bwd_q(a, dim3(p.nchunk, (unsigned)p.BH), s);
@@ -463,11 +491,17 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   race::NCArgs b{};
   b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = W; b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
   b.st_content = dcontent; b.st_mass = dmass; b.chunk_tokens = p.chunk_tokens; b.nchunk = p.nchunk;
+  b.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
   {
     ProfScope ps(s, "race_bwd_kv");
     p.ks->bwd_kv(b, dim3(p.nchunk, (unsigned)p.BH), s);
   }
-  return check_launch("race_bwd_kv");
+  if ((st = check_launch("race_bwd_kv")) != RACE_OK) return st;
+  if (dbeta) {
+    ProfScope ps(s, "race_dbeta_finalize");
+    launch_dbeta_finalize(p, bparts, dbeta, s);
+  }
+  return check_launch("race_dbeta_finalize");
 }
 
 race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L, const race_shape* shape,

@@ -52,6 +52,7 @@ struct TWArgs {
   const float* den;       // [BH][N]
   const float* hvec;      // [BH][N]
   const float* W;
+  float* dbeta_part;      // when set: [BH][nseg][waves] shares of dL/dbeta
   float beta;
   int L, P;
   int64_t N;
@@ -281,6 +282,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
   load_stage(0);
   stage(0, 0);
   __syncthreads();
+  float bsum = 0.f;
 
   for (int64_t k = 0; k < nch; ++k) {
     const int bb = (int)(k & 1);
@@ -400,10 +402,11 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
       for (int at = 0; at < ATU; ++at)
 #pragma unroll
         for (int v = 0; v < 16; ++v) dphi[16 * at + v] = dp[at][v] * sc;
-      float dpre[G::NHP];
+      float dpre[G::NHP], bterm = 0.f;
 #pragma unroll
       for (int i = 0; i < G::NHP; ++i) dpre[i] = 0.f;
-      assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre);
+      assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre, bterm);
+      if (valid && h == 0) bsum += bterm;
       if (h == 0) {
 #pragma unroll
         for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
@@ -463,6 +466,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     __syncthreads();
   }
   dx_out(nch - 1, (int)((nch - 1) & 1));
+  if (a.dbeta_part) {
+    bsum = wave_sum(bsum);
+    if (lane == 0) a.dbeta_part[((size_t)bh * a.nseg + seg) * C::NM + w] = bsum;
+  }
 }
 
 template <typename T, class G, bool REV, int TG>
@@ -481,6 +488,20 @@ __global__ __launch_bounds__((TWCfg<T, G, REV>::NT)) void race_walk_tw(TWArgs a)
 }
 
 // ------------------------------------------------------------------ small kernels
+// dbeta = sum of the per-wave shares, in a fixed order (one workgroup of 256).
+static __global__ void race_dbeta_finalize(const float* __restrict__ part, int64_t n, float* __restrict__ out) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int m = 128; m > 0; m >>= 1) {
+    if ((int)threadIdx.x < m) red[threadIdx.x] += red[threadIdx.x + m];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = red[0];
+}
+
 // h_t = -(dO_t . O_t) / den_t for every token when the caller hands over O:
 // 16 lanes per token row, one 16-byte chunk each.
 template <typename T, int D>

@@ -414,11 +414,13 @@ __device__ __forceinline__ void tl_frag_split(const float (&x)[M / 2], int q,
 // dLambda = phi * (dphi - sum_r phi dphi) per table; dU_t = beta sum_r dLambda_r v_{r,t};
 // dPre = dU * (1 - u^2).  Both lane halves end with every dPre value.  Works on
 // bucket rows [R0, R0 + NROWS), which must hold whole tables; dPre slots of
-// tables outside the window are left untouched.
+// tables outside the window are left untouched.  bterm receives the token's
+// share of dL/dbeta over these tables: sum_r dLambda_r (u . v_r)
+// = sum_t u_t sum_r dLambda_r v_{r,t} (the logits are beta u . v_r).
 template <class G, int R0, int NROWS>
 __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 2], const float (&dphi)[NROWS / 2],
                                                      const float (&u)[G::NHP], float beta,
-                                                     float (&dpre)[G::NHP]) {
+                                                     float (&dpre)[G::NHP], float& bterm) {
   const int h = lane_id() >> 5;
   const float sgn2 = h ? 1.f : -1.f;
   constexpr int L0 = R0 / G::R;
@@ -457,14 +459,31 @@ __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 
       const float d = du[t] + xor32(du[t]);
       const float uu = u[l * G::PE + t];
       dpre[l * G::PE + t] = beta * d * (1.f - uu * uu);
+      bterm += uu * d;
     }
   }
 }
 
+template <class G, int R0, int NROWS>
+__device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 2], const float (&dphi)[NROWS / 2],
+                                                     const float (&u)[G::NHP], float beta,
+                                                     float (&dpre)[G::NHP]) {
+  float unused = 0.f;
+  assign_backward_rows<G, R0, NROWS>(phi, dphi, u, beta, dpre, unused);
+}
+
+// Sum over the 64 lanes of a wave (every lane ends with the total).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
 template <class G>
 __device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], const float (&dphi)[G::LRP / 2],
-                                                const float (&u)[G::NHP], float beta, float (&dpre)[G::NHP]) {
-  assign_backward_rows<G, 0, G::LRP>(phi, dphi, u, beta, dpre);
+                                                const float (&u)[G::NHP], float beta, float (&dpre)[G::NHP],
+                                                float& bterm) {
+  assign_backward_rows<G, 0, G::LRP>(phi, dphi, u, beta, dpre, bterm);
 }
 
 // Order this wave's LDS writes before its later LDS reads of other lanes'

@@ -41,6 +41,9 @@ struct NCArgs {
   // instead of ones (the causal backward's gradient sums Phi_Q^T [g | h]).
   const float* tok_den;
   const float* tok_extra;
+  // backward kernels: when set, each wave writes its share of dL/dbeta to
+  // dbeta_part[(bh * nchunk + chunk) * 4 + wave]
+  float* dbeta_part;
 };
 
 constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
@@ -424,6 +427,7 @@ __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
 
   const int tl = 32 * w + n;
   const int64_t last = t_end - 1;
+  float bsum = 0.f;
   auto tile = [&](const frag (&cx)[G::KD], const frag (&yy)[G::KD], int64_t base) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
@@ -469,8 +473,9 @@ __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
         const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
         dphi[16 * at + v] = av[16 * at + v] * inv + massL[lr] * hval;
       }
-    float dpre[G::NHP];
-    assign_backward<G>(phi, dphi, u, a.beta, dpre);
+    float dpre[G::NHP], bterm = 0.f;
+    assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
+    if (valid && h == 0) bsum += bterm;
     // the wave's 32 rows of Bs are free until the dO rows are staged below
     dx_mma_stage<T, G>(WTf, dpre, Bs + 32 * w * BSP);
     OutStage<G::D, T>::flush(Bs + 32 * w * BSP, dQ, base + 32 * w, t_end);
@@ -518,6 +523,10 @@ __global__ __launch_bounds__(256) void race_bwd_q(NCArgs a) {
     base += TT;
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), racc);
+  if (a.dbeta_part) {
+    bsum = wave_sum(bsum);
+    if (lane == 0) a.dbeta_part[((size_t)bh * a.nchunk + chunk) * 4 + w] = bsum;
+  }
 }
 
 // ------------------------------------------------------------------ race_bwd_kv
@@ -553,6 +562,7 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   const float beta2 = 2.f * a.beta;
 
   const int64_t last = t_end - 1;
+  float bsum = 0.f;
   auto tile = [&](const frag (&cx)[G::KD], const frag (&cy)[G::KD], int64_t base) {
     const int64_t tok = base + n;
     const bool valid = tok < t_end;
@@ -588,11 +598,11 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
         dphi[16 * at + v] = d[v] + dmassL[lr];
       }
     }
-    float dpre[G::NHP];
-    assign_backward<G>(phi, dphi, u, a.beta, dpre);
+    float dpre[G::NHP], bterm = 0.f;
+    assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
+    if (valid && h == 0) bsum += bterm;
     dx_mma_stage<T, G>(WTf, dpre, OS[w]);
     OutStage<G::D, T>::flush(OS[w], dK, base, t_end);
-    (void)valid;
   };
   frag xa[G::KD], ya[G::KD], xb[G::KD], yb[G::KD];
   int64_t base = t_begin + 32 * w;
@@ -619,6 +629,10 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     tile(xb, yb, base);
     base += TT;
+  }
+  if (a.dbeta_part) {
+    bsum = wave_sum(bsum);
+    if (lane == 0) a.dbeta_part[((size_t)bh * a.nchunk + chunk) * 4 + w] = bsum;
   }
 }
 

@@ -104,15 +104,17 @@ def test_backward_rejects_bad_arguments():
     s = _shape()
     base = [FAKE + i * 0x1000000 for i in range(12)]
 
-    def call(state=base[9], stateb=1 << 30, ws=base[10], wsb=1 << 30, beta=1.0, dq=base[6]):
+    def call(state=base[9], stateb=1 << 30, ws=base[10], wsb=1 << 30, beta=1.0, dq=base[6], dbeta=None):
         return Lb.race_attn_bwd(base[0], base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, 0, None, base[5],
-                                dq, base[7], base[8], ctypes.byref(s), state, stateb, ws, wsb, None)
+                                dq, base[7], base[8], dbeta, ctypes.byref(s), state, stateb, ws, wsb, None)
 
     assert call(state=None) == 1
     assert call(beta=math.nan) == 1
     assert call(stateb=4) == 3
     assert call(wsb=4) == 3
     assert call(dq=base[0]) == 1                # dQ overlaps Q
+    assert call(dbeta=base[1] + 2) == 1         # dbeta misaligned
+    assert call(dbeta=base[1] + 64) == 1        # dbeta inside K
 
 
 def test_softbucket_debug_rejects_small_P():
