@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dbeta", action="store_true",
+                    help="also compute dL/dbeta in every backward (beta learned)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 22)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 1 GiB once (reference kernel for rocprofv3 byte counters)")
@@ -133,11 +135,13 @@ def main():
     st = torch.empty(race.race_attn_state_bytes(shape, w.P, w.L, w.causal), dtype=torch.uint8, device=dev)
     wsf = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, False), dtype=torch.uint8, device=dev)
     wsb = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, True), dtype=torch.uint8, device=dev)
+    db = torch.zeros(1, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step():
         race.race_attn_fwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, O=O, state=st, workspace=wsf)
-        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV, workspace=wsb)
+        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV,
+                           dbeta=db if args.dbeta else None, workspace=wsb)
 
     for _ in range(args.warmup):
         step()
@@ -197,7 +201,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; iid N(0,1) Q, K, V, dO; Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "L": w.L,
-                   "beta": w.beta, "causal": w.causal, "global_batch": w.B, "seq_len": w.N},
+                   "beta": w.beta, "causal": w.causal, "dbeta": bool(args.dbeta), "global_batch": w.B,
+                   "seq_len": w.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": dname, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": avg_ms},
