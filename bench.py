@@ -63,7 +63,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--workload", type=int, default=None,
+                    help="workload key (default 4; with --decode, 2)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the recurrent decode step instead: one new token per sequence per step from a "
+                         "state prefilled with the workload's N tokens")
+    ap.add_argument("--decode-batch", type=int, default=None, help="batch rows for --decode (default: workload's)")
+    ap.add_argument("--decode-prompt", type=int, default=4096,
+                    help="prompt tokens prefilled before --decode (the state size does not depend on it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dbeta", action="store_true",
                     help="also compute dL/dbeta in every backward (beta learned)")
@@ -111,6 +118,63 @@ def load_traffic(workload_name: str, kernel: str, launches_tokens: int):
     return float(k["bytes_per_launch"])
 
 
+def bench_decode(args):
+    """Decode steps: every (batch, head) sequence takes one new token per step
+    (update-then-read on its fixed-size bank), inputs resident in HBM."""
+    import torch
+    import linear_attention_soft_amd as race
+    import race_inputs as ri
+
+    w = ri.WORKLOADS[2 if args.workload is None else args.workload]
+    w = w.with_size(N=min(w.N, args.decode_prompt), B=args.decode_batch or w.B)
+    dev = "cuda"
+    steps, n_new = args.steps * 10, 1
+    print(f"# decode on {w.name}: prompt of {w.N} tokens, {steps} steps of {n_new} token", file=sys.stderr,
+          flush=True)
+    prompt = ri.make_inputs(w, device=dev)
+    W = prompt["W"].to(dev)
+    st = race.race_attn_decode_prefill(prompt["K"], prompt["V"], W, w.beta, w.P, w.L)
+    nw = w.with_size(N=(args.warmup + steps) * n_new)
+    new = ri.make_inputs(nw, device=dev, seed_base=7000 + w.key)
+    toks = [{k: new[k][:, :, i * n_new:(i + 1) * n_new].contiguous() for k in ("Q", "K", "V")}
+            for i in range(args.warmup + steps)]
+    O = torch.empty_like(toks[0]["Q"])
+    race.profile_enable(False)
+    for i in range(args.warmup):
+        race.race_attn_decode(toks[i]["Q"], toks[i]["K"], toks[i]["V"], W, w.beta, w.P, w.L, st, O=O)
+    torch.cuda.synchronize()
+    race.profile_reset()
+    race.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.warmup, args.warmup + steps):
+        race.race_attn_decode(toks[i]["Q"], toks[i]["K"], toks[i]["V"], W, w.beta, w.P, w.L, st, O=O)
+    e1.record()
+    torch.cuda.synchronize()
+    race.profile_enable(False)
+    ms_step = e0.elapsed_time(e1) / steps
+    kern = race.profile_report()
+    cnt, tot = kern.get("race_decode", (1, ms_step))
+    avg_ms = tot / cnt
+    s = 2 if w.dtype == "bf16" else 4
+    state_bytes = st.numel() * 4
+    alg = 2 * state_bytes + 4 * w.B * w.H * n_new * w.d * s   # state read + write; q, k, v, o rows
+    achieved = alg / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "RACE decode tokens/s (one new token per sequence per step, fixed-size state)",
+        "value": w.B * n_new / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
+        "config": {"workload": "decode_" + w.name, "B": w.B, "H": w.H, "prompt_tokens": w.N, "d": w.d, "P": w.P,
+                   "L": w.L, "beta": w.beta, "new_tokens_per_step": n_new, "state_bytes": state_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "race_decode",
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": avg_ms},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -121,7 +185,9 @@ def main():
     import linear_attention_soft_amd as race
     import race_inputs as ri
 
-    w = ri.WORKLOADS[args.workload]
+    if args.decode:
+        return bench_decode(args)
+    w = ri.WORKLOADS[4 if args.workload is None else args.workload]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     race.lib()
     dev = "cuda"

@@ -102,6 +102,36 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
                           const race_shape* shape, const void* state, size_t state_bytes,
                           void* workspace, size_t workspace_bytes, race_stream_t stream);
 
+/* Recurrent decode (slides, frame "Causality is a prefix update of the same
+ * statistics"): the causal layer as a fixed-size state per (batch, head),
+ * the bucket bank after the tokens seen so far: float32 content
+ * [B*H][LRP][d] followed by mass [B*H][LRP] (LRP = L * 2^max(P,3) padded to
+ * the compiled size; the same layout as the non-causal forward's state).
+ * shape->N is the number of tokens of the call; the state size does not
+ * depend on it. */
+size_t race_attn_decode_state_bytes(const race_shape* shape, int P, int L);
+
+/* Workspace of race_attn_decode_prefill for a prompt of shape->N tokens. */
+size_t race_attn_decode_prefill_workspace_bytes(const race_shape* shape, int P, int L);
+
+/* The state after the prompt K, V [B][H][N][d]: the bank of all N tokens
+ * (overwrites state).  Deterministic fixed-order sums. */
+race_status race_attn_decode_prefill(const void* K, const void* V, const float* W, float beta,
+                                     int P, int L, const race_shape* shape, void* state,
+                                     size_t state_bytes, void* workspace, size_t workspace_bytes,
+                                     race_stream_t stream);
+
+/* Decode N new tokens Q, K, V [B][H][N][d] in order, updating state in
+ * place: for each token the key and value enter the bank first, then
+ * O_t = sum_l phi(Q_t) content / sum_l phi(Q_t) mass (the token attends to
+ * itself and to every earlier token).  A zeroed state is the empty prefix.
+ * Soft assignments are computed in float32 without rounding; O has the I/O
+ * dtype.  Tokens are taken one after another inside one workgroup per
+ * (batch, head): meant for a few tokens per call. */
+race_status race_attn_decode(const void* Q, const void* K, const void* V, const float* W,
+                             float beta, int P, int L, void* O, const race_shape* shape,
+                             void* state, size_t state_bytes, race_stream_t stream);
+
 /* Test export: the soft assignments phi^(l)(X) as float32 [B*H][N][L][2^P]
  * (slides frame "Soft corner assignments make hashing differentiable").
  * X has the I/O dtype; no workspace. */

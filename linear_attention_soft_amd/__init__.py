@@ -14,7 +14,8 @@ import torch
 
 __all__ = [
     "RaceError", "lib", "library_path", "race_attn_fwd", "race_attn_bwd", "race_softbucket_debug",
-    "race_attn_state_bytes", "race_attn_workspace_bytes", "EXPORTED_SYMBOLS",
+    "race_attn_state_bytes", "race_attn_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode",
+    "race_attn_decode_state_bytes", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,8 @@ library_path = os.path.join(_PKG, "librace_attn.so")
 RACE_F32, RACE_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("race_attn_fwd", "race_attn_bwd", "race_attn_state_bytes", "race_attn_workspace_bytes",
                     "race_softbucket_debug", "race_status_string", "race_last_error", "race_profile_enable",
-                    "race_profile_reset", "race_profile_report")
+                    "race_profile_reset", "race_profile_report", "race_attn_decode_state_bytes",
+                    "race_attn_decode_prefill_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode")
 
 
 class RaceError(RuntimeError):
@@ -71,6 +73,14 @@ def lib() -> ctypes.CDLL:
         L.race_profile_reset.restype = None
         L.race_profile_report.argtypes = [ctypes.c_char_p, sz]
         L.race_profile_report.restype = sz
+        L.race_attn_decode_state_bytes.argtypes = [sp, i32, i32]
+        L.race_attn_decode_state_bytes.restype = sz
+        L.race_attn_decode_prefill_workspace_bytes.argtypes = [sp, i32, i32]
+        L.race_attn_decode_prefill_workspace_bytes.restype = sz
+        L.race_attn_decode_prefill.argtypes = [vp, vp, vp, f32, i32, i32, sp, vp, sz, vp, sz, vp]
+        L.race_attn_decode_prefill.restype = i32
+        L.race_attn_decode.argtypes = [vp, vp, vp, vp, f32, i32, i32, vp, sp, vp, sz, vp]
+        L.race_attn_decode.restype = i32
         _LIB = L
     return _LIB
 
@@ -210,3 +220,36 @@ def race_softbucket_debug(X, W, beta, P, L, stream=None):
     _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
                                        ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
     return out
+
+
+def race_attn_decode_state_bytes(shape: race_shape, P: int, L: int) -> int:
+    return lib().race_attn_decode_state_bytes(ctypes.byref(shape), int(P), int(L))
+
+
+def race_attn_decode_prefill(K, V, W, beta, P, L, state=None, workspace=None, stream=None):
+    """Decode state (float32 bank: content [B*H][LRP][d] then mass [B*H][LRP])
+    after the prompt K, V [B, H, N, d].  Returns the state tensor."""
+    shape = _shape_of(K)
+    nb = race_attn_decode_state_bytes(shape, P, L)
+    if nb == 0:
+        _check(lib().race_attn_decode_prefill(None, None, None, float(beta), int(P), int(L), ctypes.byref(shape),
+                                              None, 0, None, 0, None))
+    if state is None:
+        state = torch.empty(nb // 4, dtype=torch.float32, device=K.device)
+    wb = lib().race_attn_decode_prefill_workspace_bytes(ctypes.byref(shape), int(P), int(L))
+    workspace = _buffer(wb, K.device, workspace)
+    _check(lib().race_attn_decode_prefill(_dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P), int(L),
+                                          ctypes.byref(shape), _dev(state, "state"), _bytes(state),
+                                          _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
+    return state
+
+
+def race_attn_decode(Q, K, V, W, beta, P, L, state, O=None, stream=None):
+    """Decode the new tokens Q, K, V [B, H, n, d] in order from state (updated
+    in place; a zeroed state is the empty prefix).  Returns O."""
+    shape = _shape_of(Q)
+    O = torch.empty_like(Q) if O is None else O
+    _check(lib().race_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                  int(L), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"), _bytes(state),
+                                  _stream(stream)))
+    return O

@@ -17,6 +17,7 @@
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
 #include "race_walk.hpp"
+#include "race_decode.hpp"
 
 namespace race {
 // ------------------------------------------------------------------ fixed-order chunk sums
@@ -112,6 +113,20 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
     if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
     if (causal && (!k.w_fwd || !k.tw_dq)) continue;
     if (!causal && !k.readout) continue;
+    if (!best || k.LRP < best->LRP) best = &k;
+  }
+  return best;
+}
+
+// Decode and prefill need the bucket reduce and the decode kernel only (every
+// compiled set has them); smallest padded bank first.
+const race::KernelSet* find_decode_set(int dtype, int D, int PE, int LRP_min) {
+  int count = 0;
+  const race::KernelSet* sets = dtype == RACE_BF16 ? race::kernel_sets_bf16(&count) : race::kernel_sets_f32(&count);
+  const race::KernelSet* best = nullptr;
+  for (int i = 0; i < count; ++i) {
+    const race::KernelSet& k = sets[i];
+    if (k.D != D || k.PE != PE || k.LRP < LRP_min || !k.decode || !k.reduce) continue;
     if (!best || k.LRP < best->LRP) best = &k;
   }
   return best;
@@ -502,6 +517,99 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
     launch_dbeta_finalize(p, bparts, dbeta, s);
   }
   return check_launch("race_dbeta_finalize");
+}
+
+// ---- recurrent decode: the state is the bank [BH][LRP][d] + mass [BH][LRP]
+race_status decode_plan(const race_shape* shape, int P, int L, Plan* p) {
+  race_status st = make_plan(shape, P, L, 0, p, false);
+  if (st != RACE_OK) return st;
+  p->ks = find_decode_set(p->dtype, (int)p->D, p->PE, p->LRP);
+  if (!p->ks) return fail(RACE_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, d, P, L)");
+  p->LRP = p->ks->LRP;
+  return RACE_OK;
+}
+
+size_t race_attn_decode_state_bytes(const race_shape* shape, int P, int L) {
+  Plan p;
+  if (decode_plan(shape, P, L, &p) != RACE_OK) return 0;
+  return bank_bytes(p);
+}
+
+size_t race_attn_decode_prefill_workspace_bytes(const race_shape* shape, int P, int L) {
+  Plan p;
+  if (decode_plan(shape, P, L, &p) != RACE_OK) return 0;
+  return align256(part_bytes(p));
+}
+
+race_status race_attn_decode_prefill(const void* K, const void* V, const float* W, float beta, int P, int L,
+                                     const race_shape* shape, void* state, size_t state_bytes_in, void* workspace,
+                                     size_t workspace_bytes_in, race_stream_t stream) {
+  g_last_error.clear();
+  Plan p;
+  race_status st = decode_plan(shape, P, L, &p);
+  if (st != RACE_OK) return st;
+  if (!K || !V || !W || !state) return fail(RACE_ERR_INVALID_ARG, "K, V, W and state must be non-NULL");
+  if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(state) || (workspace && !aligned16(workspace)))
+    return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const size_t need_state = bank_bytes(p), need_ws = align256(part_bytes(p));
+  if (state_bytes_in < need_state)
+    return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
+  if (!workspace || workspace_bytes_in < need_ws)
+    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+  if (overlaps(state, need_state, K, tbytes) || overlaps(state, need_state, V, tbytes) ||
+      overlaps(state, need_state, workspace, need_ws))
+    return fail(RACE_ERR_INVALID_ARG, "state overlaps an input or the workspace");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(workspace);
+  float* content = static_cast<float*>(state);
+  float* mass = content + (size_t)p.BH * p.LRP * p.D;
+  race::NCArgs a{};
+  a.X = K; a.Y = V; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.part = part; a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
+  {
+    ProfScope ps(s, "race_bucket_reduce");
+    p.ks->reduce(a, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bucket_reduce")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nchunk, p, content, mass, s);
+  }
+  return check_launch("race_bank_finalize");
+}
+
+race_status race_attn_decode(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
+                             void* O, const race_shape* shape, void* state, size_t state_bytes_in,
+                             race_stream_t stream) {
+  g_last_error.clear();
+  Plan p;
+  race_status st = decode_plan(shape, P, L, &p);
+  if (st != RACE_OK) return st;
+  if (!Q || !K || !V || !W || !O || !state) return fail(RACE_ERR_INVALID_ARG, "Q, K, V, W, O and state must be non-NULL");
+  if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(O) || !aligned16(state))
+    return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const size_t need_state = bank_bytes(p);
+  if (state_bytes_in < need_state)
+    return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
+  if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) || overlaps(O, tbytes, V, tbytes))
+    return fail(RACE_ERR_INVALID_ARG, "O overlaps an input");
+  if (overlaps(state, need_state, O, tbytes) || overlaps(state, need_state, Q, tbytes) ||
+      overlaps(state, need_state, K, tbytes) || overlaps(state, need_state, V, tbytes))
+    return fail(RACE_ERR_INVALID_ARG, "state overlaps a token buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  race::DArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.content = static_cast<float*>(state);
+  a.mass = a.content + (size_t)p.BH * p.LRP * p.D;
+  {
+    ProfScope ps(s, "race_decode");
+    p.ks->decode(a, (unsigned)p.BH, s);
+  }
+  return check_launch("race_decode");
 }
 
 race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L, const race_shape* shape,

@@ -1,0 +1,126 @@
+// Recurrent decode step: the causal RACE layer as a fixed-size recurrent
+// state (slides frame "Causality is a prefix update of the same statistics",
+// paper Algorithm 2; reading notes section 2.6).  The state of every
+// (batch, head) is its bucket bank after the tokens seen so far: content
+// [LRP][d] and mass [LRP], float32 (the same layout as the non-causal state).
+// For each new token t, in order: the key is added first, then the query
+// reads (the token sees itself):
+//   content += phi(K_t) V_t^T,  mass += phi(K_t)
+//   O_t = sum_l phi(Q_t) content / sum_l phi(Q_t) mass
+// One workgroup of 256 threads per (batch, head): thread (column c, row group
+// g) keeps bank rows [g * LRP / NG, (g + 1) * LRP / NG) of column c in
+// registers for all new tokens.  Projections, tanh, sigmoids and the soft
+// assignments are float32 and are not rounded.
+#pragma once
+#include "race_device.hpp"
+
+namespace race {
+
+struct DArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* content;   // [BH][LRP][d], updated in place
+  float* mass;      // [BH][LRP], updated in place
+  const float* W;
+  float beta;
+  int L, P;
+  int64_t N;        // new tokens per (batch, head)
+};
+
+template <typename T, class G>
+__global__ __launch_bounds__(256) void race_decode(DArgs a) {
+  constexpr int D = G::D, LRP = G::LRP;
+  constexpr int NG = 256 / D;              // row groups per column
+  constexpr int RPT = LRP / NG;            // bank rows per thread
+  static_assert(256 % D == 0 && LRP % NG == 0, "thread layout");
+  __shared__ float xs[3][D];               // q, k, v of the current token
+  __shared__ float pre[2][G::NHP];         // projections of q and k
+  __shared__ float ph[2][LRP];             // soft assignments of q and k
+  __shared__ float ms[LRP];                // mass
+  __shared__ float num[NG][D];             // partial numerators
+  __shared__ float red[256];
+
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int c = tid % D, g = tid / D;
+  float* content = a.content + (size_t)bh * LRP * D;
+  float* mass = a.mass + (size_t)bh * LRP;
+  const T* src[3] = {static_cast<const T*>(a.Q) + (size_t)bh * a.N * D,
+                     static_cast<const T*>(a.K) + (size_t)bh * a.N * D,
+                     static_cast<const T*>(a.V) + (size_t)bh * a.N * D};
+  T* out = static_cast<T*>(a.O) + (size_t)bh * a.N * D;
+
+  float bank[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) bank[i] = content[(size_t)(g * RPT + i) * D + c];
+  for (int lr = tid; lr < LRP; lr += 256) ms[lr] = mass[lr];
+  const float beta2 = 2.f * a.beta;
+
+  for (int64_t t = 0; t < a.N; ++t) {
+    for (int i = tid; i < 3 * D; i += 256) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];
+    __syncthreads();
+    // projections pre[role][hp] = W_hp . x (role 0: query, 1: key)
+    if (tid < 2 * G::NHP) {
+      const int role = tid / G::NHP, hp = tid % G::NHP;
+      const int l = hp / G::PE, tt = hp % G::PE;
+      float s = 0.f;
+      if (l < a.L && tt < a.P) {
+        const float* w = a.W + (size_t)(l * a.P + tt) * D;
+        for (int e = 0; e < D; ++e) s += w[e] * xs[role][e];
+      }
+      pre[role][hp] = s;
+    }
+    __syncthreads();
+    // soft assignments phi_r = prod_t sigma(2 beta u_t v_{r,t}), u = tanh(pre)
+    for (int j = tid; j < 2 * LRP; j += 256) {
+      const int role = j / LRP, lr = j % LRP;
+      const int l = lr / G::R, r = lr % G::R;
+      float p = 0.f;
+      if (l < a.L && l < G::LMAX) {
+        p = 1.f;
+        for (int tt = 0; tt < G::PE; ++tt) {
+          float sp, sm;
+          sigmoid_pair(beta2 * tanh_f(pre[role][l * G::PE + tt]), sp, sm);
+          p *= ((r >> tt) & 1) ? sp : sm;
+        }
+      }
+      ph[role][lr] = p;
+    }
+    __syncthreads();
+    // key first, then the query reads the updated bank
+    const float vc = xs[2][c];
+    float nacc = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int lr = g * RPT + i;
+      bank[i] += ph[1][lr] * vc;
+      nacc += ph[0][lr] * bank[i];
+    }
+    num[g][c] = nacc;
+    float dacc = 0.f;
+    for (int lr = tid; lr < LRP; lr += 256) {
+      ms[lr] += ph[1][lr];
+      dacc += ph[0][lr] * ms[lr];
+    }
+    red[tid] = dacc;
+    __syncthreads();
+    for (int m = 128; m > 0; m >>= 1) {
+      if (tid < m) red[tid] += red[tid + m];
+      __syncthreads();
+    }
+    if (g == 0) {
+      float nn = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) nn += num[gg][c];
+      out[t * D + c] = (T)(nn / red[0]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) content[(size_t)(g * RPT + i) * D + c] = bank[i];
+  for (int lr = tid; lr < LRP; lr += 256) mass[lr] = ms[lr];
+}
+
+}  // namespace race

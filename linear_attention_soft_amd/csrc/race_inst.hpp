@@ -4,6 +4,7 @@
 #include "race_noncausal.hpp"
 #include "race_registry.hpp"
 #include "race_walk.hpp"
+#include "race_decode.hpp"
 
 namespace race {
 
@@ -75,6 +76,9 @@ struct Inst {
     hipLaunchKernelGGL((race_h_from_o<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                        static_cast<const T*>(dO), static_cast<const T*>(O), den, h, total);
   }
+  static void decode(const DArgs& a, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((race_decode<T, G>), dim3(grid), dim3(256), 0, s, a);
+  }
   // nc: compile the non-causal kernels; causal: compile the causal ones
   template <bool NC, bool CAUSAL>
   static KernelSet set(int dtype) {
@@ -82,6 +86,7 @@ struct Inst {
     k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP;
     k.reduce = reduce;
     k.softbucket_dbg = dbg;
+    k.decode = decode;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
       k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;

@@ -8,6 +8,7 @@ namespace race {
 struct NCArgs;
 struct WArgs;
 struct TWArgs;
+struct DArgs;
 
 typedef void (*nc_launch_fn)(const NCArgs&, dim3 grid, hipStream_t);
 typedef void (*tw_launch_fn)(const TWArgs&, dim3 grid, hipStream_t);
@@ -26,6 +27,8 @@ struct KernelSet {
   w_launch_fn w_segsum, w_gsum, w_fwd, w_h, w_dv;
   tw_launch_fn tw_dq, tw_dk;
   void (*h_from_o)(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t);
+  // recurrent decode step (grid: BH)
+  void (*decode)(const DArgs&, unsigned grid, hipStream_t);
 };
 
 const KernelSet* kernel_sets_f32(int* count);

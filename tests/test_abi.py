@@ -122,3 +122,29 @@ def test_softbucket_debug_rejects_small_P():
     s = _shape()
     assert Lb.race_softbucket_debug(FAKE, FAKE + 0x1000000, ctypes.c_float(1.0), 2, 2, ctypes.byref(s),
                                     FAKE + 0x2000000, None) == 2
+
+
+def test_decode_rejects_bad_arguments():
+    Lb = _lib()
+    s = _shape()
+    base = [FAKE + i * 0x1000000 for i in range(8)]
+    nb = Lb.race_attn_decode_state_bytes(ctypes.byref(s), 3, 2)
+    assert nb > 0
+    assert Lb.race_attn_decode_state_bytes(ctypes.byref(_shape(d=96)), 3, 2) == 0
+
+    def call(q=base[0], state=base[5], sb=nb, beta=1.0, shape=s):
+        return Lb.race_attn_decode(q, base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, base[4],
+                                   ctypes.byref(shape), state, sb, None)
+
+    assert call(q=None) == 1
+    assert call(state=None) == 1
+    assert call(beta=math.inf) == 1
+    assert call(sb=16) == 3
+    assert call(q=base[0] + 4) == 1             # misaligned
+    assert call(shape=_shape(d=96)) == 2
+    wb = Lb.race_attn_decode_prefill_workspace_bytes(ctypes.byref(s), 3, 2)
+    assert wb > 0
+    assert Lb.race_attn_decode_prefill(base[1], base[2], base[3], ctypes.c_float(1.0), 3, 2, ctypes.byref(s),
+                                       base[5], nb, None, 0, None) == 3
+    assert Lb.race_attn_decode_prefill(base[1], base[2], base[3], ctypes.c_float(1.0), 3, 2, ctypes.byref(s),
+                                       base[5], 8, base[6], wb, None) == 3
