@@ -35,14 +35,16 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
   constexpr int NG = 256 / D;              // row groups per column
   constexpr int RPT = LRP / NG;            // bank rows per thread
   static_assert(256 % D == 0 && LRP % NG == 0, "thread layout");
+  constexpr int TPH = 4;                   // threads per projection dot product
+  static_assert(2 * G::NHP * TPH <= 256, "projection threads");
   __shared__ float xs[3][D];               // q, k, v of the current token
-  __shared__ float pre[2][G::NHP];         // projections of q and k
+  __shared__ float sg[2][2][G::NHP];       // sigma(+-2 beta u) per role and hyperplane
   __shared__ float ph[2][LRP];             // soft assignments of q and k
   __shared__ float ms[LRP];                // mass
   __shared__ float num[NG][D];             // partial numerators
-  __shared__ float red[256];
+  __shared__ float red[4];                 // per-wave partial denominators
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t bh = blockIdx.x;
   const int c = tid % D, g = tid / D;
   float* content = a.content + (size_t)bh * LRP * D;
@@ -57,34 +59,39 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
   for (int i = 0; i < RPT; ++i) bank[i] = content[(size_t)(g * RPT + i) * D + c];
   for (int lr = tid; lr < LRP; lr += 256) ms[lr] = mass[lr];
   const float beta2 = 2.f * a.beta;
+  // projection thread: (role, hyperplane, quarter of d)
+  const int prole = tid / (G::NHP * TPH), php = (tid / TPH) % G::NHP, pq = tid % TPH;
+  const int pl = php / G::PE, pt = php % G::PE;
+  const bool pok = tid < 2 * G::NHP * TPH && pl < a.L && pt < a.P;
+  const float* pw = a.W + (size_t)(pok ? pl * a.P + pt : 0) * D;
 
   for (int64_t t = 0; t < a.N; ++t) {
     for (int i = tid; i < 3 * D; i += 256) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];
     __syncthreads();
-    // projections pre[role][hp] = W_hp . x (role 0: query, 1: key)
-    if (tid < 2 * G::NHP) {
-      const int role = tid / G::NHP, hp = tid % G::NHP;
-      const int l = hp / G::PE, tt = hp % G::PE;
+    // projections: TPH consecutive lanes split d, then tanh and the sigmoid pair
+    if (tid < 2 * G::NHP * TPH) {
       float s = 0.f;
-      if (l < a.L && tt < a.P) {
-        const float* w = a.W + (size_t)(l * a.P + tt) * D;
-        for (int e = 0; e < D; ++e) s += w[e] * xs[role][e];
+      if (pok)
+        for (int e = pq; e < D; e += TPH) s += pw[e] * xs[prole][e];
+#pragma unroll
+      for (int m = TPH / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+      if (pq == 0) {
+        float sp, sm;
+        sigmoid_pair(beta2 * tanh_f(s), sp, sm);
+        sg[prole][0][php] = sp;
+        sg[prole][1][php] = sm;
       }
-      pre[role][hp] = s;
     }
     __syncthreads();
-    // soft assignments phi_r = prod_t sigma(2 beta u_t v_{r,t}), u = tanh(pre)
+    // soft assignments phi_r = prod_t sigma(2 beta u_t v_{r,t})
     for (int j = tid; j < 2 * LRP; j += 256) {
       const int role = j / LRP, lr = j % LRP;
       const int l = lr / G::R, r = lr % G::R;
       float p = 0.f;
       if (l < a.L && l < G::LMAX) {
         p = 1.f;
-        for (int tt = 0; tt < G::PE; ++tt) {
-          float sp, sm;
-          sigmoid_pair(beta2 * tanh_f(pre[role][l * G::PE + tt]), sp, sm);
-          p *= ((r >> tt) & 1) ? sp : sm;
-        }
+#pragma unroll
+        for (int tt = 0; tt < G::PE; ++tt) p *= sg[role][((r >> tt) & 1) ? 0 : 1][l * G::PE + tt];
       }
       ph[role][lr] = p;
     }
@@ -104,17 +111,14 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
       ms[lr] += ph[1][lr];
       dacc += ph[0][lr] * ms[lr];
     }
-    red[tid] = dacc;
+    dacc = wave_sum(dacc);
+    if (lane == 0) red[tid >> 6] = dacc;
     __syncthreads();
-    for (int m = 128; m > 0; m >>= 1) {
-      if (tid < m) red[tid] += red[tid + m];
-      __syncthreads();
-    }
     if (g == 0) {
       float nn = 0.f;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) nn += num[gg][c];
-      out[t * D + c] = (T)(nn / red[0]);
+      out[t * D + c] = (T)(nn / ((red[0] + red[1]) + (red[2] + red[3])));
     }
     __syncthreads();
   }
