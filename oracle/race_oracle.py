@@ -28,10 +28,13 @@ Conventions (readings where the pages are silent):
   in Num/Den exactly.  ``brute_force`` keeps it, as the implicit kernel is
   written with it.
 * No epsilon is added to the denominator; all features are positive.
-* W has shape (L, P, d) and is shared by every batch row and head.
+* W has shape (L, P, d) and is shared by every batch row and head; the
+  batched functions also take per-head tables (H, L, P, d).
 * The backward pass is the exact gradient of the forward map with W and beta
   held fixed; ``dbeta_head`` adds the gradient with respect to beta, the
-  inverse temperature the pages train (logits beta * u . v_r).
+  inverse temperature the pages train (logits beta * u . v_r), and
+  ``dW_head`` the gradient with respect to the tables, for tables that are
+  trained or differ per head.
 
 Everything is float64 numpy.  Arrays for one head are (N, d); batched
 arrays are (B, H, N, d).
@@ -269,10 +272,10 @@ def beta_terms(X, W, beta, Phi, dPhi):
     return np.sum(dLam * np.matmul(U, C.T), axis=(0, 2))
 
 
-def dbeta_head(Q, K, V, W, beta, dO, causal=False):
-    """dL/dbeta of L = sum(O * dO) for one head, as per-row terms of the
-    query side and of the key side: returns (terms_Q, terms_K), each (N,);
-    dbeta is their total.  The dPhi of each side are those of backward_head."""
+def _assignment_grads(Q, K, V, W, beta, dO, causal=False):
+    """Soft assignments of both sides and the gradients of sum(O * dO) with
+    respect to them, as backward_head forms them: returns
+    (Phi_Q, dPhi_Q, Phi_K, dPhi_K), each (L, N, R)."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -286,7 +289,6 @@ def dbeta_head(Q, K, V, W, beta, dO, causal=False):
         dcontent, dmass = grad_banks(Q, W, beta, g, h, Phi_Q)
         dPhi_K = np.matmul(V[None], dcontent.transpose(0, 2, 1)) + dmass[:, None, :]
     else:
-        L, N, R = Phi_Q.shape
         O, Den = causal_forward_head(Q, K, V, W, beta, return_den=True)
         g = dO / Den[:, None]
         h = -np.sum(dO * O, axis=1) / Den
@@ -297,15 +299,71 @@ def dbeta_head(Q, K, V, W, beta, dO, causal=False):
         sD = np.cumsum((Phi_Q[:, :, :, None] * g[None, :, None, :])[:, ::-1], axis=1)[:, ::-1]
         sE = np.cumsum((Phi_Q * h[None, :, None])[:, ::-1], axis=1)[:, ::-1]
         dPhi_K = np.einsum("nc,lnrc->lnr", V, sD) + sE
+    return Phi_Q, dPhi_Q, Phi_K, dPhi_K
+
+
+def dbeta_head(Q, K, V, W, beta, dO, causal=False):
+    """dL/dbeta of L = sum(O * dO) for one head, as per-row terms of the
+    query side and of the key side: returns (terms_Q, terms_K), each (N,);
+    dbeta is their total.  The dPhi of each side are those of backward_head."""
+    Phi_Q, dPhi_Q, Phi_K, dPhi_K = _assignment_grads(Q, K, V, W, beta, dO, causal)
     return beta_terms(Q, W, beta, Phi_Q, dPhi_Q), beta_terms(K, W, beta, Phi_K, dPhi_K)
 
 
+def weight_terms(X, W, beta, Phi, dPhi):
+    """Contribution of the rows X to dL/dW through their soft assignments.
+
+    The pre-activations are W^(l) x (slides, frame "Soft corner assignments
+    make hashing differentiable"), so with dPre = beta dLambda C * (1 - U^2)
+    (the chain _assign_backward follows) the rows contribute
+    dW^(l) = dPre^(l)^T X.  Returns an (L, P, d) array.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    U = _projected(X, W)                                   # (L, N, P)
+    C = corners(W.shape[1])
+    dLam = Phi * (dPhi - np.sum(Phi * dPhi, axis=-1, keepdims=True))
+    dPre = float(beta) * np.matmul(dLam, C) * (1.0 - U * U)
+    return np.matmul(dPre.transpose(0, 2, 1), X)
+
+
+def dW_head(Q, K, V, W, beta, dO, causal=False):
+    """dL/dW of L = sum(O * dO) for one head whose tables are W (L, P, d):
+    returns the query-side and key-side parts (dW_Q, dW_K), each (L, P, d);
+    dW is their sum (W enters both projections)."""
+    Phi_Q, dPhi_Q, Phi_K, dPhi_K = _assignment_grads(Q, K, V, W, beta, dO, causal)
+    return weight_terms(Q, W, beta, Phi_Q, dPhi_Q), weight_terms(K, W, beta, Phi_K, dPhi_K)
+
+
+def head_tables(W, hh):
+    """Tables of head hh: W is (L, P, d), shared by every head, or
+    (H, L, P, d), one set of tables per head."""
+    W = np.asarray(W)
+    return W[hh] if W.ndim == 4 else W
+
+
+def dW(Q, K, V, W, beta, dO, causal=False):
+    """Batched dL/dW over (B, H, N, d) arrays.  Shared tables (L, P, d) sum
+    the contributions of every batch row and head; per-head tables
+    (H, L, P, d) sum those of every batch row for each head."""
+    W = np.asarray(W)
+    out = np.zeros(W.shape, dtype=np.float64)
+    for b in range(np.asarray(Q).shape[0]):
+        for hh in range(np.asarray(Q).shape[1]):
+            wq, wk = dW_head(Q[b, hh], K[b, hh], V[b, hh], head_tables(W, hh), beta, dO[b, hh], causal)
+            if W.ndim == 4:
+                out[hh] += wq + wk
+            else:
+                out += wq + wk
+    return out
+
+
 def dbeta(Q, K, V, W, beta, dO, causal=False):
-    """Batched dL/dbeta over (B, H, N, d) arrays (one beta for every head)."""
+    """Batched dL/dbeta over (B, H, N, d) arrays (one beta for every head;
+    W shared (L, P, d) or per head (H, L, P, d))."""
     tot = 0.0
     for b in range(np.asarray(Q).shape[0]):
         for hh in range(np.asarray(Q).shape[1]):
-            tq, tk = dbeta_head(Q[b, hh], K[b, hh], V[b, hh], W, beta, dO[b, hh], causal)
+            tq, tk = dbeta_head(Q[b, hh], K[b, hh], V[b, hh], head_tables(W, hh), beta, dO[b, hh], causal)
             tot += float(tq.sum() + tk.sum())
     return tot
 
@@ -409,20 +467,23 @@ def backward_head(Q, K, V, W, beta, dO, causal=False, content0=None, mass0=None)
 
 
 def forward(Q, K, V, W, beta, causal=False):
-    """Batched forward over (B, H, N, d) arrays; returns float64 O."""
+    """Batched forward over (B, H, N, d) arrays; returns float64 O.  W is
+    (L, P, d), shared by every head, or (H, L, P, d), per head."""
     Q = np.asarray(Q)
     out = np.empty(Q.shape, dtype=np.float64)
     for b in range(Q.shape[0]):
         for hh in range(Q.shape[1]):
+            Wh = head_tables(W, hh)
             if causal:
-                out[b, hh] = causal_forward_head(Q[b, hh], K[b, hh], V[b, hh], W, beta)
+                out[b, hh] = causal_forward_head(Q[b, hh], K[b, hh], V[b, hh], Wh, beta)
             else:
-                out[b, hh] = forward_head(Q[b, hh], K[b, hh], V[b, hh], W, beta)
+                out[b, hh] = forward_head(Q[b, hh], K[b, hh], V[b, hh], Wh, beta)
     return out
 
 
 def backward(Q, K, V, W, beta, dO, causal=False):
-    """Batched backward over (B, H, N, d) arrays; returns float64 (dQ, dK, dV)."""
+    """Batched backward over (B, H, N, d) arrays; returns float64 (dQ, dK, dV).
+    W as in forward."""
     Q = np.asarray(Q)
     dQ = np.empty(Q.shape, dtype=np.float64)
     dK = np.empty(Q.shape, dtype=np.float64)
@@ -430,5 +491,5 @@ def backward(Q, K, V, W, beta, dO, causal=False):
     for b in range(Q.shape[0]):
         for hh in range(Q.shape[1]):
             dQ[b, hh], dK[b, hh], dV[b, hh] = backward_head(
-                Q[b, hh], K[b, hh], V[b, hh], W, beta, dO[b, hh], causal)
+                Q[b, hh], K[b, hh], V[b, hh], head_tables(W, hh), beta, dO[b, hh], causal)
     return dQ, dK, dV

@@ -494,3 +494,76 @@ def test_dbeta_invariants(causal):
     assert abs((tq2.sum() + tk2.sum()) - (tq.sum() + tk.sum())) < 1e-10 * scale
     tqc, tkc = orc.dbeta_head(Q, K, np.tile(c, (N, 1)), W, beta, dO, causal)
     assert abs(tqc.sum() + tkc.sum()) < 1e-11 * scale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dW_finite_differences(causal):
+    """dL/dW (query-side plus key-side parts) equals the central finite
+    difference of sum(O * dO) in every entry of the tables (the
+    pre-activations are W^(l) x; slides, frame "Soft corner assignments make
+    hashing differentiable")."""
+    rng = np.random.default_rng(80 + causal)
+    N, d, L, P, beta = 9, 5, 2, 3, 1.5
+    Q, K, V, W = _rand_head(rng, N, d, L, P)
+    dO = rng.standard_normal((N, d))
+    wq, wk = orc.dW_head(Q, K, V, W, beta, dO, causal)
+    got = wq + wk
+    eps = 1e-6
+    num = np.empty_like(W)
+    for idx in np.ndindex(*W.shape):
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += eps
+        Wm[idx] -= eps
+        num[idx] = (_loss(Q, K, V, Wp, beta, dO, causal) - _loss(Q, K, V, Wm, beta, dO, causal)) / (2 * eps)
+    scale = max(1.0, np.abs(got).max())
+    assert np.abs(got - num).max() <= 1e-7 * scale, (causal, np.abs(got - num).max())
+    # the batched wrapper adds the same parts
+    np.testing.assert_allclose(orc.dW(Q[None, None], K[None, None], V[None, None], W, beta, dO[None, None], causal),
+                               got, rtol=0, atol=1e-12 * scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dW_scaling_identity(causal):
+    """Scaling the rows of one side by s and its projection by 1/s leaves
+    every pre-activation W^(l) x unchanged, so per side
+    <dW_side, W> = <dX, X> with dX the finite-difference-pinned input
+    gradient (Q side: dQ, K side: dK)."""
+    rng = np.random.default_rng(90 + causal)
+    N, d, L, P, beta = 150, 6, 3, 3, 2.5
+    Q, K, V, W = _rand_head(rng, N, d, L, P)
+    dO = rng.standard_normal((N, d))
+    wq, wk = orc.dW_head(Q, K, V, W, beta, dO, causal)
+    dQ, dK, _ = orc.backward_head(Q, K, V, W, beta, dO, causal)
+    for part, dX, X in ((wq, dQ, Q), (wk, dK, K)):
+        lhs, rhs = float(np.sum(part * W)), float(np.sum(dX * X))
+        assert abs(lhs - rhs) <= 1e-10 * max(1.0, float(np.sum(np.abs(dX * X)))), (causal, lhs, rhs)
+
+
+def test_dW_zero_beta_and_per_head_tables():
+    """beta = 0 makes every assignment uniform whatever W is, so dW = 0.
+    Per-head tables that are all equal give per-head gradients whose sum over
+    heads is the shared-table gradient; a finite difference in one head's
+    table moves only that head's loss."""
+    rng = np.random.default_rng(95)
+    B, H, N, d, L, P = 2, 3, 40, 6, 2, 3
+    Q = rng.standard_normal((B, H, N, d))
+    K = rng.standard_normal((B, H, N, d))
+    V = rng.standard_normal((B, H, N, d))
+    dO = rng.standard_normal((B, H, N, d))
+    W = rng.standard_normal((L, P, d))
+    for causal in (False, True):
+        assert np.abs(orc.dW(Q, K, V, W, 0.0, dO, causal)).max() == 0.0
+        shared = orc.dW(Q, K, V, W, 1.7, dO, causal)
+        per_head = orc.dW(Q, K, V, np.stack([W] * H), 1.7, dO, causal)
+        np.testing.assert_allclose(per_head.sum(axis=0), shared, rtol=0, atol=1e-12 * np.abs(shared).max())
+    W4 = rng.standard_normal((H, L, P, d))
+    for causal in (False, True):
+        g = orc.dW(Q, K, V, W4, 1.7, dO, causal)
+        eps = 1e-6
+        for idx in [(0, 0, 1, 2), (2, 1, 0, 5), (1, 1, 2, 0)]:
+            Wp, Wm = W4.copy(), W4.copy()
+            Wp[idx] += eps
+            Wm[idx] -= eps
+            num = (np.sum(orc.forward(Q, K, V, Wp, 1.7, causal) * dO)
+                   - np.sum(orc.forward(Q, K, V, Wm, 1.7, causal) * dO)) / (2 * eps)
+            assert abs(g[idx] - num) <= 1e-7 * max(1.0, np.abs(g).max()), (causal, idx, g[idx], num)
