@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dbeta", action="store_true",
                     help="also compute dL/dbeta in every backward (beta learned)")
+    ap.add_argument("--dW", action="store_true",
+                    help="also compute dL/dW in every backward (tables learned)")
+    ap.add_argument("--per-head", action="store_true",
+                    help="one set of tables per head (W is [H][L][P][d])")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 22)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 1 GiB once (reference kernel for rocprofv3 byte counters)")
@@ -194,20 +198,22 @@ def main():
     print(f"# workload {w.name}: generating inputs on the GPU", file=sys.stderr, flush=True)
     inp = ri.make_inputs(w, device=dev, with_grad_out=True)
     Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
-    W = inp["W"].to(dev)
+    W = (ri.make_W_per_head(w) if args.per_head else inp["W"]).to(dev)
     O = torch.empty_like(Q)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
-    shape = race._shape_of(Q)
+    shape = race._shape_of(Q, W, w.L, w.P)
     st = torch.empty(race.race_attn_state_bytes(shape, w.P, w.L, w.causal), dtype=torch.uint8, device=dev)
     wsf = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, False), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, True), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, 2 if args.dW else 1),
+                      dtype=torch.uint8, device=dev)
     db = torch.zeros(1, dtype=torch.float32, device=dev)
+    dW = torch.zeros_like(W) if args.dW else None
     torch.cuda.synchronize()
 
     def step():
         race.race_attn_fwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, O=O, state=st, workspace=wsf)
         race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV,
-                           dbeta=db if args.dbeta else None, workspace=wsb)
+                           dbeta=db if args.dbeta else None, dW=dW, workspace=wsb)
 
     for _ in range(args.warmup):
         step()
@@ -267,7 +273,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; iid N(0,1) Q, K, V, dO; Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "L": w.L,
-                   "beta": w.beta, "causal": w.causal, "dbeta": bool(args.dbeta), "global_batch": w.B,
+                   "beta": w.beta, "causal": w.causal, "dbeta": bool(args.dbeta), "dW": bool(args.dW),
+                   "per_head_tables": bool(args.per_head), "global_batch": w.B,
                    "seq_len": w.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -276,6 +283,15 @@ def main():
         "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items()},
         "cpu_baseline": cpu,
     }
+    if args.dW and "race_dw_partial" in kern:
+        # the table-gradient stream: both sides' rows plus their float32 dPre
+        pe = max(w.P, 3)
+        lrp = -(-(w.L << pe) // 32) * 32
+        nhp = (lrp >> pe) * pe
+        dpre_bytes = 2 * w.B * w.H * w.N * nhp * 4
+        c, ms = kern["race_dw_partial"]
+        out["dw_partial"] = {"avg_launch_ms": ms / c, "alg_bytes_per_launch": 2 * row_bytes + dpre_bytes,
+                             "achieved_GBps": (2 * row_bytes + dpre_bytes) / (ms / c * 1e-3) / 1e9}
     print(json.dumps(out), flush=True)
 
 

@@ -22,7 +22,9 @@
  *    [B][H][N][d] arrays of the I/O dtype (RACE_F32 or RACE_BF16), 16-byte
  *    aligned.  Outputs must not overlap inputs.
  *  - W is a device pointer to float32 [L][P][d] (table l, hyperplane t,
- *    column c at (l*P + t)*d + c), shared by every batch row and head.
+ *    column c at (l*P + t)*d + c), shared by every batch row and head; with
+ *    shape->w_per_head = 1 it is [H][L][P][d], one set of tables per head
+ *    (head h of every batch row uses the tables at h*L*P*d).
  *  - beta is a host float; any finite value is accepted.
  *  - stream is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns; device-side faults surface at the
@@ -61,6 +63,7 @@ typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype;
 typedef struct {
   int64_t B, H, N, d;
   int32_t dtype;              /* race_dtype */
+  int32_t w_per_head;         /* 0: W is [L][P][d] for every head; 1: [H][L][P][d] */
 } race_shape;
 
 /* Bytes of the state buffer the forward pass fills and the backward pass
@@ -72,8 +75,11 @@ typedef struct {
  * Returns 0 for invalid arguments. */
 size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal);
 
-/* Bytes of scratch workspace for the forward (is_bwd = 0) or backward
- * (is_bwd = 1) call.  Returns 0 for invalid arguments. */
+/* Bytes of scratch workspace for the forward (is_bwd = 0), the backward
+ * (is_bwd = 1) or the backward with the table gradient dW (is_bwd = 2:
+ * adds float32 dL/dPre of every token of both sides, 2 * B*H*N *
+ * (LRP / 2^max(P,3)) * max(P,3) floats, and one partial per workgroup).
+ * Returns 0 for invalid arguments. */
 size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd);
 
 /* Forward pass: O = RACE(Q, K, V; W, beta, P, L, causal).
@@ -95,11 +101,17 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
  * the forward output or NULL: the non-causal backward never reads it; the
  * causal backward takes h = -(dO . O) / Den from it elementwise when given,
  * and rebuilds Den O with one more walk over Q, K, V when it is NULL.
- * workspace must hold race_attn_workspace_bytes(..., 1). */
+ * When dW (a device pointer, 4-byte aligned, W's layout: [L][P][d] or
+ * [H][L][P][d]) is not NULL it receives dL/dW: the pre-activations of a
+ * row x are W^(l) x (same frame), so each table's gradient is the sum over
+ * the query and key rows of dL/dPre^(l) x^T, over every batch row and head
+ * that uses the table; summed in a fixed order (same bits on every run).
+ * workspace must hold race_attn_workspace_bytes(..., 1), or (..., 2) when
+ * dW is requested; dW must not overlap W or any other buffer. */
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W,
                           float beta, int P, int L, int causal, const void* O,
                           const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
-                          const race_shape* shape, const void* state, size_t state_bytes,
+                          float* dW, const race_shape* shape, const void* state, size_t state_bytes,
                           void* workspace, size_t workspace_bytes, race_stream_t stream);
 
 /* Recurrent decode (slides, frame "Causality is a prefix update of the same

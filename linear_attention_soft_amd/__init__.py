@@ -37,7 +37,7 @@ class RaceError(RuntimeError):
 
 class race_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64), ("d", ctypes.c_int64),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("w_per_head", ctypes.c_int32)]
 
 
 _LIB = None
@@ -59,7 +59,8 @@ def lib() -> ctypes.CDLL:
         L.race_attn_workspace_bytes.restype = sz
         L.race_attn_fwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, sp, vp, sz, vp, sz, vp]
         L.race_attn_fwd.restype = i32
-        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sp, vp, sz, vp, sz, vp]
+        L.race_attn_bwd.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sp, vp, sz, vp, sz,
+                                    vp]
         L.race_attn_bwd.restype = i32
         L.race_softbucket_debug.argtypes = [vp, vp, f32, i32, i32, sp, vp, vp]
         L.race_softbucket_debug.restype = i32
@@ -99,16 +100,29 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def make_shape(B, H, N, d, dtype) -> race_shape:
+def make_shape(B, H, N, d, dtype, w_per_head=False) -> race_shape:
     code = dtype if isinstance(dtype, int) else (RACE_BF16 if dtype == torch.bfloat16 else RACE_F32)
-    return race_shape(int(B), int(H), int(N), int(d), code)
+    return race_shape(int(B), int(H), int(N), int(d), code, int(bool(w_per_head)))
 
 
-def _shape_of(x: torch.Tensor) -> race_shape:
+def _shape_of(x: torch.Tensor, W: torch.Tensor = None, L: int = None, P: int = None) -> race_shape:
+    """Shape record of the token tensor x; W of shape [L, P, d] is shared by
+    every head, W of shape [H, L, P, d] holds one set of tables per head."""
     if x.dim() != 4:
         raise ValueError("tensors must be [B, H, N, d]")
     B, H, N, d = x.shape
-    return race_shape(B, H, N, d, _dtype_code(x))
+    per_head = 0
+    if W is not None:
+        if W.dim() == 4:
+            per_head = 1
+            if W.shape[0] != H:
+                raise ValueError(f"per-head tables must be [H, L, P, d] with H = {H}")
+        elif W.dim() != 3:
+            raise ValueError("W must be [L, P, d] or [H, L, P, d]")
+        if W.dtype != torch.float32 or W.shape[-1] != d or (L is not None and W.shape[-3] != L) or \
+                (P is not None and W.shape[-2] != P):
+            raise ValueError(f"W must be float32 [.., L={L}, P={P}, d={d}]")
+    return race_shape(B, H, N, d, _dtype_code(x), per_head)
 
 
 def _dev(t: torch.Tensor, name: str) -> int:
@@ -129,7 +143,8 @@ def race_attn_state_bytes(shape: race_shape, P: int, L: int, causal: bool) -> in
     return int(lib().race_attn_state_bytes(ctypes.byref(shape), P, L, int(causal)))
 
 
-def race_attn_workspace_bytes(shape: race_shape, P: int, L: int, causal: bool, is_bwd: bool) -> int:
+def race_attn_workspace_bytes(shape: race_shape, P: int, L: int, causal: bool, is_bwd) -> int:
+    """is_bwd: 0 / False forward, 1 / True backward, 2 backward with dW."""
     return int(lib().race_attn_workspace_bytes(ctypes.byref(shape), P, L, int(causal), int(is_bwd)))
 
 
@@ -144,8 +159,9 @@ def _buffer(nbytes: int, device, given=None):
 
 
 def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, workspace=None, stream=None):
-    """O = RACE(Q, K, V; W, beta, P, L, causal).  Returns (O, state)."""
-    shape = _shape_of(Q)
+    """O = RACE(Q, K, V; W, beta, P, L, causal).  Returns (O, state).  W is
+    [L, P, d] (every head) or [H, L, P, d] (per head)."""
+    shape = _shape_of(Q, W, L, P)
     if O is None:
         O = torch.empty_like(Q)
     sb = race_attn_state_bytes(shape, P, L, causal)
@@ -163,11 +179,13 @@ def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, work
 
 
 def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK=None, dV=None,
-                  dbeta=None, workspace=None, stream=None):
-    """Exact gradients of sum(O * dO).  Returns (dQ, dK, dV), or (dQ, dK, dV,
-    dbeta) when dbeta is True (a new float32 tensor of one element) or a
-    float32 device tensor to write dL/dbeta into."""
-    shape = _shape_of(Q)
+                  dbeta=None, dW=None, workspace=None, stream=None):
+    """Exact gradients of sum(O * dO).  Returns (dQ, dK, dV), followed by
+    dbeta when dbeta is True (a new float32 tensor of one element) or a
+    float32 device tensor to write dL/dbeta into, then by dW when dW is True
+    (a new float32 tensor shaped like W) or a float32 device tensor of W's
+    shape to write dL/dW into."""
+    shape = _shape_of(Q, W, L, P)
     dQ = torch.empty_like(Q) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
     dV = torch.empty_like(V) if dV is None else dV
@@ -176,18 +194,24 @@ def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK
         dbeta = torch.zeros(1, dtype=torch.float32, device=Q.device)
     if want_dbeta and (dbeta.dtype != torch.float32 or not dbeta.is_cuda or dbeta.numel() < 1):
         raise ValueError("dbeta must be a float32 device tensor with at least one element")
-    wb = race_attn_workspace_bytes(shape, P, L, causal, True)
+    want_dW = dW is not None and dW is not False
+    if dW is True:
+        dW = torch.empty_like(W)
+    if want_dW and (dW.dtype != torch.float32 or not dW.is_cuda or dW.shape != W.shape):
+        raise ValueError("dW must be a float32 device tensor shaped like W")
+    wb = race_attn_workspace_bytes(shape, P, L, causal, 2 if want_dW else 1)
     if wb == 0:
         _check(lib().race_attn_bwd(None, None, None, None, float(beta), P, L, int(causal), None, None, None, None,
-                                   None, None, ctypes.byref(shape), None, 0, None, 0, None))
+                                   None, None, None, ctypes.byref(shape), None, 0, None, 0, None))
     workspace = _buffer(wb, Q.device, workspace)
     _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
                                int(L), int(causal), O.data_ptr() if O is not None else None, _dev(dO, "dO"),
                                _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
-                               dbeta.data_ptr() if want_dbeta else None, ctypes.byref(shape),
+                               dbeta.data_ptr() if want_dbeta else None,
+                               _dev(dW, "dW") if want_dW else None, ctypes.byref(shape),
                                _dev(state, "state"), _bytes(state), _dev(workspace, "workspace"),
                                _bytes(workspace), _stream(stream)))
-    return (dQ, dK, dV, dbeta) if want_dbeta else (dQ, dK, dV)
+    return (dQ, dK, dV) + ((dbeta,) if want_dbeta else ()) + ((dW,) if want_dW else ())
 
 
 def profile_enable(on: bool = True):
@@ -216,7 +240,7 @@ def race_softbucket_debug(X, W, beta, P, L, stream=None):
     """Soft assignments phi^(l)(X) as float32 [B, H, N, L, 2^P] (test export)."""
     B, H, N, d = X.shape
     out = torch.empty((B, H, N, L, 1 << P), dtype=torch.float32, device=X.device)
-    shape = _shape_of(X)
+    shape = _shape_of(X, W, L, P)
     _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
                                        ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
     return out
@@ -229,7 +253,7 @@ def race_attn_decode_state_bytes(shape: race_shape, P: int, L: int) -> int:
 def race_attn_decode_prefill(K, V, W, beta, P, L, state=None, workspace=None, stream=None):
     """Decode state (float32 bank: content [B*H][LRP][d] then mass [B*H][LRP])
     after the prompt K, V [B, H, N, d].  Returns the state tensor."""
-    shape = _shape_of(K)
+    shape = _shape_of(K, W, L, P)
     nb = race_attn_decode_state_bytes(shape, P, L)
     if nb == 0:
         _check(lib().race_attn_decode_prefill(None, None, None, float(beta), int(P), int(L), ctypes.byref(shape),
@@ -247,7 +271,7 @@ def race_attn_decode_prefill(K, V, W, beta, P, L, state=None, workspace=None, st
 def race_attn_decode(Q, K, V, W, beta, P, L, state, O=None, stream=None):
     """Decode the new tokens Q, K, V [B, H, n, d] in order from state (updated
     in place; a zeroed state is the empty prefix).  Returns O."""
-    shape = _shape_of(Q)
+    shape = _shape_of(Q, W, L, P)
     O = torch.empty_like(Q) if O is None else O
     _check(lib().race_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
                                   int(L), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"), _bytes(state),

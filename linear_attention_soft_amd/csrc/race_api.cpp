@@ -18,6 +18,7 @@
 #include "race_registry.hpp"
 #include "race_walk.hpp"
 #include "race_decode.hpp"
+#include "race_dw.hpp"
 
 namespace race {
 // ------------------------------------------------------------------ fixed-order chunk sums
@@ -93,6 +94,7 @@ struct Plan {
   int64_t B = 0, H = 0, N = 0, D = 0, BH = 0;
   int P = 0, L = 0, PE = 0, LR = 0, LRP = 0;
   bool causal = false;
+  bool w_per_head = false;   // W is [H][L][P][d] instead of [L][P][d]
   // non-causal chunking
   int nchunk = 0;
   int64_t chunk_tokens = 0;
@@ -149,6 +151,7 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
   if (s->B < 1 || s->H < 1 || s->N < 1 || s->d < 1)
     return fail(RACE_ERR_INVALID_ARG, "B, H, N and d must be >= 1");
   if (s->dtype != RACE_F32 && s->dtype != RACE_BF16) return fail(RACE_ERR_INVALID_ARG, "dtype must be RACE_F32 or RACE_BF16");
+  if (s->w_per_head != 0 && s->w_per_head != 1) return fail(RACE_ERR_INVALID_ARG, "w_per_head must be 0 or 1");
   if (P < 1 || P > 8) return fail(RACE_ERR_INVALID_ARG, "P must be in [1, 8]");
   if (L < 1) return fail(RACE_ERR_INVALID_ARG, "L must be >= 1");
   if (causal != 0 && causal != 1) return fail(RACE_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -162,6 +165,7 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
   p->LR = L << p->PE;
   p->LRP = (p->LR + 31) / 32 * 32;
   p->causal = causal != 0;
+  p->w_per_head = s->w_per_head != 0;
   if (p->D != 64 && p->D != 128) return fail(RACE_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
   if (need_kernels) {
     p->ks = find_set(p->dtype, (int)p->D, p->PE, p->LRP, p->causal);
@@ -213,7 +217,18 @@ CausalBwdWs causal_bwd_ws(const Plan& p) {
   return w;
 }
 
-size_t workspace_bytes(const Plan& p, bool bwd) {
+// Table gradient: dPre of both sides [2][BH][N][NHP] and the partials
+// [2][BH][nchunk][NHP][d] of race_dw_partial.
+int nhp(const Plan& p) { return p.ks ? p.ks->NHP : 0; }
+size_t dpre_side_bytes(const Plan& p) { return align256((size_t)p.BH * p.N * nhp(p) * sizeof(float)); }
+size_t dw_part_bytes(const Plan& p) {
+  return align256(2 * (size_t)p.BH * p.nchunk * nhp(p) * p.D * sizeof(float));
+}
+size_t dw_bytes(const Plan& p) { return 2 * dpre_side_bytes(p) + dw_part_bytes(p); }
+size_t dw_out_floats(const Plan& p) { return (size_t)(p.w_per_head ? p.H : 1) * p.L * p.P * p.D; }
+
+size_t workspace_bytes(const Plan& p, bool bwd, bool dw = false) {
+  if (bwd && dw) return workspace_bytes(p, true, false) + dw_bytes(p);
   if (!p.causal) {
     size_t w = align256(part_bytes(p));
     if (!bwd) w += align256(bank_bytes(p));          // bank when no state buffer is given
@@ -250,14 +265,46 @@ void launch_finalize(const float* part, int nchunk, const Plan& p, float* conten
 
 
 // ---- causal sequences
+race::Tables tables(const Plan& p, const float* W) {
+  race::Tables t;
+  t.W = W;
+  t.hstride = p.w_per_head ? (int64_t)p.L * p.P * p.D : 0;
+  t.H = (int)p.H;
+  return t;
+}
+
 race::WArgs walk_args(const Plan& p, const float* W, float beta) {
   race::WArgs w{};
-  w.W = W; w.beta = beta; w.L = p.L; w.P = p.P; w.N = p.N; w.seg_tokens = p.seg_tokens; w.nseg = p.nseg;
+  w.W = tables(p, W); w.beta = beta; w.L = p.L; w.P = p.P; w.N = p.N; w.seg_tokens = p.seg_tokens; w.nseg = p.nseg;
   return w;
 }
 
 void launch_dbeta_finalize(const Plan& p, const float* parts, float* dbeta, hipStream_t s) {
   hipLaunchKernelGGL(race::race_dbeta_finalize, dim3(1), dim3(256), 0, s, parts, 2 * dbeta_parts_per_side(p), dbeta);
+}
+
+// dW from the dPre rows the backward kernels wrote into the workspace's
+// table-gradient region (query side, key side, partials).
+race_status launch_dw(const Plan& p, const void* Q, const void* K, float* dW, char* region, hipStream_t s) {
+  race_status st;
+  race::DWArgs a{};
+  a.X0 = Q; a.X1 = K;
+  a.dpre0 = reinterpret_cast<const float*>(region);
+  a.dpre1 = reinterpret_cast<const float*>(region + dpre_side_bytes(p));
+  a.part = reinterpret_cast<float*>(region + 2 * dpre_side_bytes(p));
+  a.N = p.N; a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
+  {
+    ProfScope ps(s, "race_dw_partial");
+    p.ks->dw_partial(a, dim3((unsigned)p.nchunk, (unsigned)p.BH, 2), s);
+  }
+  if ((st = check_launch("race_dw_partial")) != RACE_OK) return st;
+  const unsigned rows = (unsigned)((p.w_per_head ? p.H : 1) * p.L * p.P);
+  {
+    ProfScope ps(s, "race_dw_finalize");
+    hipLaunchKernelGGL(race::race_dw_finalize, dim3(rows), dim3(1024), 0, s, a.part, (int)p.B, (int)p.H,
+                       p.w_per_head ? 1 : 0, p.nchunk, nhp(p), p.PE, p.L, p.P, (int)p.D, dW);
+  }
+  return check_launch("race_dw_finalize");
 }
 
 void launch_seg_scan(const Plan& p, const float* part, float* out, int reverse, hipStream_t s) {
@@ -298,7 +345,7 @@ race_status causal_forward(const Plan& p, const void* Q, const void* K, const vo
 
 race_status causal_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
                             const void* O, const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
-                            const void* state, char* ws, hipStream_t s) {
+                            float* dW, const void* state, char* ws, hipStream_t s) {
   race_status st;
   const float* prefix = static_cast<const float*>(state);
   const float* den = reinterpret_cast<const float*>(static_cast<const char*>(state) + align256(seg_bank_bytes(p)));
@@ -340,10 +387,12 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   if ((st = check_launch("race_causal_dv")) != RACE_OK) return st;
   // 4. dQ: forward transposed walk (dPhi_Q, softmax / tanh / projection backward)
   race::TWArgs t{};
-  t.W = W; t.beta = beta; t.L = p.L; t.P = p.P; t.N = p.N; t.seg_tokens = p.seg_tokens; t.nseg = p.nseg;
+  t.W = tables(p, W); t.beta = beta; t.L = p.L; t.P = p.P; t.N = p.N; t.seg_tokens = p.seg_tokens; t.nseg = p.nseg;
   t.den = den; t.hvec = h;
   float* bparts = dbeta ? reinterpret_cast<float*>(ws + L.dbeta) : nullptr;
+  char* dwr = dW ? ws + L.total : nullptr;
   t.A_src = Q; t.B_src = K; t.X_src = V; t.U_src = dO; t.bank_in = prefix; t.dX = dQ; t.dbeta_part = bparts;
+  t.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
   {
     ProfScope ps(s, "race_causal_dq");
     p.ks->tw_dq(t, grid, s);
@@ -352,6 +401,7 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   // 5. dK: reverse transposed walk (dPhi_K) from the gradient suffix banks
   t.A_src = K; t.B_src = Q; t.X_src = dO; t.U_src = V; t.bank_in = gsuf; t.dX = dK;
   t.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
+  t.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
   {
     ProfScope ps(s, "race_causal_dk");
     p.ks->tw_dk(t, grid, s);
@@ -361,7 +411,8 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
     ProfScope ps(s, "race_dbeta_finalize");
     launch_dbeta_finalize(p, bparts, dbeta, s);
   }
-  return check_launch("race_dbeta_finalize");
+  if ((st = check_launch("race_dbeta_finalize")) != RACE_OK) return st;
+  return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
 }
 
 }  // namespace
@@ -378,10 +429,12 @@ size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal) 
 
 size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd) {
   Plan p;
+  if (is_bwd < 0 || is_bwd > 2) return 0;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
   const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
   if (ks) p.LRP = ks->LRP;
-  return workspace_bytes(p, is_bwd != 0);
+  p.ks = ks;
+  return workspace_bytes(p, is_bwd != 0, is_bwd == 2);
 }
 
 race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
@@ -418,7 +471,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
   float* mass = bank + (size_t)p.BH * p.LRP * p.D;
 
   race::NCArgs a{};
-  a.X = K; a.Y = V; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.part = part;
   {
     ProfScope ps(s, "race_bucket_reduce");
@@ -431,7 +484,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
   }
   if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
   race::NCArgs r{};
-  r.X = Q; r.out0 = O; r.W = W; r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
+  r.X = Q; r.out0 = O; r.W = tables(p, W); r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
   r.st_content = content; r.st_mass = mass; r.chunk_tokens = p.chunk_tokens; r.nchunk = p.nchunk;
   {
     ProfScope ps(s, "race_readout_norm");
@@ -442,7 +495,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
 
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
                           int causal, const void* O, const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
-                          const race_shape* shape, const void* state, size_t state_bytes_in, void* workspace,
+                          float* dW, const race_shape* shape, const void* state, size_t state_bytes_in, void* workspace,
                           size_t workspace_bytes_in, race_stream_t stream) {
   g_last_error.clear();
   Plan p;
@@ -457,6 +510,8 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
       (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   if (dbeta && ((uintptr_t)dbeta & 3u)) return fail(RACE_ERR_INVALID_ARG, "dbeta must be 4-byte aligned");
+  if (dW && ((uintptr_t)dW & 3u)) return fail(RACE_ERR_INVALID_ARG, "dW must be 4-byte aligned");
+  const size_t dw_out = dW ? dw_out_floats(p) * sizeof(float) : 0;
   const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
   if (!p.causal) O = nullptr;   // the non-causal backward never reads O
   const void* ins[] = {Q, K, V, dO, O};
@@ -467,19 +522,27 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
     for (void* o2 : outs)
       if (o2 != o && overlaps(o, tbytes, o2, tbytes)) return fail(RACE_ERR_INVALID_ARG, "outputs overlap");
     if (overlaps(o, tbytes, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dbeta overlaps an output");
+    if (overlaps(o, tbytes, dW, dw_out)) return fail(RACE_ERR_INVALID_ARG, "dW overlaps an output");
   }
-  for (const void* i : ins)
+  for (const void* i : ins) {
     if (overlaps(i, tbytes, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dbeta overlaps an input");
+    if (overlaps(i, tbytes, dW, dw_out)) return fail(RACE_ERR_INVALID_ARG, "dW overlaps an input");
+  }
+  if (overlaps(dW, dw_out, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dW overlaps dbeta");
+  if (overlaps(dW, dw_out, W, dw_out_floats(p) * sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dW overlaps W");
   const size_t need_state = state_bytes(p);
   if (state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
-  const size_t need_ws = workspace_bytes(p, true);
+  const size_t need_ws = workspace_bytes(p, true, dW != nullptr);
   if (!workspace || workspace_bytes_in < need_ws)
-    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes" +
+                                        (dW ? " (backward with dW)" : ""));
+  if (dW && overlaps(dW, dw_out, workspace, need_ws)) return fail(RACE_ERR_INVALID_ARG, "dW overlaps the workspace");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, state, ws, s);
+  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
+  char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
 
   const float* content = static_cast<const float*>(state);
   const float* mass = content + (size_t)p.BH * p.LRP * p.D;
@@ -490,9 +553,10 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   float* bparts = dbeta ? reinterpret_cast<float*>(ws + align256(part_bytes(p)) + align256(bank_bytes(p))) : nullptr;
 
   race::NCArgs a{};
-  a.X = Q; a.Y = dO; a.out0 = dQ; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.X = Q; a.Y = dO; a.out0 = dQ; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.st_content = content; a.st_mass = mass; a.part = part;
   a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.dbeta_part = bparts;
+  a.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
   {
     ProfScope ps(s, "race_bwd_q");
     p.ks->bwd_q(a, dim3(p.nchunk, (unsigned)p.BH), s);
@@ -504,9 +568,10 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   }
   if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
   race::NCArgs b{};
-  b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = W; b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
+  b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = tables(p, W); b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
   b.st_content = dcontent; b.st_mass = dmass; b.chunk_tokens = p.chunk_tokens; b.nchunk = p.nchunk;
   b.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
+  b.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
   {
     ProfScope ps(s, "race_bwd_kv");
     p.ks->bwd_kv(b, dim3(p.nchunk, (unsigned)p.BH), s);
@@ -516,7 +581,8 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
     ProfScope ps(s, "race_dbeta_finalize");
     launch_dbeta_finalize(p, bparts, dbeta, s);
   }
-  return check_launch("race_dbeta_finalize");
+  if ((st = check_launch("race_dbeta_finalize")) != RACE_OK) return st;
+  return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
 }
 
 // ---- recurrent decode: the state is the bank [BH][LRP][d] + mass [BH][LRP]
@@ -566,7 +632,7 @@ race_status race_attn_decode_prefill(const void* K, const void* V, const float* 
   float* content = static_cast<float*>(state);
   float* mass = content + (size_t)p.BH * p.LRP * p.D;
   race::NCArgs a{};
-  a.X = K; a.Y = V; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.part = part; a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
   {
     ProfScope ps(s, "race_bucket_reduce");
@@ -602,7 +668,7 @@ race_status race_attn_decode(const void* Q, const void* K, const void* V, const 
     return fail(RACE_ERR_INVALID_ARG, "state overlaps a token buffer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   race::DArgs a{};
-  a.Q = Q; a.K = K; a.V = V; a.O = O; a.W = W; a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.content = static_cast<float*>(state);
   a.mass = a.content + (size_t)p.BH * p.LRP * p.D;
   {
@@ -624,7 +690,7 @@ race_status race_softbucket_debug(const void* X, const float* W, float beta, int
   if (!aligned16(X) || !aligned16(W) || !aligned16(phi_out)) return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   int64_t blocks = (p.N + race::TT - 1) / race::TT;
   if (blocks > 4096) blocks = 4096;
-  p.ks->softbucket_dbg(X, W, beta, p.L, p.P, p.N, phi_out, dim3((unsigned)blocks, (unsigned)p.BH),
+  p.ks->softbucket_dbg(X, tables(p, W), beta, p.L, p.P, p.N, phi_out, dim3((unsigned)blocks, (unsigned)p.BH),
                        reinterpret_cast<hipStream_t>(stream));
   return check_launch("race_softbucket_dbg");
 }

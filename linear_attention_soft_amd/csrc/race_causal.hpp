@@ -51,8 +51,9 @@ struct TWArgs {
   const float* bank_in;   // [BH][nseg][LRP][d+1]: bank before (forward) / after (reverse) the segment
   const float* den;       // [BH][N]
   const float* hvec;      // [BH][N]
-  const float* W;
+  Tables W;
   float* dbeta_part;      // when set: [BH][nseg][waves] shares of dL/dbeta
+  float* dpre_out;        // when set: dL/dPre of every token, float32 [BH][N][NHP]
   float beta;
   int L, P;
   int64_t N;
@@ -172,7 +173,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
 
   frag wt[C::NCTW][G::NQS];
 #pragma unroll
-  for (int j = 0; j < C::NCTW; ++j) wt_frags_reg<T, G>(a.W, a.L, a.P, w + C::NM * j, wt[j]);
+  for (int j = 0; j < C::NCTW; ++j) wt_frags_reg<T, G>(a.W.at(bh), a.L, a.P, w + C::NM * j, wt[j]);
   // identity operands: lane (c, h), element i is 1 where kmap(s, h, i) == c
   frag idn[2];
 #pragma unroll
@@ -263,6 +264,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     float dp[G::NHP];
 #pragma unroll
     for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * G::NHP + i];
+    if (a.dpre_out && w == 0 && t0 + n < s1)
+      store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + t0 + n) * G::NHP, dp, h);
     frag bq[G::NQS];
 #pragma unroll
     for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dp, qs);
@@ -278,7 +281,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     }
   };
 
-  build_proj_frags<T, G>(a.W, a.L, a.P, S.Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
   load_stage(0);
   stage(0, 0);
   __syncthreads();

@@ -23,7 +23,7 @@ struct DArgs {
   void* O;
   float* content;   // [BH][LRP][d], updated in place
   float* mass;      // [BH][LRP], updated in place
-  const float* W;
+  Tables W;
   float beta;
   int L, P;
   int64_t N;        // new tokens per (batch, head)
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
   const int prole = tid / (G::NHP * TPH), php = (tid / TPH) % G::NHP, pq = tid % TPH;
   const int pl = php / G::PE, pt = php % G::PE;
   const bool pok = tid < 2 * G::NHP * TPH && pl < a.L && pt < a.P;
-  const float* pw = a.W + (size_t)(pok ? pl * a.P + pt : 0) * D;
+  const float* pw = a.W.at(bh) + (size_t)(pok ? pl * a.P + pt : 0) * D;
 
   for (int64_t t = 0; t < a.N; ++t) {
     for (int i = tid; i < 3 * D; i += 256) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];

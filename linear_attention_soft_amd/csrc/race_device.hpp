@@ -151,6 +151,16 @@ __device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Projection tables: float32 [L][P][d] shared by every head (hstride 0), or
+// [H][L][P][d] with one set per head (hstride L * P * d).  Sequence bh of a
+// [B][H] batch is head bh % H.
+struct Tables {
+  const float* W;
+  int64_t hstride;
+  int H;
+  __device__ __forceinline__ const float* at(int64_t bh) const { return W + (size_t)(bh % H) * hstride; }
+};
+
 // ---------------------------------------------------------------- geometry
 // Compile-time geometry of one kernel instance.
 //   D     head dim (multiple of 32)
@@ -461,6 +471,18 @@ __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 
       dpre[l * G::PE + t] = beta * d * (1.f - uu * uu);
       bterm += uu * d;
     }
+  }
+}
+
+// One token's dPre slots to row[0, NHP): the two lanes that hold the token
+// (lane halves h = 0, 1, both with every slot) write one half each.
+template <class G>
+__device__ __forceinline__ void store_dpre_half(float* __restrict__ row, const float (&dpre)[G::NHP], int h) {
+  constexpr int HALF = cdiv(G::NHP, 2);
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float v = h ? dpre[HALF + i < G::NHP ? HALF + i : G::NHP - 1] : dpre[i];
+    if (HALF * h + i < G::NHP) row[HALF * h + i] = v;
   }
 }
 

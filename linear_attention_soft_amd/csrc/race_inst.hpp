@@ -5,20 +5,21 @@
 #include "race_registry.hpp"
 #include "race_walk.hpp"
 #include "race_decode.hpp"
+#include "race_dw.hpp"
 
 namespace race {
 
 // Soft assignments of token rows written out as float32 [BH][N][L][R]
 // (a test export of the fused front end every kernel uses).
 template <typename T, class G>
-__global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, const float* W, float beta,
+__global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, Tables W, float beta,
                                                            int L, int P, int64_t N, float* out) {
   using E = Eng<T>;
   using frag = typename E::frag;
   __shared__ frag Wf[G::NPT * G::KD * 64];
-  build_proj_frags<T, G>(W, L, P, Wf);
-  __syncthreads();
   const int bh = blockIdx.y;
+  build_proj_frags<T, G>(W.at(bh), L, P, Wf);
+  __syncthreads();
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const T* X = static_cast<const T*>(Xv) + (size_t)bh * N * G::D;
   const int LR = L << G::PE;
@@ -58,7 +59,7 @@ struct Inst {
   static void bwd_kv(const NCArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_bwd_kv<T, G>), g, dim3(256), 0, s, a);
   }
-  static void dbg(const void* X, const float* W, float beta, int L, int P, int64_t N, float* out,
+  static void dbg(const void* X, const Tables& W, float beta, int L, int P, int64_t N, float* out,
                   dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, out);
   }
@@ -79,14 +80,18 @@ struct Inst {
   static void decode(const DArgs& a, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((race_decode<T, G>), dim3(grid), dim3(256), 0, s, a);
   }
+  static void dw_partial(const DWArgs& a, dim3 g, hipStream_t s) {
+    hipLaunchKernelGGL((race_dw_partial<T, G>), g, dim3(256), 0, s, a);
+  }
   // nc: compile the non-causal kernels; causal: compile the causal ones
   template <bool NC, bool CAUSAL>
   static KernelSet set(int dtype) {
     KernelSet k{};
-    k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP;
+    k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP; k.NHP = G::NHP;
     k.reduce = reduce;
     k.softbucket_dbg = dbg;
     k.decode = decode;
+    k.dw_partial = dw_partial;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
       k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;

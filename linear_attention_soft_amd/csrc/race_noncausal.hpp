@@ -27,7 +27,7 @@ struct NCArgs {
   const void* Y;            // V (reduce, bwd_kv) or dO (bwd_q)
   void* out0;               // O (readout), dQ (bwd_q), dV (bwd_kv)
   void* out1;               // dK (bwd_kv)
-  const float* W;           // [L][P][d]
+  Tables W;
   const float* st_content;  // [BH][LRP][d]   bucket (or gradient) bank
   const float* st_mass;     // [BH][LRP]
   float* part;              // [BH][nchunk][LRP][d+1] partial banks
@@ -44,6 +44,9 @@ struct NCArgs {
   // backward kernels: when set, each wave writes its share of dL/dbeta to
   // dbeta_part[(bh * nchunk + chunk) * 4 + wave]
   float* dbeta_part;
+  // backward kernels: when set, dL/dPre of every token, float32 [BH][N][NHP]
+  // (hyperplane slot l * PE + t), for the table gradient
+  float* dpre_out;
 };
 
 constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
   __syncthreads();
 
   const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   __shared__ T OS[4][OutStage<G::D, T>::ELEMS];
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
   build_readout_frags<T, G>(a.st_content + (size_t)bh * G::LRP * G::D, a.st_mass + (size_t)bh * G::LRP, RF);
   __syncthreads();
 
@@ -410,9 +413,9 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const float* content = a.st_content + (size_t)bh * G::LRP * G::D;
   const float* mass = a.st_mass + (size_t)bh * G::LRP;
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
   build_bank_rows_frags<T, G, false>(content, DF);
-  build_wt_frags<T, G>(a.W, a.L, a.P, WTf);
+  build_wt_frags<T, G>(a.W.at(bh), a.L, a.P, WTf);
   for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) massL[i] = mass[i];
   __syncthreads();
 
@@ -478,6 +481,7 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
     float dpre[G::NHP], bterm = 0.f;
     assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
     if (valid && h == 0) bsum += bterm;
+    if (a.dpre_out && valid) store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + tok) * G::NHP, dpre, h);
     // the wave's 32 rows of Bs are free until the dO rows are staged below
     dx_mma_stage<T, G>(WTf, dpre, Bs + 32 * w * BSP);
     OutStage<G::D, T>::flush(Bs + 32 * w * BSP, dQ, base + 32 * w, t_end);
@@ -548,10 +552,10 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const float* dcontent = a.st_content + (size_t)bh * G::LRP * G::D;
   const float* dmass = a.st_mass + (size_t)bh * G::LRP;
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
   build_bank_cols_frags<T, G>(dcontent, VF);
   build_bank_rows_frags<T, G, false>(dcontent, KF);
-  build_wt_frags<T, G>(a.W, a.L, a.P, WTf);
+  build_wt_frags<T, G>(a.W.at(bh), a.L, a.P, WTf);
   for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) dmassL[i] = dmass[i];
   __syncthreads();
 
@@ -603,6 +607,7 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
     float dpre[G::NHP], bterm = 0.f;
     assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
     if (valid && h == 0) bsum += bterm;
+    if (a.dpre_out && valid) store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + tok) * G::NHP, dpre, h);
     dx_mma_stage<T, G>(WTf, dpre, OS[w]);
     OutStage<G::D, T>::flush(OS[w], dK, base, t_end);
   };

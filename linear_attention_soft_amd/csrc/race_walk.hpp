@@ -51,7 +51,7 @@ struct WArgs {
   float* den_out;         // FWD: [BH][N]
   const float* hvec;      // GSUM: h [BH][N]
   float* h_out;           // H: [BH][N]
-  const float* W;
+  Tables W;
   float beta;
   int L, P;
   int64_t N;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   const int win = w % C::NWIN;
   const int ct = w - C::NF;
 
-  build_proj_frags<T, G>(a.W, a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
   if (C::MASS && is_f && role_b) {
     for (int r = lane; r < C::WROWS; r += 64) {
       const int row = win * C::WROWS + r;

@@ -10,7 +10,7 @@ Shapes follow the pages' workloads: the single-layer scaling runs (batch 1,
 reaches 12M tokens at a small budget") and the language-model and
 long-classification task shapes (slides backup frame "task models differ from
 the scaling operator").  Each tensor has its own sub-seed
-1000 * config + {Q: 1, K: 2, V: 3, dO: 4, W: 5, aux: 6}.
+1000 * config + {Q: 1, K: 2, V: 3, dO: 4, W: 5, per-head W: 6}.
 """
 from __future__ import annotations
 
@@ -118,6 +118,13 @@ def make_W(w: Workload, seed_base: int | None = None) -> torch.Tensor:
     """Gaussian projection W[L][P][d], iid N(0, 1), float32, on the CPU."""
     base = 1000 * w.key if seed_base is None else seed_base
     return _randn((w.L, w.P, w.d), base + 5, "cpu")
+
+
+def make_W_per_head(w: Workload, seed_base: int | None = None) -> torch.Tensor:
+    """One set of Gaussian tables per head, W[H][L][P][d], iid N(0, 1),
+    float32, on the CPU."""
+    base = 1000 * w.key if seed_base is None else seed_base
+    return _randn((w.H, w.L, w.P, w.d), base + 6, "cpu")
 
 
 def make_inputs(w: Workload, device="cpu", seed_base: int | None = None,

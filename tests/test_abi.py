@@ -46,8 +46,8 @@ def test_status_strings():
     assert L.race_status_string(2) == b"RACE_ERR_UNSUPPORTED"
 
 
-def _shape(B=1, H=2, N=1000, d=64, dtype=1):
-    return race.race_shape(B, H, N, d, dtype)
+def _shape(B=1, H=2, N=1000, d=64, dtype=1, w_per_head=0):
+    return race.race_shape(B, H, N, d, dtype, w_per_head)
 
 
 def test_size_queries():
@@ -56,6 +56,12 @@ def test_size_queries():
     assert sb == 2 * 32 * 129 * 4            # B*H x LRP x (d + 1) float32
     assert race.race_attn_workspace_bytes(s, 4, 2, False, False) > 0
     assert race.race_attn_workspace_bytes(s, 4, 2, False, True) > 0
+    # backward with dW adds float32 dPre of both sides: 2 x B*H*N x NHP, NHP = (LRP / 2^P) * P = 8 here
+    for causal in (False, True):
+        extra = (race.race_attn_workspace_bytes(s, 4, 2, causal, 2)
+                 - race.race_attn_workspace_bytes(s, 4, 2, causal, 1))
+        assert extra >= 2 * 2 * 4096 * 8 * 4
+    assert race.race_attn_workspace_bytes(s, 4, 2, False, 3) == 0
     # invalid arguments give 0
     assert race.race_attn_state_bytes(s, 0, 2, False) == 0
     assert race.race_attn_state_bytes(s, 4, 0, False) == 0
@@ -94,6 +100,7 @@ def test_forward_rejects_bad_arguments(kw, code):
 
 @pytest.mark.parametrize("shape,code", [
     (_shape(d=96), 2), (_shape(d=0), 1), (_shape(N=0), 1), (_shape(B=0), 1), (_shape(dtype=7), 1),
+    (_shape(w_per_head=2), 1),
 ])
 def test_forward_rejects_bad_shapes(shape, code):
     assert _fwd(shape) == code
@@ -104,9 +111,9 @@ def test_backward_rejects_bad_arguments():
     s = _shape()
     base = [FAKE + i * 0x1000000 for i in range(12)]
 
-    def call(state=base[9], stateb=1 << 30, ws=base[10], wsb=1 << 30, beta=1.0, dq=base[6], dbeta=None):
+    def call(state=base[9], stateb=1 << 30, ws=base[10], wsb=1 << 30, beta=1.0, dq=base[6], dbeta=None, dW=None):
         return Lb.race_attn_bwd(base[0], base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, 0, None, base[5],
-                                dq, base[7], base[8], dbeta, ctypes.byref(s), state, stateb, ws, wsb, None)
+                                dq, base[7], base[8], dbeta, dW, ctypes.byref(s), state, stateb, ws, wsb, None)
 
     assert call(state=None) == 1
     assert call(beta=math.nan) == 1
@@ -115,6 +122,12 @@ def test_backward_rejects_bad_arguments():
     assert call(dq=base[0]) == 1                # dQ overlaps Q
     assert call(dbeta=base[1] + 2) == 1         # dbeta misaligned
     assert call(dbeta=base[1] + 64) == 1        # dbeta inside K
+    assert call(dW=base[11] + 2) == 1           # dW misaligned
+    assert call(dW=base[2] + 64) == 1           # dW inside V
+    assert call(dW=base[3]) == 1                # dW is W
+    assert call(dW=base[11], dbeta=base[11] + 8) == 1   # dW overlaps dbeta
+    wb1 = race.race_attn_workspace_bytes(s, 3, 2, False, 1)
+    assert call(dW=base[11], wsb=wb1) == 3      # workspace sized for the backward without dW
 
 
 def test_softbucket_debug_rejects_small_P():
