@@ -247,12 +247,23 @@ def main():
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name, dname, tokens)
 
+    # the runtime's own 1 GiB device copy, timed in the same run: the stream
+    # rate a read + write kernel reaches on this part (context for frac)
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     if args.calibrate_copy:
-        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -278,7 +289,8 @@ def main():
                    "seq_len": w.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": dname, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": avg_ms},
+                     "kernel": dname, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": avg_ms,
+                     "device_copy_GBps_same_run": copy_gbps},
         "step_hbm_frac": (11 * row_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items()},
         "cpu_baseline": cpu,

@@ -117,3 +117,36 @@ def test_decode_with_per_head_tables():
     Q, K, V = (to64(inp[k]) for k in ("Q", "K", "V"))
     ref = orc.forward(Q, K, V, inp["W"].double().numpy(), w.beta, True)[:, :, n0:]
     check("O decode", O, ref, TOL["f32"], float(np.abs(V).max()))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dW_edge_cases(causal):
+    """Two tokens, a ragged length of one tile plus a few rows, one token
+    (the layer returns V whatever the assignments are, so dW = 0 up to the
+    float32 rounding of terms that cancel) and beta = 0 (uniform assignments
+    whatever W is: dW is exactly zero)."""
+    wide = 5 if causal else 4          # the P = 6, L = 4 kernels are compiled for the causal variant only
+    for key, N, B, H, dtype, beta in [(1, 2, 1, 2, "f32", None), (2, 131, 2, 1, "f32", None),
+                                       (wide, 67, 1, 1, "bf16", None), (1, 1, 1, 2, "f32", None),
+                                       (1, 300, 1, 1, "f32", 0.0)]:
+        w = replace(ri.WORKLOADS[key].with_size(N=N, B=B, H=H), causal=causal, dtype=dtype)
+        if beta is not None:
+            w = replace(w, beta=beta)
+        inp = _inputs(w, per_head=(B > 1))
+        dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        say(f"dW edge key={key} N={N} B={B} H={H} {dtype} causal={causal} beta={w.beta}")
+        O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal)
+        *_, dW = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal, dev["dO"],
+                                    state, O=O if causal else None, dW=True)
+        torch.cuda.synchronize()
+        if w.beta == 0.0:
+            assert float(dW.abs().max()) == 0.0
+            continue
+        if N == 1:
+            scale = w.beta * float(inp["dO"].abs().max() * inp["V"].abs().max()
+                                   * torch.maximum(inp["Q"].abs().max(), inp["K"].abs().max()))
+            say(f"  one token: max|dW| {float(dW.abs().max()):.3e}, cancelling-term scale {scale:.3e}")
+            assert float(dW.abs().max()) <= 1e-5 * scale
+            continue
+        Q, K, V, dO = (to64(inp[k]) for k in ("Q", "K", "V", "dO"))
+        check("dW", dW, orc.dW(Q, K, V, inp["W"].double().numpy(), w.beta, dO, causal), TOL[dtype])
