@@ -193,13 +193,11 @@ size_t state_bytes(const Plan& p) {
 // Causal backward workspace: h [BH][N], gradient segment sums and their
 // reverse scan [BH][nseg][LRP][d+1] each.
 // Per-wave shares of dL/dbeta: query side then key side.  Non-causal: 4
-// waves per (chunk, head); causal: one wave per table window per (segment,
-// head).
+// waves per (chunk, head); causal: one wave per 32 bucket rows per (segment,
+// head) (the transposed walks' waves).
 int64_t dbeta_parts_per_side(const Plan& p) {
   if (!p.causal) return (int64_t)p.BH * p.nchunk * 4;
-  const int R = 1 << p.PE;
-  const int URP = R > 32 ? R : 32;
-  return (int64_t)p.BH * p.nseg * (p.LRP / URP);
+  return (int64_t)p.BH * p.nseg * (p.LRP / 32);
 }
 size_t dbeta_bytes(const Plan& p) { return align256(2 * (size_t)dbeta_parts_per_side(p) * sizeof(float)); }
 

@@ -61,11 +61,15 @@ struct TWArgs {
   int nseg;
 };
 
-// One wave per window of URP bucket rows (whole tables); the workgroup walks
-// one (segment, batch x head).
+// One wave per window of 32 bucket rows: whole tables when 2^PE <= 32, half
+// a table at 2^PE = 64 (SPL = 2 waves per table, which exchange their
+// softmax-backward sums once per chunk).  The workgroup walks one (segment,
+// batch x head).
 template <typename T, class G, bool REV>
 struct TWCfg {
-  static constexpr int URP = G::R > 32 ? G::R : 32;
+  static constexpr int URP = 32;
+  static constexpr int SPL = G::R > 32 ? G::R / 32 : 1;   // waves per table
+  static_assert(SPL <= 2 && G::PE + 1 <= 8, "tables of at most 64 corners");
   static constexpr int NM = G::LRP / URP;             // waves
   static constexpr int ATU = URP / 32;                // 32-row tiles per wave
   static constexpr int NT = 64 * NM;
@@ -81,13 +85,14 @@ struct TWCfg {
   // hi + lo parts (the softmax backward that follows subtracts nearly equal
   // terms).
   static constexpr bool BANK_LO = false;
-  static_assert(G::LRP % URP == 0, "windows of whole tables");
+  static_assert(G::LRP % URP == 0, "windows of 32 rows");
 };
 
 template <typename T, class G, bool REV>
 struct TWLds {
   using C = TWCfg<T, G, REV>;
-  typename Eng<T>::frag Wf[G::NPT * G::KD * 64];   // projection operands
+  // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
+  typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
   alignas(16) T PhiBT[C::NM][C::URP * C::TSP];   // wave-private Phi_B^T of the current chunk
   alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
   alignas(16) T AR[2][WC * C::FS];               // output-role rows (projection operands)
@@ -96,6 +101,7 @@ struct TWLds {
   alignas(16) T XF[2][C::NXS][WC * C::FS];       // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
+  alignas(16) float XS[C::SPL > 1 ? C::NM : 1][WC][8];   // half-table softmax-backward sums (SPL = 2)
 };
 
 // W^T frags of the dX contraction for column tile ct, built into registers
@@ -281,7 +287,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     }
   };
 
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
+  if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
+  else build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
   load_stage(0);
   stage(0, 0);
   __syncthreads();
@@ -291,8 +298,6 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     const int bb = (int)(k & 1);
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     const bool valid = t0 + n < s1;
-    load_stage(k + 1);
-    __builtin_amdgcn_sched_barrier(0);
     // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
     float uA[G::NHP], phA[URP / 2];
     {
@@ -300,7 +305,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[bb][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP];
-      project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, pre);
+      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, pre);
+      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, pre);
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uA, phA);
     }
     {
@@ -308,7 +314,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[bb][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP], uB[G::NHP], phB[URP / 2];
-      project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
+      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
+      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uB, phB);
       T* pt = S.PhiBT[w];
 #pragma unroll
@@ -408,13 +415,46 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
       float dpre[G::NHP], bterm = 0.f;
 #pragma unroll
       for (int i = 0; i < G::NHP; ++i) dpre[i] = 0.f;
-      assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre, bterm);
-      if (valid && h == 0) bsum += bterm;
-      if (h == 0) {
+      if constexpr (C::SPL == 1) {
+        assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre, bterm);
+        if (valid && h == 0) bsum += bterm;
+        if (h == 0) {
 #pragma unroll
-        for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
+          for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
+        }
+      } else {
+        // half table: exchange the sums with the other half (waves 2j, 2j + 1),
+        // add them in the same order in both, then dU_t = A_t - s tanh(beta u_t)
+        constexpr bool LOWER = (TG & 1) == 0;
+        constexpr int l = R0 / G::R;
+        float part[1 + G::PE];
+        assign_partials_half<G, R0>(phA, dphi, part);
+        if (h == 0) {
+#pragma unroll
+          for (int i = 0; i <= G::PE; ++i) S.XS[w][n][i] = part[i];
+        }
+        __syncthreads();
+        const float* lo = S.XS[w & ~1][n];
+        const float* hi = S.XS[w | 1][n];
+        const float s = lo[0] + hi[0];
+#pragma unroll
+        for (int t = 0; t < G::PE; ++t) {
+          const float uu = uA[l * G::PE + t];
+          const float du = (lo[1 + t] + hi[1 + t]) - s * tanh_f(a.beta * uu);
+          dpre[l * G::PE + t] = a.beta * du * (1.f - uu * uu);
+          bterm += uu * du;
+        }
+        if (LOWER && valid && h == 0) bsum += bterm;
+        if (LOWER && h == 0) {
+#pragma unroll
+          for (int t = 0; t < G::PE; ++t) S.DP[bb][n * G::NHP + l * G::PE + t] = dpre[l * G::PE + t];
+        }
       }
     }
+    // rows of chunk k + 1: loaded here rather than at the top of the chunk
+    // (their registers are not live through the features and readout)
+    load_stage(k + 1);
+    __builtin_amdgcn_sched_barrier(0);
     // bank update: B[c][lr] += sum_b X_b[c] phi_B,b[lr]; X^T tiles (lane = column,
     // registers = tokens in kmap order) from X rows times the identity
     {

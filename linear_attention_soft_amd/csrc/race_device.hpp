@@ -217,6 +217,48 @@ __device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
   }
 }
 
+// Projection A operand with one tile per table: tile l holds the PE
+// hyperplanes of table l (bf16: rows t then the lo parts at 8 + t; f32: rows
+// t), rows past PE zero, duplicated in both row halves as above.
+template <typename T, class G>
+__device__ void build_table_frags(const float* __restrict__ W, int L, int P,
+                                  typename Eng<T>::frag* __restrict__ Wt) {
+  using E = Eng<T>;
+  static_assert(G::PE <= (E::NSPLIT == 2 ? 8 : 16), "one tile per table");
+  for (int idx = threadIdx.x; idx < G::LMAX * G::KD * 64; idx += blockDim.x) {
+    const int lane = idx & 63;
+    const int q = (idx >> 6) % G::KD;
+    const int l = (idx >> 6) / G::KD;
+    const int row = lane & 31, h = lane >> 5;
+    const int rho = 4 * (row >> 3) + (row & 3);
+    const int t = E::NSPLIT == 2 ? (rho & 7) : rho;
+    const int part = E::NSPLIT == 2 ? (rho >> 3) : 0;
+    const bool ok = (t < G::PE) && (l < L) && (t < P);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ok ? W[(size_t)(l * P + t) * G::D + 16 * q + 8 * h + i] : 0.f;
+    typename E::frag hi, lo;
+    E::split(v, hi, lo);
+    Wt[idx] = part ? lo : hi;
+  }
+}
+
+// pre[l * PE + t] = W^(l)_t . x for table l only (tile l of build_table_frags);
+// other slots are 0.
+template <typename T, class G, int l>
+__device__ __forceinline__ void project_table(const typename Eng<T>::frag* __restrict__ Wt,
+                                              const typename Eng<T>::frag (&xf)[G::KD], float (&pre)[G::NHP]) {
+  using E = Eng<T>;
+  const int lane = lane_id();
+#pragma unroll
+  for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int q = 0; q < G::KD; ++q) E::mma(Wt[(l * G::KD + q) * 64 + lane], xf[q], acc);
+#pragma unroll
+  for (int t = 0; t < G::PE; ++t) pre[l * G::PE + t] = E::NSPLIT == 2 ? acc[t] + acc[t + 8] : acc[t];
+}
+
 // dX A operand: W^T[c][e] for the contraction dX = dPre . W.  bf16 entries e
 // cover (hp, W_hi, dPre_hi), (hp, W_hi, dPre_lo), (hp, W_lo, dPre_hi).
 template <typename T, class G>
@@ -472,6 +514,36 @@ __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 
       bterm += uu * d;
     }
   }
+}
+
+// Softmax-backward sums of one token over the 32 corners of a half table
+// (bucket rows [R0, R0 + 32), R0 a multiple of 32, 2^PE = 64): out[0] =
+// sum_r phi_r dphi_r and out[1 + t] = sum_r phi_r dphi_r v_{r,t}.  Both lane
+// halves end with the sums over all 32 corners.  The two halves of a table
+// give dU_t = A_t - s E[v_t] with s, A the sums over the whole table and
+// E[v_t] = sum_r phi_r v_{r,t} = tanh(beta u_t) (phi factorises over the
+// corner bits, each bit a two-way softmax).
+template <class G, int R0>
+__device__ __forceinline__ void assign_partials_half(const float (&phi)[16], const float (&dphi)[16],
+                                                     float (&out)[1 + G::PE]) {
+  static_assert(R0 % 32 == 0 && G::R == 64, "half tables of 64 corners");
+  const int h = lane_id() >> 5;
+  const float sgn2 = h ? 1.f : -1.f;
+#pragma unroll
+  for (int i = 0; i <= G::PE; ++i) out[i] = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r0 = (R0 + 8 * (v >> 2) + (v & 3)) % G::R;
+    const float pd = phi[v] * dphi[v];
+    out[0] += pd;
+#pragma unroll
+    for (int t = 0; t < G::PE; ++t) {
+      if (t == 2) out[1 + t] += sgn2 * pd;
+      else out[1 + t] += ((r0 >> t) & 1) ? pd : -pd;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i <= G::PE; ++i) out[i] += xor32(out[i]);
 }
 
 // One token's dPre slots to row[0, NHP): the two lanes that hold the token
