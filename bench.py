@@ -49,6 +49,20 @@ ROW_PASSES = {
 }
 
 
+# algorithmic flops per (token, head) of the causal walks' contractions, with
+# LR = L * 2^P buckets: the bank read out or contracted over columns (2 LR d),
+# the bank update (2 LR (d + 1)), and for the transposed walks dX = dPre W
+# (2 L P d); the chunked intra terms and the soft assignments are not counted
+def causal_flops(kernel: str, L: int, P: int, d: int):
+    LR = L << P
+    upd = 2 * LR * (d + 1)
+    return {"race_causal_segsum": upd, "race_causal_gradsum": upd,
+            "race_causal_fwd": 2 * LR * (d + 1) + upd, "race_causal_h": 2 * LR * (d + 1) + upd,
+            "race_causal_dv": 2 * LR * d + upd,
+            "race_causal_dq": 2 * LR * d + upd + 2 * L * P * d,
+            "race_causal_dk": 2 * LR * d + upd + 2 * L * P * d}.get(kernel)
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "linear_attention_soft_amd", "csrc", "*"))):
@@ -295,6 +309,13 @@ def main():
         "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items()},
         "cpu_baseline": cpu,
     }
+    fl = causal_flops(dname, w.L, w.P, w.d) if w.causal else None
+    if fl:
+        # the causal walks also sit far below the MFMA roofline: bf16 dense peak
+        tf = fl * w.B * w.H * w.N / (avg_ms * 1e-3) / 1e12
+        peak = 2500.0 if w.dtype == "bf16" else 157.3
+        out["roofline_mfma"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                                "frac": tf / peak, "kernel": dname, "alg_flops_per_launch": fl * w.B * w.H * w.N}
     if args.dW and "race_dw_partial" in kern:
         # the table-gradient stream: both sides' rows plus their float32 dPre
         pe = max(w.P, 3)

@@ -76,7 +76,10 @@ struct TWCfg {
   static constexpr bool XSPLIT = REV && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
   static constexpr int NXS = XSPLIT ? 2 : 1;
   static constexpr int FS = G::D + 16 / (int)sizeof(T);   // staged row (elements)
-  static constexpr int TSP = WC + 8;                  // Phi_B^T row (elements)
+  // Phi_B^T row (elements): an 88-byte stride keeps both its 2-byte transposed
+  // writes (rows 4 apart fall 96 bytes apart) and its 8-byte operand reads (32
+  // consecutive rows start on distinct 8-byte bank pairs) free of bank conflicts
+  static constexpr int TSP = WC + 12;
   static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
   static constexpr int EPC = 16 / (int)sizeof(T);
   static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
@@ -101,7 +104,7 @@ struct TWLds {
   alignas(16) T XF[2][C::NXS][WC * C::FS];       // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
-  alignas(16) float XS[C::SPL > 1 ? C::NM : 1][WC][8];   // half-table softmax-backward sums (SPL = 2)
+  alignas(16) float XS[C::SPL > 1 ? C::NM : 1][8][WC];   // half-table softmax-backward sums (SPL = 2)
 };
 
 // W^T frags of the dX contraction for column tile ct, built into registers
@@ -328,12 +331,17 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     }
     wave_lds_sync();
 
-    // inter: bank . U_a (U exact in T)
+    // inter: bank . U_a (U exact in T), and the intra scores
+    // mf[b][a] = X_b . U_a (+ xe_b ue_a below), masked (b <= a forward, b >= a
+    // reverse); one read of each U fragment serves both
     f32x16 dp[ATU];
 #pragma unroll
     for (int at = 0; at < ATU; ++at) dp[at] = zero16();
+    f32x16 mf = zero16();
     {
       const T* uf = S.UF[bb] + n * FS + 8 * h;
+      const T* xf = S.XF[bb][0] + n * FS + 8 * h;
+      const T* xl = S.XF[bb][C::NXS - 1] + n * FS + 8 * h;
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) {
         const frag ub = *reinterpret_cast<const frag*>(uf + 16 * q);
@@ -351,17 +359,6 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
             E::mma(E::pack(v8), ub, dp[at]);
           }
         }
-      }
-    }
-    // intra scores mf[b][a] = X_b . U_a + xe_b ue_a, masked (b <= a forward, b >= a reverse)
-    f32x16 mf = zero16();
-    {
-      const T* uf = S.UF[bb] + n * FS + 8 * h;
-      const T* xf = S.XF[bb][0] + n * FS + 8 * h;
-      const T* xl = S.XF[bb][C::NXS - 1] + n * FS + 8 * h;
-#pragma unroll
-      for (int q = 0; q < G::KD; ++q) {
-        const frag ub = *reinterpret_cast<const frag*>(uf + 16 * q);
         E::mma(*reinterpret_cast<const frag*>(xf + 16 * q), ub, mf);
         if (C::XSPLIT) E::mma(*reinterpret_cast<const frag*>(xl + 16 * q), ub, mf);
       }
@@ -431,16 +428,14 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
         assign_partials_half<G, R0>(phA, dphi, part);
         if (h == 0) {
 #pragma unroll
-          for (int i = 0; i <= G::PE; ++i) S.XS[w][n][i] = part[i];
+          for (int i = 0; i <= G::PE; ++i) S.XS[w][i][n] = part[i];
         }
         __syncthreads();
-        const float* lo = S.XS[w & ~1][n];
-        const float* hi = S.XS[w | 1][n];
-        const float s = lo[0] + hi[0];
+        const float s = S.XS[w & ~1][0][n] + S.XS[w | 1][0][n];
 #pragma unroll
         for (int t = 0; t < G::PE; ++t) {
           const float uu = uA[l * G::PE + t];
-          const float du = (lo[1 + t] + hi[1 + t]) - s * tanh_f(a.beta * uu);
+          const float du = (S.XS[w & ~1][1 + t][n] + S.XS[w | 1][1 + t][n]) - s * tanh_f(a.beta * uu);
           dpre[l * G::PE + t] = a.beta * du * (1.f - uu * uu);
           bterm += uu * du;
         }
