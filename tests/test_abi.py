@@ -161,3 +161,23 @@ def test_decode_rejects_bad_arguments():
                                        base[5], nb, None, 0, None) == 3
     assert Lb.race_attn_decode_prefill(base[1], base[2], base[3], ctypes.c_float(1.0), 3, 2, ctypes.byref(s),
                                        base[5], 8, base[6], wb, None) == 3
+
+
+def test_plain_c_client(tmp_path):
+    """The header compiles as C99 and a C program linked against the library
+    sees the documented host-side contract (no GPU calls are made)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib = race.library_path
+    if not os.path.exists(lib):
+        pytest.skip("library not built")
+    exe = tmp_path / "c_abi_check"
+    src = os.path.join(os.path.dirname(__file__), "c_abi_check.c")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), src, lib,
+                        f"-Wl,-rpath,{os.path.dirname(lib)}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout, r.stderr)
