@@ -101,3 +101,40 @@ def test_prefill_bank_matches_oracle():
         LR = w.L * w.R
         check(f"content head {h}", content[h, :LR], c.reshape(LR, w.d), TOL["bf16"])
         check(f"mass head {h}", mass[h, :LR], m.reshape(LR), 2.0 ** -9)
+
+
+def test_decode_steps_replayed_from_a_graph():
+    """Decode steps captured in a HIP graph (the launch-bound loop of a
+    serving step) replay to the eager results bit for bit: the state is reset
+    from the same prefill before each replay, and other eager decode work and
+    synchronisations run between the replays."""
+    w, inp = _case(2, 512, 2, 2, "f32")
+    n0, steps = 500, 6
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    say(f"decode graph replay key=2 prompt={n0} steps={steps}")
+    s0 = race.race_attn_decode_prefill(dev["K"][:, :, :n0].contiguous(), dev["V"][:, :, :n0].contiguous(),
+                                       dev["W"], w.beta, w.P, w.L)
+    toks = [{k: dev[k][:, :, n0 + i:n0 + i + 1].contiguous() for k in ("Q", "K", "V")} for i in range(steps)]
+    st_e = s0.clone()
+    O_e = [race.race_attn_decode(t["Q"], t["K"], t["V"], dev["W"], w.beta, w.P, w.L, st_e) for t in toks]
+    torch.cuda.synchronize()
+
+    race.profile_enable(False)
+    st_g = s0.clone()
+    O_g = [torch.empty_like(t["Q"]) for t in toks]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t, o in zip(toks, O_g):
+            race.race_attn_decode(t["Q"], t["K"], t["V"], dev["W"], w.beta, w.P, w.L, st_g, O=o)
+    other = s0.clone()
+    for rep in range(3):
+        st_g.copy_(s0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(O_e, O_g):
+            assert torch.equal(a, b), f"replay {rep}: O differs from the eager steps"
+        assert torch.equal(st_e, st_g), f"replay {rep}: state differs from the eager steps"
+        # unrelated eager decode work between replays
+        race.race_attn_decode(toks[rep]["Q"], toks[rep]["K"], toks[rep]["V"], dev["W"], w.beta, w.P, w.L, other)
+        torch.cuda.synchronize()
