@@ -269,23 +269,30 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   const float* den = a.tok_den ? a.tok_den + (size_t)bh * a.N : nullptr;
   const int tl = 32 * w + n;
   const int64_t last = t_end - 1;
-  // rows of the wave's 32 tokens: key rows as projection operands, value rows
-  // as 16-byte chunks (row = flat / CPR) for the LDS tile
-  auto load_tile = [&](int64_t b, frag (&xf)[G::KD], uint4 (&yv)[NCH]) {
-    load_row_frags_nb<T, G>(X + min(b + tl, last) * G::D, xf);
+  // one register set per operand: the next tile's key rows are loaded as
+  // soon as this tile's projection has consumed them, its value rows as soon
+  // as this tile's are in LDS; both loads stay in flight through the rest of
+  // the tile (fewer registers: two waves per SIMD)
+  frag xa[G::KD];
+  uint4 ya[NCH];
+  auto load_x = [&](int64_t b) { load_row_frags_nb<T, G>(X + min(b + tl, last) * G::D, xa); };
+  auto load_y = [&](int64_t b) {
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const int64_t trow = min(b + 32 * w + row, last);
-      yv[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
+      ya[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(Y + trow * G::D) + 16 * ch);
     }
   };
-  auto tile = [&](const frag (&cx)[G::KD], const uint4 (&cy)[NCH], int64_t base) {
+  load_x(t_begin);
+  load_y(t_begin);
+  for (int64_t base = t_begin; base < t_end; base += TT) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, cx, pre);
+    project<T, G>(Wf, xa, pre);
+    load_x(base + TT);
     soft_assign<G>(pre, beta2, a.L, u, phi);
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const int64_t trow = base + 32 * w + row;
-      uint4 val = trow < t_end ? cy[it] : make_uint4(0, 0, 0, 0);
+      uint4 val = trow < t_end ? ya[it] : make_uint4(0, 0, 0, 0);
       if (den && trow < t_end) {
         const float inv = 1.f / den[trow];
         T* e = reinterpret_cast<T*>(&val);
@@ -308,25 +315,11 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
       }
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
     }
+    load_y(base + TT);
     if (a.tok_extra && h == 0) hsv[tl] = valid ? a.tok_extra[(size_t)bh * a.N + tok] : 0.f;
     __syncthreads();
     reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, a.tok_extra ? hsv : nullptr, acc);
     __syncthreads();
-  };
-  frag xa[G::KD], xb[G::KD];
-  uint4 ya[NCH], yb[NCH];
-  int64_t base = t_begin;
-  load_tile(base, xa, ya);
-  while (base < t_end) {
-    load_tile(base + TT, xb, yb);
-    __builtin_amdgcn_sched_barrier(0);
-    tile(xa, ya, base);
-    base += TT;
-    if (base >= t_end) break;
-    load_tile(base + TT, xa, ya);
-    __builtin_amdgcn_sched_barrier(0);
-    tile(xb, yb, base);
-    base += TT;
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), acc);
 }
