@@ -16,7 +16,7 @@ race = pytest.importorskip("linear_attention_soft_amd")
 
 def _lib():
     if not os.path.exists(race.library_path):
-        pytest.fail("librace_attn.so is not built (run __graft_entry__.build())")
+        pytest.fail("librace_attn.so is not built (python -m linear_attention_soft_amd.build)")
     return race.lib()
 
 
