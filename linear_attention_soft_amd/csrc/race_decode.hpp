@@ -7,9 +7,10 @@
 // reads (the token sees itself):
 //   content += phi(K_t) V_t^T,  mass += phi(K_t)
 //   O_t = sum_l phi(Q_t) content / sum_l phi(Q_t) mass
-// One workgroup of 256 threads per (batch, head): thread (column c, row group
-// g) keeps bank rows [g * LRP / NG, (g + 1) * LRP / NG) of column c in
-// registers for all new tokens.  Projections, tanh, sigmoids and the soft
+// One workgroup of NT = d * NG threads per (batch, head): thread (column c,
+// row group g) keeps bank rows [g * LRP / NG, (g + 1) * LRP / NG) of column c
+// in registers for all new tokens; NG gives at least 256 threads and at most
+// 1024, and about 16 bank rows per thread in between.  Projections, tanh, sigmoids and the soft
 // assignments are float32 and are not rounded.
 #pragma once
 #include "race_device.hpp"
@@ -29,20 +30,28 @@ struct DArgs {
   int64_t N;        // new tokens per (batch, head)
 };
 
+template <class G>
+struct DecCfg {
+  static constexpr int lo = 256 / G::D, hi = 1024 / G::D, want = G::LRP / 16;
+  static constexpr int NG = want < lo ? lo : (want > hi ? hi : want);   // row groups per column
+  static constexpr int NT = G::D * NG;                                  // threads per (batch, head)
+};
+
 template <typename T, class G>
-__global__ __launch_bounds__(256) void race_decode(DArgs a) {
+__global__ __launch_bounds__((DecCfg<G>::NT)) void race_decode(DArgs a) {
   constexpr int D = G::D, LRP = G::LRP;
-  constexpr int NG = 256 / D;              // row groups per column
+  constexpr int NG = DecCfg<G>::NG;
+  constexpr int DEC_NT = DecCfg<G>::NT;
   constexpr int RPT = LRP / NG;            // bank rows per thread
-  static_assert(256 % D == 0 && LRP % NG == 0, "thread layout");
+  static_assert(DEC_NT % 64 == 0 && LRP % NG == 0, "thread layout");
   constexpr int TPH = 4;                   // threads per projection dot product
-  static_assert(2 * G::NHP * TPH <= 256, "projection threads");
+  static_assert(2 * G::NHP * TPH <= DEC_NT, "projection threads");
   __shared__ float xs[3][D];               // q, k, v of the current token
   __shared__ float sg[2][2][G::NHP];       // sigma(+-2 beta u) per role and hyperplane
   __shared__ float ph[2][LRP];             // soft assignments of q and k
   __shared__ float ms[LRP];                // mass
   __shared__ float num[NG][D];             // partial numerators
-  __shared__ float red[4];                 // per-wave partial denominators
+  __shared__ float red[DEC_NT / 64];       // per-wave partial denominators
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t bh = blockIdx.x;
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
   float bank[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) bank[i] = content[(size_t)(g * RPT + i) * D + c];
-  for (int lr = tid; lr < LRP; lr += 256) ms[lr] = mass[lr];
+  for (int lr = tid; lr < LRP; lr += DEC_NT) ms[lr] = mass[lr];
   const float beta2 = 2.f * a.beta;
   // projection thread: (role, hyperplane, quarter of d)
   const int prole = tid / (G::NHP * TPH), php = (tid / TPH) % G::NHP, pq = tid % TPH;
@@ -66,7 +75,7 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
   const float* pw = a.W.at(bh) + (size_t)(pok ? pl * a.P + pt : 0) * D;
 
   for (int64_t t = 0; t < a.N; ++t) {
-    for (int i = tid; i < 3 * D; i += 256) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];
+    for (int i = tid; i < 3 * D; i += DEC_NT) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];
     __syncthreads();
     // projections: TPH consecutive lanes split d, then tanh and the sigmoid pair
     if (tid < 2 * G::NHP * TPH) {
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
     }
     __syncthreads();
     // soft assignments phi_r = prod_t sigma(2 beta u_t v_{r,t})
-    for (int j = tid; j < 2 * LRP; j += 256) {
+    for (int j = tid; j < 2 * LRP; j += DEC_NT) {
       const int role = j / LRP, lr = j % LRP;
       const int l = lr / G::R, r = lr % G::R;
       float p = 0.f;
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
     }
     num[g][c] = nacc;
     float dacc = 0.f;
-    for (int lr = tid; lr < LRP; lr += 256) {
+    for (int lr = tid; lr < LRP; lr += DEC_NT) {
       ms[lr] += ph[1][lr];
       dacc += ph[0][lr] * ms[lr];
     }
@@ -118,13 +127,16 @@ __global__ __launch_bounds__(256) void race_decode(DArgs a) {
       float nn = 0.f;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) nn += num[gg][c];
-      out[t * D + c] = (T)(nn / ((red[0] + red[1]) + (red[2] + red[3])));
+      float den = 0.f;
+#pragma unroll
+      for (int k = 0; k < DEC_NT / 64; ++k) den += red[k];
+      out[t * D + c] = (T)(nn / den);
     }
     __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) content[(size_t)(g * RPT + i) * D + c] = bank[i];
-  for (int lr = tid; lr < LRP; lr += 256) mass[lr] = ms[lr];
+  for (int lr = tid; lr < LRP; lr += DEC_NT) mass[lr] = ms[lr];
 }
 
 }  // namespace race

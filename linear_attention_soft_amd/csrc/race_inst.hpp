@@ -78,7 +78,7 @@ struct Inst {
                        static_cast<const T*>(dO), static_cast<const T*>(O), den, h, total);
   }
   static void decode(const DArgs& a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((race_decode<T, G>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((race_decode<T, G>), dim3(grid), dim3(DecCfg<G>::NT), 0, s, a);
   }
   static void dw_partial(const DWArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_dw_partial<T, G>), g, dim3(256), 0, s, a);
