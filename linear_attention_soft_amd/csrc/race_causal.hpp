@@ -574,6 +574,8 @@ static __global__ void race_seg_scan(const float* __restrict__ part, float* __re
   if (idx >= (int64_t)BH * per) return;
   const int64_t bh = idx / per, rem = idx % per;
   float run = 0.f;
+  // unrolled so that several segment loads are in flight at once
+#pragma unroll 8
   for (int k = 0; k < nseg; ++k) {
     const int s = reverse ? nseg - 1 - k : k;
     const size_t o = ((size_t)bh * nseg + s) * per + rem;
