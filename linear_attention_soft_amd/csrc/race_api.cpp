@@ -32,6 +32,8 @@ __global__ void race_bank_finalize(const float* __restrict__ part, int nchunk, i
   const int lr = (int)(rem / (D + 1)), c = (int)(rem % (D + 1));
   const float* p = part + (size_t)bh * nchunk * per + rem;
   float s = 0.f;
+  // unrolled so that several partial loads are in flight (the sum stays in chunk order)
+#pragma unroll 8
   for (int k = 0; k < nchunk; ++k) s += p[(size_t)k * per];
   if (c < D) content[((size_t)bh * LRP + lr) * D + c] = s;
   else mass[(size_t)bh * LRP + lr] = s;

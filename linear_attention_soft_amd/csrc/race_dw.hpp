@@ -147,6 +147,7 @@ static __global__ __launch_bounds__(1024) void race_dw_finalize(const float* __r
     for (int b = 0; b < B; ++b)
       for (int hh = h0; hh < h0 + nh; ++hh) {
         const float* p = part + ((((size_t)side * B + b) * H + hh) * nchunk * NHP + slot) * D + c;
+#pragma unroll 8
         for (int ch = g; ch < nchunk; ch += G) s += p[(size_t)ch * NHP * D];
       }
   red[threadIdx.x] = s;
