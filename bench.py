@@ -92,35 +92,62 @@ def parse():
                     help="also compute dL/dW in every backward (tables learned)")
     ap.add_argument("--per-head", action="store_true",
                     help="one set of tables per head (W is [H][L][P][d])")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 22)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="oracle sample length (default: sized for about 15 s of CPU work)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same step captured once in a HIP graph and replayed")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 1 GiB once (reference kernel for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(inp, w, n_tok):
-    """fp64 oracle, forward + backward, on head (0, 0)'s first n_tok tokens taken as one sequence."""
-    import numpy as np
+def cpu_baseline(inp, w, n_tok=None, target_s=15.0):
+    """fp64 oracle on head (0, 0)'s first n tokens taken as one sequence
+    (forward, plus backward for training workloads).
+
+    n is n_tok when given; otherwise a 2048-token probe sets n so that one
+    pass takes about target_s seconds (the causal oracle keeps a bank per
+    token and costs ~100x more per token than the non-causal one).  Samples
+    shorter than a second are repeated until a second has passed.  A token of
+    the metric carries all H heads, so the rate is scaled by 1/H: the whole
+    job would take H times the sample's time per token."""
     from oracle import race_oracle as orc
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    n = min(n_tok, w.N)
-    f64 = lambda t: t[0, 0, :n].to("cpu").double().numpy()
-    Q, K, V, dO = (f64(inp[k]) for k in ("Q", "K", "V", "dO"))
     Wn = inp["W"].double().numpy()
-    t0 = time.perf_counter()
-    if w.causal:
-        orc.causal_forward_head(Q, K, V, Wn, w.beta)
+    train = "bwd" in w.phases
+
+    def run(n):
+        f64 = lambda t: t[0, 0, :n].to("cpu").double().numpy()
+        Q, K, V = (f64(inp[k]) for k in ("Q", "K", "V"))
+        dO = f64(inp["dO"]) if train else None
+        t0 = time.perf_counter()
+        if w.causal:
+            orc.causal_forward_head(Q, K, V, Wn, w.beta)
+        else:
+            orc.forward_head(Q, K, V, Wn, w.beta)
+        if train:
+            orc.backward_head(Q, K, V, Wn, w.beta, dO, w.causal)
+        return time.perf_counter() - t0
+
+    if n_tok is None:
+        probe = min(w.N, 2048)
+        t_probe = run(probe)
+        n = min(w.N, 1 << 22, max(probe, int(probe * target_s / max(t_probe, 1e-6)) // 1024 * 1024))
     else:
-        orc.forward_head(Q, K, V, Wn, w.beta)
-    if "bwd" in w.phases:
-        orc.backward_head(Q, K, V, Wn, w.beta, dO, w.causal)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head (0,0), first {n} tokens as one sequence, fwd+bwd fp64 numpy, {dt:.1f} s"}
+        n = min(n_tok, w.N)
+    print(f"# oracle sample: {n} tokens of head (0,0)", file=sys.stderr, flush=True)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < 1.0:
+        dt += run(n)
+        reps += 1
+    ph = "fwd+bwd" if train else "fwd"
+    return {"value": n * reps / (dt * w.H), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head (0,0), first {n} tokens as one sequence, {ph} fp64 numpy, {reps} pass(es) "
+                      f"in {dt:.2f} s; rate divided by H = {w.H} heads per token"}
 
 
 def load_traffic(workload_name: str, kernel: str, launches_tokens: int):
@@ -247,11 +274,14 @@ def main():
     db = torch.zeros(1, dtype=torch.float32, device=dev)
     dW = torch.zeros_like(W) if args.dW else None
     torch.cuda.synchronize()
+    # forward-only workloads (the pages' inference-shaped runs) time the forward alone
+    train = "bwd" in w.phases
 
     def step():
         race.race_attn_fwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, O=O, state=st, workspace=wsf)
-        race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV,
-                           dbeta=db if args.dbeta else None, dW=dW, workspace=wsb)
+        if train:
+            race.race_attn_bwd(Q, K, V, W, w.beta, w.P, w.L, w.causal, dO, st, O=O, dQ=dQ, dK=dK, dV=dV,
+                               dbeta=db if args.dbeta else None, dW=dW, workspace=wsb)
 
     for _ in range(args.warmup):
         step()
@@ -303,13 +333,37 @@ def main():
         torch.cuda.synchronize()
     del src, dst
 
+    graph_ms = None
+    if args.graph:
+        # the same step captured once and replayed: the launch cost per step
+        # drops to one graph launch (the library enqueues kernels only)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        del g
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# timing the fp64 oracle on a CPU sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, w, args.cpu_sample_tokens)
 
+    if w.key == 4:
+        metric = "RACE layer fwd+bwd tokens/s at N=12M, H=4, d=128; % of HBM roofline"
+    else:
+        metric = f"RACE layer {'fwd+bwd' if train else 'fwd'} tokens/s, workload {w.name}; % of HBM roofline"
+    dist = {"iid": "iid N(0,1) Q, K, V, dO", "iid_over_sqrt_d": "iid N(0,1)/sqrt(d) Q, K, V",
+            "lognormal_norms": "rows with isotropic directions and log-uniform norms in [0.5, 2]; iid dO",
+            "clustered_keys": "K around 256 unit centroids plus 0.3 N(0,1) noise; iid Q, V, dO"}[w.dist]
     out = {
-        "metric": "RACE layer fwd+bwd tokens/s at N=12M, H=4, d=128; % of HBM roofline",
+        "metric": metric,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -320,19 +374,23 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded; iid N(0,1) Q, K, V, dO; Gaussian W)",
+        "data": f"synthetic (seeded; {dist}; Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "P": w.P, "L": w.L,
-                   "beta": w.beta, "causal": w.causal, "dbeta": bool(args.dbeta), "dW": bool(args.dW),
+                   "beta": w.beta, "causal": w.causal, "phases": "fwd+bwd" if train else "fwd",
+                   "dbeta": bool(args.dbeta), "dW": bool(args.dW),
                    "per_head_tables": bool(args.per_head), "global_batch": w.B,
                    "seq_len": w.N},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": dname, "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": avg_ms,
                      "device_copy_GBps_same_run": copy_gbps},
-        "step_hbm_frac": (11 * row_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_hbm_frac": ((11 if train else 4) * row_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms_per_launch": {k: v[1] / v[0] for k, v in kern.items()},
         "cpu_baseline": cpu,
     }
+    if graph_ms is not None:
+        out["graph_ms_per_step"] = graph_ms
+        out["graph_tokens_per_s"] = tokens / (graph_ms * 1e-3)
     fl = causal_flops(dname, w.L, w.P, w.d) if w.causal else None
     if fl:
         # the causal walks also sit far below the MFMA roofline: bf16 dense peak
