@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--per-head", action="store_true",
                     help="one set of tables per head (W is [H][L][P][d])")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
-                    help="oracle sample length (default: sized for about 15 s of CPU work)")
+                    help="oracle sample length (default: sized for about 20 s of CPU work)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same step captured once in a HIP graph and replayed")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -101,13 +101,14 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(inp, w, n_tok=None, target_s=15.0):
+def cpu_baseline(inp, w, n_tok=None, target_s=20.0):
     """fp64 oracle on head (0, 0)'s first n tokens taken as one sequence
     (forward, plus backward for training workloads).
 
-    n is n_tok when given; otherwise a 2048-token probe sets n so that one
-    pass takes about target_s seconds (the causal oracle keeps a bank per
-    token and costs ~100x more per token than the non-causal one).  Samples
+    n is n_tok when given; otherwise probes of 256, 1024, 4096, ... tokens
+    run until one takes an eighth of target_s, and n is scaled from it so that
+    one pass takes about target_s seconds (the causal oracle keeps a bank per
+    token and costs ~1000x more per token than the non-causal one).  Samples
     shorter than a second are repeated until a second has passed.  A token of
     the metric carries all H heads, so the rate is scaled by 1/H: the whole
     job would take H times the sample's time per token."""
@@ -134,9 +135,13 @@ def cpu_baseline(inp, w, n_tok=None, target_s=15.0):
         return time.perf_counter() - t0
 
     if n_tok is None:
-        probe = min(w.N, 2048)
+        cap = min(w.N, 1 << 22)
+        probe = min(cap, 256)
         t_probe = run(probe)
-        n = min(w.N, 1 << 22, max(probe, int(probe * target_s / max(t_probe, 1e-6)) // 1024 * 1024))
+        while t_probe < target_s / 8 and probe < cap:
+            probe = min(cap, 4 * probe)
+            t_probe = run(probe)
+        n = min(cap, max(probe, int(probe * target_s / max(t_probe, 1e-6)) // 256 * 256))
     else:
         n = min(n_tok, w.N)
     print(f"# oracle sample: {n} tokens of head (0,0)", file=sys.stderr, flush=True)
