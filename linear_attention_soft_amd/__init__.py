@@ -125,6 +125,24 @@ def _shape_of(x: torch.Tensor, W: torch.Tensor = None, L: int = None, P: int = N
     return race_shape(B, H, N, d, _dtype_code(x), per_head)
 
 
+def _like(ref: torch.Tensor, ref_name: str, **tensors):
+    """Every given token tensor must match ref's shape, dtype and device: the
+    library receives one shape record and would read or write past the end
+    of a smaller tensor."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{name} must have {ref_name}'s shape {tuple(ref.shape)}, dtype {ref.dtype} and "
+                             f"device {ref.device}; got {tuple(t.shape)}, {t.dtype}, {t.device}")
+
+
+def _same_device(ref: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device}; got {t.device}")
+
+
 def _dev(t: torch.Tensor, name: str) -> int:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -162,6 +180,8 @@ def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, work
     """O = RACE(Q, K, V; W, beta, P, L, causal).  Returns (O, state).  W is
     [L, P, d] (every head) or [H, L, P, d] (per head)."""
     shape = _shape_of(Q, W, L, P)
+    _like(Q, "Q", K=K, V=V, O=O)
+    _same_device(Q, W=W, state=state, workspace=workspace)
     if O is None:
         O = torch.empty_like(Q)
     sb = race_attn_state_bytes(shape, P, L, causal)
@@ -186,6 +206,8 @@ def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK
     (a new float32 tensor shaped like W) or a float32 device tensor of W's
     shape to write dL/dW into."""
     shape = _shape_of(Q, W, L, P)
+    _like(Q, "Q", K=K, V=V, dO=dO, O=O, dQ=dQ, dK=dK, dV=dV)
+    _same_device(Q, W=W, state=state, workspace=workspace)
     dQ = torch.empty_like(Q) if dQ is None else dQ
     dK = torch.empty_like(K) if dK is None else dK
     dV = torch.empty_like(V) if dV is None else dV
@@ -205,7 +227,7 @@ def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK
                                    None, None, None, ctypes.byref(shape), None, 0, None, 0, None))
     workspace = _buffer(wb, Q.device, workspace)
     _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
-                               int(L), int(causal), O.data_ptr() if O is not None else None, _dev(dO, "dO"),
+                               int(L), int(causal), _dev(O, "O") if O is not None else None, _dev(dO, "dO"),
                                _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
                                dbeta.data_ptr() if want_dbeta else None,
                                _dev(dW, "dW") if want_dW else None, ctypes.byref(shape),
@@ -238,9 +260,10 @@ def profile_report() -> dict:
 
 def race_softbucket_debug(X, W, beta, P, L, stream=None):
     """Soft assignments phi^(l)(X) as float32 [B, H, N, L, 2^P] (test export)."""
+    shape = _shape_of(X, W, L, P)
+    _same_device(X, W=W)
     B, H, N, d = X.shape
     out = torch.empty((B, H, N, L, 1 << P), dtype=torch.float32, device=X.device)
-    shape = _shape_of(X, W, L, P)
     _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
                                        ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
     return out
@@ -254,6 +277,8 @@ def race_attn_decode_prefill(K, V, W, beta, P, L, state=None, workspace=None, st
     """Decode state (float32 bank: content [B*H][LRP][d] then mass [B*H][LRP])
     after the prompt K, V [B, H, N, d].  Returns the state tensor."""
     shape = _shape_of(K, W, L, P)
+    _like(K, "K", V=V)
+    _same_device(K, W=W, state=state, workspace=workspace)
     nb = race_attn_decode_state_bytes(shape, P, L)
     if nb == 0:
         _check(lib().race_attn_decode_prefill(None, None, None, float(beta), int(P), int(L), ctypes.byref(shape),
@@ -272,6 +297,8 @@ def race_attn_decode(Q, K, V, W, beta, P, L, state, O=None, stream=None):
     """Decode the new tokens Q, K, V [B, H, n, d] in order from state (updated
     in place; a zeroed state is the empty prefix).  Returns O."""
     shape = _shape_of(Q, W, L, P)
+    _like(Q, "Q", K=K, V=V, O=O)
+    _same_device(Q, W=W, state=state)
     O = torch.empty_like(Q) if O is None else O
     _check(lib().race_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
                                   int(L), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"), _bytes(state),

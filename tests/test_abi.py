@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "race_attn.h")
@@ -181,3 +182,28 @@ def test_plain_c_client(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout, r.stderr)
+
+
+def test_binding_rejects_mismatched_token_tensors():
+    """The library takes one shape record for every token tensor, so the
+    binding refuses tensors that differ from Q in shape, dtype or device
+    before anything is launched (a shorter K would otherwise be read past
+    its end)."""
+    Q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    W = torch.zeros(2, 3, 64)
+    short = torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16)
+    wrong_dtype = torch.zeros(1, 2, 64, 64)
+    with pytest.raises(ValueError, match="K must have Q's shape"):
+        race.race_attn_fwd(Q, short, Q, W, 1.0, 3, 2)
+    with pytest.raises(ValueError, match="V must have Q's shape"):
+        race.race_attn_fwd(Q, Q, wrong_dtype, W, 1.0, 3, 2)
+    with pytest.raises(ValueError, match="O must have Q's shape"):
+        race.race_attn_fwd(Q, Q, Q, W, 1.0, 3, 2, O=short)
+    with pytest.raises(ValueError, match="dO must have Q's shape"):
+        race.race_attn_bwd(Q, Q, Q, W, 1.0, 3, 2, False, short, None)
+    with pytest.raises(ValueError, match="dK must have Q's shape"):
+        race.race_attn_bwd(Q, Q, Q, W, 1.0, 3, 2, False, Q, None, dK=short)
+    with pytest.raises(ValueError, match="V must have K's shape"):
+        race.race_attn_decode_prefill(Q, short, W, 1.0, 3, 2)
+    with pytest.raises(ValueError, match="O must have Q's shape"):
+        race.race_attn_decode(Q, Q, Q, W, 1.0, 3, 2, None, O=wrong_dtype)
