@@ -51,6 +51,22 @@ struct NCArgs {
 
 constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
 
+// Token tiles of one workgroup of the non-causal kernels.  Interleaved: tiles
+// chunk, chunk + nchunk, chunk + 2 nchunk, ... of the sequence, so the whole
+// grid sweeps each tensor front to back together and neighbouring
+// workgroups read neighbouring rows; contiguous: one run of chunk_tokens
+// tokens per workgroup.  Either way every tile is taken by one workgroup and
+// the partial banks are summed in workgroup order.
+constexpr bool kInterleaveTiles = true;
+struct TileSpan {
+  int64_t begin, end, step;   // first tile's first token, token bound, stride between tiles
+};
+__device__ __forceinline__ TileSpan tile_span(const NCArgs& a, int chunk) {
+  if (kInterleaveTiles) return {(int64_t)chunk * TT, a.N, (int64_t)a.nchunk * TT};
+  const int64_t b = (int64_t)chunk * a.chunk_tokens;
+  return {b, min(a.N, b + a.chunk_tokens), (int64_t)TT};
+}
+
 // Row padding (elements) of LDS staging tiles: keeps 16-byte (bf16) and
 // 32-byte (float32) fragment rows aligned and shifts rows across banks.
 template <typename T> struct Pad { static constexpr int v = 8; };
@@ -255,8 +271,8 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
 
   const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
   const T* Y = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
-  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
-  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const TileSpan span = tile_span(a, chunk);
+  const int64_t t_begin = span.begin, t_end = span.end, step = span.step;
   const float beta2 = 2.f * a.beta;
 
   f32x16 acc[NTW];
@@ -287,12 +303,12 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   };
   load_x(t_begin);
   load_y(t_begin);
-  for (int64_t base = t_begin; base < t_end; base += TT) {
+  for (int64_t base = t_begin; base < t_end; base += step) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, xa, pre);
-    load_x(base + TT);
+    load_x(base + step);
     soft_assign<G>(pre, beta2, a.L, u, phi);
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
       }
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
     }
-    load_y(base + TT);
+    load_y(base + step);
     if (a.tok_extra && h == 0) hsv[tl] = valid ? a.tok_extra[(size_t)bh * a.N + tok] : 0.f;
     __syncthreads();
     reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, a.tok_extra ? hsv : nullptr, acc);
@@ -340,8 +356,8 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
 
   const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
   T* O = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
-  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
-  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const TileSpan span = tile_span(a, chunk);
+  const int64_t t_begin = span.begin, t_end = span.end, step = span.step;
   const float beta2 = 2.f * a.beta;
 
   const int64_t last = t_end - 1;
@@ -365,15 +381,15 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   int64_t base = t_begin + 32 * w;
   load_row_frags_nb<T, G>(X + min(base + n, last) * G::D, xa);
   while (base < t_end) {
-    load_row_frags_nb<T, G>(X + min(base + TT + n, last) * G::D, xb);
+    load_row_frags_nb<T, G>(X + min(base + step + n, last) * G::D, xb);
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this tile's work
     tile(xa, base);
-    base += TT;
+    base += step;
     if (base >= t_end) break;
-    load_row_frags_nb<T, G>(X + min(base + TT + n, last) * G::D, xa);
+    load_row_frags_nb<T, G>(X + min(base + step + n, last) * G::D, xa);
     __builtin_amdgcn_sched_barrier(0);
     tile(xb, base);
-    base += TT;
+    base += step;
   }
 }
 
@@ -415,8 +431,8 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
   const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
   const T* dO = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
   T* dQ = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
-  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
-  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const TileSpan span = tile_span(a, chunk);
+  const int64_t t_begin = span.begin, t_end = span.end, step = span.step;
   const float beta2 = 2.f * a.beta;
 
   f32x16 racc[NTW];
@@ -504,22 +520,22 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
   }
   while (base < t_end) {
     {
-      const int64_t r = min(base + TT + tl, last);
+      const int64_t r = min(base + step + tl, last);
       load_row_frags_nb<T, G>(X + r * G::D, xb);
       load_row_frags_nb<T, G>(dO + r * G::D, yb);
     }
     __builtin_amdgcn_sched_barrier(0);
     tile(xa, ya, base);
-    base += TT;
+    base += step;
     if (base >= t_end) break;
     {
-      const int64_t r = min(base + TT + tl, last);
+      const int64_t r = min(base + step + tl, last);
       load_row_frags_nb<T, G>(X + r * G::D, xa);
       load_row_frags_nb<T, G>(dO + r * G::D, ya);
     }
     __builtin_amdgcn_sched_barrier(0);
     tile(xb, yb, base);
-    base += TT;
+    base += step;
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), racc);
   if (a.dbeta_part) {
@@ -556,8 +572,8 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   const T* Vx = static_cast<const T*>(a.Y) + (size_t)bh * a.N * G::D;
   T* dV = static_cast<T*>(a.out0) + (size_t)bh * a.N * G::D;
   T* dK = static_cast<T*>(a.out1) + (size_t)bh * a.N * G::D;
-  const int64_t t_begin = (int64_t)chunk * a.chunk_tokens;
-  const int64_t t_end = min(a.N, t_begin + a.chunk_tokens);
+  const TileSpan span = tile_span(a, chunk);
+  const int64_t t_begin = span.begin, t_end = span.end, step = span.step;
   const float beta2 = 2.f * a.beta;
 
   const int64_t last = t_end - 1;
@@ -613,22 +629,22 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   }
   while (base < t_end) {
     {
-      const int64_t r = min(base + TT + n, last);
+      const int64_t r = min(base + step + n, last);
       load_row_frags_nb<T, G>(Kx + r * G::D, xb);
       load_row_frags_nb<T, G>(Vx + r * G::D, yb);
     }
     __builtin_amdgcn_sched_barrier(0);
     tile(xa, ya, base);
-    base += TT;
+    base += step;
     if (base >= t_end) break;
     {
-      const int64_t r = min(base + TT + n, last);
+      const int64_t r = min(base + step + n, last);
       load_row_frags_nb<T, G>(Kx + r * G::D, xa);
       load_row_frags_nb<T, G>(Vx + r * G::D, ya);
     }
     __builtin_amdgcn_sched_barrier(0);
     tile(xb, yb, base);
-    base += TT;
+    base += step;
   }
   if (a.dbeta_part) {
     bsum = wave_sum(bsum);
