@@ -51,18 +51,25 @@ struct NCArgs {
 
 constexpr int TT = 128;     // tokens per workgroup iteration (4 waves x 32)
 
-// Token tiles of one workgroup of the non-causal kernels.  Interleaved: tiles
-// chunk, chunk + nchunk, chunk + 2 nchunk, ... of the sequence, so the whole
-// grid sweeps each tensor front to back together and neighbouring
-// workgroups read neighbouring rows; contiguous: one run of chunk_tokens
-// tokens per workgroup.  Either way every tile is taken by one workgroup and
-// the partial banks are summed in workgroup order.
+// Token tiles of one workgroup of the non-causal kernels.  Interleaved: the
+// grid sweeps each tensor front to back together, one tile per workgroup per
+// sweep (workgroup slot c takes tiles c, c + nchunk, c + 2 nchunk, ...), so
+// neighbouring workgroups read neighbouring rows.  Workgroups are dealt to
+// the 8 XCDs round-robin by linear id; with nchunk a multiple of 8 the slots
+// are ordered so that each XCD's workgroups take one contiguous eighth of
+// every sweep.  Contiguous: one run of chunk_tokens tokens per workgroup.
+// Either way every tile is taken by one workgroup and the partial banks are
+// summed in workgroup order.
 constexpr bool kInterleaveTiles = true;
 struct TileSpan {
   int64_t begin, end, step;   // first tile's first token, token bound, stride between tiles
 };
 __device__ __forceinline__ TileSpan tile_span(const NCArgs& a, int chunk) {
-  if (kInterleaveTiles) return {(int64_t)chunk * TT, a.N, (int64_t)a.nchunk * TT};
+  if (kInterleaveTiles) {
+    int64_t c = chunk;
+    if (a.nchunk % 8 == 0) c = (int64_t)(chunk % 8) * (a.nchunk / 8) + chunk / 8;
+    return {c * TT, a.N, (int64_t)a.nchunk * TT};
+  }
   const int64_t b = (int64_t)chunk * a.chunk_tokens;
   return {b, min(a.N, b + a.chunk_tokens), (int64_t)TT};
 }
