@@ -252,8 +252,9 @@ def bench_decode(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              f"(the layer shards by heads or by sequence segments; see the design notes)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (across GPUs the "
+              f"layer would shard by heads, or by sequence segments with one all-reduce of the banks)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import linear_attention_soft_amd as race
