@@ -30,13 +30,16 @@
 
 namespace race {
 
-// Segments: about 512 (segment, batch x head) units over the whole problem,
-// 64-token multiples.  Against 1024: the 1M-token, 4-head step 13.1 -> 12.9 ms
-// (a shorter scan, fewer bank loads), the 64 x 1K-token step 0.259 -> 0.224
-// ms (segments of 128 instead of 64 tokens); 256 or 2048 were slower.
+// Segments, in 64-token multiples: about 256 (segment, batch x head) units
+// over the whole problem, one per CU (a walk workgroup fills a CU), when each
+// segment still gets at least 64 tiles; otherwise about 512.  Measured in one
+// process on one set of buffers: the 1M-token, 4-head step 13.25 -> 13.09 ms
+// with 256 units against 512 (768: 13.29); the 64 x 1K-token step keeps 512
+// units of 128 tokens (0.221 ms; 256 units: 0.260; 1024 units: 0.259).
 inline void causal_segmentation(int64_t N, int64_t BH, int* nseg, int64_t* seg_tokens) {
-  int64_t want = (512 + BH - 1) / BH;
   const int64_t tiles = (N + 63) / 64;
+  int64_t want = (256 + BH - 1) / BH;
+  if (tiles / want < 64) want = (512 + BH - 1) / BH;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int64_t per = (tiles + want - 1) / want;
