@@ -19,7 +19,7 @@ struct DWArgs {
   const float* dpre1;      // dL/dPre of the key rows [BH][N][NHP]
   float* part;             // [2][BH][nchunk][NHP][d]
   int64_t N;
-  int64_t chunk_tokens;    // tokens per workgroup
+  int64_t chunk_tokens;    // unused: workgroups take interleaved tiles (below)
   int nchunk;
 };
 
@@ -30,7 +30,10 @@ struct alignas(sizeof(T) * C) ColsT {
   T v[C];
 };
 
-// grid (nchunk, BH, 2 sides), 256 threads.  Lane owns columns
+// grid (nchunk, BH, 2 sides), 256 threads.  Workgroup slot c takes tiles
+// c, c + nchunk, c + 2 nchunk, ... (slots ordered so that each XCD takes one
+// contiguous eighth of every sweep when nchunk is a multiple of 8), as the
+// other streaming kernels do.  Lane owns columns
 // [C * lane, C * lane + C) of d; wave w takes rows w, w + 4, ... of each tile;
 // the tile's dPre rows are staged in LDS and read as broadcasts.  The next
 // tile's loads are in flight while the current tile is accumulated.
@@ -50,10 +53,12 @@ __global__ __launch_bounds__(256) void race_dw_partial(DWArgs a) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const T* X = static_cast<const T*>(side ? a.X1 : a.X0) + (size_t)bh * a.N * D;
   const float* dp = (side ? a.dpre1 : a.dpre0) + (size_t)bh * a.N * NHP;
-  const int64_t t0 = (int64_t)chunk * a.chunk_tokens;
-  const int64_t t1 = min(a.N, t0 + a.chunk_tokens);
-  const int ntiles = (int)((t1 - t0 + DW_TT - 1) / DW_TT);
-  const int64_t last = t1 - 1;
+  int64_t slot = chunk;
+  if (a.nchunk % 8 == 0) slot = (int64_t)(chunk % 8) * (a.nchunk / 8) + chunk / 8;
+  const int64_t t0 = slot * DW_TT, tstep = (int64_t)a.nchunk * DW_TT;
+  const int64_t total_tiles = (a.N + DW_TT - 1) / DW_TT;   // >= nchunk > slot
+  const int ntiles = (int)((total_tiles - slot + a.nchunk - 1) / a.nchunk);
+  const int64_t last = a.N - 1;
 
   float acc[NHP][C];
 #pragma unroll
@@ -63,9 +68,10 @@ __global__ __launch_bounds__(256) void race_dw_partial(DWArgs a) {
 
   Cols xa[TPW], xc[TPW];
   float4 pa[NPR];
-  // loads of tile k, rows clamped to the chunk (rows past it get dPre = 0)
+  // loads of the workgroup's tile k, rows clamped to the sequence (rows past
+  // it get dPre = 0)
   auto load_tile = [&](int k) {
-    const int64_t base = t0 + (int64_t)k * DW_TT;
+    const int64_t base = t0 + (int64_t)k * tstep;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int64_t r = min(base + 4 * j + w, last);
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256) void race_dw_partial(DWArgs a) {
   load_tile(0);
   for (int k = 0; k < ntiles; ++k) {
     const int bb = k & 1;
-    const int64_t base = t0 + (int64_t)k * DW_TT;
+    const int64_t base = t0 + (int64_t)k * tstep;
 #pragma unroll
     for (int i = 0; i < NPR; ++i) {
       const int idx = (int)threadIdx.x + 256 * i;

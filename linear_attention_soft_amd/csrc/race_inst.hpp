@@ -9,6 +9,10 @@
 
 namespace race {
 
+// race_dw_partial takes the non-causal chunking's workgroup count, which never
+// exceeds the number of 128-token tiles: each of its workgroups gets a tile.
+static_assert(DW_TT == TT, "dW tiles are the non-causal tiles");
+
 // Soft assignments of token rows written out as float32 [BH][N][L][R]
 // (a test export of the fused front end every kernel uses).
 template <typename T, class G>
