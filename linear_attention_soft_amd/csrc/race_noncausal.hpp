@@ -449,14 +449,22 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
   const int tl = 32 * w + n;
   const int64_t last = t_end - 1;
   float bsum = 0.f;
-  auto tile = [&](const frag (&cx)[G::KD], const frag (&yy)[G::KD], int64_t base) {
+  // one register set per operand: the next tile's Q rows are loaded as soon
+  // as this tile's projection has consumed them, its dO rows as soon as this
+  // tile's are staged in LDS; both loads stay in flight through the rest of
+  // the tile
+  frag xa[G::KD], ya[G::KD];
+  auto load_x = [&](int64_t b) { load_row_frags_nb<T, G>(X + min(b + tl, last) * G::D, xa); };
+  auto load_y = [&](int64_t b) { load_row_frags_nb<T, G>(dO + min(b + tl, last) * G::D, ya); };
+  auto tile = [&](int64_t base) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
     frag cy[G::KD];
 #pragma unroll
-    for (int q = 0; q < G::KD; ++q) cy[q] = valid ? yy[q] : E::zero();
+    for (int q = 0; q < G::KD; ++q) cy[q] = valid ? ya[q] : E::zero();
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
-    project<T, G>(Wf, cx, pre);
+    project<T, G>(Wf, xa, pre);
+    load_x(base + step);
     soft_assign<G>(pre, beta2, a.L, u, phi);
     if (!valid) {
 #pragma unroll
@@ -513,37 +521,15 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
 #pragma unroll
     for (int q = 0; q < G::KD; ++q)
       *reinterpret_cast<frag*>(Bs + tl * BSP + 16 * q + 8 * h) = cy[q];
+    load_y(base + step);
     if (h == 0) hs[tl] = valid ? -hd * inv : 0.f;
     __syncthreads();
     reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, hs, racc);
     __syncthreads();
   };
-  frag xa[G::KD], ya[G::KD], xb[G::KD], yb[G::KD];
-  int64_t base = t_begin;
-  {
-    const int64_t r = min(base + tl, last);
-    load_row_frags_nb<T, G>(X + r * G::D, xa);
-    load_row_frags_nb<T, G>(dO + r * G::D, ya);
-  }
-  while (base < t_end) {
-    {
-      const int64_t r = min(base + step + tl, last);
-      load_row_frags_nb<T, G>(X + r * G::D, xb);
-      load_row_frags_nb<T, G>(dO + r * G::D, yb);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    tile(xa, ya, base);
-    base += step;
-    if (base >= t_end) break;
-    {
-      const int64_t r = min(base + step + tl, last);
-      load_row_frags_nb<T, G>(X + r * G::D, xa);
-      load_row_frags_nb<T, G>(dO + r * G::D, ya);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    tile(xb, yb, base);
-    base += step;
-  }
+  load_x(t_begin);
+  load_y(t_begin);
+  for (int64_t base = t_begin; base < t_end; base += step) tile(base);
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), racc);
   if (a.dbeta_part) {
     bsum = wave_sum(bsum);
