@@ -150,9 +150,14 @@ def cpu_baseline(inp, w, n_tok=None, target_s=20.0):
         dt += run(n)
         reps += 1
     ph = "fwd+bwd" if train else "fwd"
+    whole = n >= w.N and w.B * w.H == 1
     return {"value": n * reps / (dt * w.H), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head (0,0), first {n} tokens as one sequence, {ph} fp64 numpy, {reps} pass(es) "
-                      f"in {dt:.2f} s; rate divided by H = {w.H} heads per token"}
+            "extrapolated": not whole,
+            "sample": f"head (0,0), first {n} of {w.N} tokens as one sequence, {ph} fp64 numpy, {reps} pass(es) "
+                      f"in {dt:.2f} s; value extrapolated to the whole workload ({w.B} x {w.H} sequences of "
+                      f"{w.N} tokens) as sample tokens / (H = {w.H} heads per token x sample time)"
+                      if not whole else
+                      f"the whole workload, {ph} fp64 numpy, {reps} pass(es) in {dt:.2f} s"}
 
 
 def load_traffic(workload_name: str, kernel: str, launches_tokens: int):

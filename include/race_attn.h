@@ -75,16 +75,29 @@ typedef struct {
  * Returns 0 for invalid arguments. */
 size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal);
 
-/* Bytes of scratch workspace for the forward (is_bwd = 0), the backward
- * (is_bwd = 1) or the backward with the table gradient dW (is_bwd = 2:
- * adds float32 dL/dPre of every token of both sides, 2 * B*H*N *
- * (LRP / 2^max(P,3)) * max(P,3) floats, and one partial per workgroup).
- * Returns 0 for invalid arguments. */
+/* Workspace phases for race_attn_workspace_bytes: the forward, the
+ * backward, the backward with the table gradient dW; RACE_WS_NO_STATE is
+ * OR-ed into a backward phase when race_attn_bwd will get no state (it then
+ * rebuilds the state inside the workspace). */
+enum {
+  RACE_WS_FWD = 0,
+  RACE_WS_BWD = 1,
+  RACE_WS_BWD_DW = 2,
+  RACE_WS_NO_STATE = 4
+};
+
+/* Bytes of scratch workspace for the phase is_bwd: RACE_WS_FWD (0),
+ * RACE_WS_BWD (1) or RACE_WS_BWD_DW (2: adds float32 dL/dPre of every token
+ * of both sides, 2 * B*H*N * (LRP / 2^max(P,3)) * max(P,3) floats, and one
+ * partial per workgroup), optionally with RACE_WS_NO_STATE (adds room for
+ * the rebuilt state: the bank, or for the causal layer the segment banks
+ * and Den).  Returns 0 for invalid arguments. */
 size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd);
 
 /* Forward pass: O = RACE(Q, K, V; W, beta, P, L, causal).
  * state (may be NULL when state_bytes is 0) receives the statistics the
- * backward pass needs; workspace must hold race_attn_workspace_bytes(..., 0). */
+ * backward pass needs; workspace must hold race_attn_workspace_bytes(...,
+ * RACE_WS_FWD).  state and O must not overlap each other or the workspace. */
 race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W,
                           float beta, int P, int L, int causal, void* O,
                           const race_shape* shape, void* state, size_t state_bytes,
@@ -97,7 +110,12 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
  * corner assignments make hashing differentiable"), one beta for every
  * batch row and head, so dbeta sums over both sides, every head, table and
  * token; it is summed in a fixed order (same bits on every run).
- * state must be the one written by race_attn_fwd on the same inputs.  O is
+ * state is the one written by race_attn_fwd on the same inputs, or NULL:
+ * the backward then rebuilds it from K, V (non-causal: one more read of K
+ * and V; causal: the segment sums and a forward walk over Q, K, V that
+ * writes Den but no O) in the workspace, which must then be sized with
+ * RACE_WS_NO_STATE.  A given state must not overlap an output, the
+ * workspace, dbeta or dW.  O is
  * the forward output or NULL: the non-causal backward never reads it; the
  * causal backward takes h = -(dO . O) / Den from it elementwise when given,
  * and rebuilds Den O with one more walk over Q, K, V when it is NULL.
@@ -106,8 +124,10 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
  * row x are W^(l) x (same frame), so each table's gradient is the sum over
  * the query and key rows of dL/dPre^(l) x^T, over every batch row and head
  * that uses the table; summed in a fixed order (same bits on every run).
- * workspace must hold race_attn_workspace_bytes(..., 1), or (..., 2) when
- * dW is requested; dW must not overlap W or any other buffer. */
+ * workspace must hold race_attn_workspace_bytes(..., RACE_WS_BWD), or
+ * (..., RACE_WS_BWD_DW) when dW is requested, with RACE_WS_NO_STATE OR-ed in
+ * when state is NULL; dW and dbeta must not overlap W, the workspace or any
+ * other buffer. */
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W,
                           float beta, int P, int L, int causal, const void* O,
                           const void* dO, void* dQ, void* dK, void* dV, float* dbeta,
@@ -150,6 +170,35 @@ race_status race_attn_decode(const void* Q, const void* K, const void* V, const 
 race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L,
                                   const race_shape* shape, float* phi_out,
                                   race_stream_t stream);
+
+/* Test export of the bucket banks (slides frame "Each bucket stores mass and
+ * a weighted value sum"; the causal banks follow frame "Causality is a
+ * prefix update of the same statistics").  The number of banks per (batch,
+ * head): 1 for the non-causal layer, one per sequence segment for the causal
+ * one; *seg_tokens (if not NULL) receives the segment length (segment s
+ * holds tokens [s * seg_tokens, min(N, (s + 1) * seg_tokens))).  Returns 0
+ * for invalid or unsupported arguments. */
+int race_bucket_stats_segments(const race_shape* shape, int P, int L, int causal, int64_t* seg_tokens);
+
+/* Copies banks that race_attn_fwd left in state and race_attn_bwd left in
+ * its workspace (the same shape, P, L and causal; a workspace sized for the
+ * backward, used by no call since) into float32 arrays with S banks per
+ * (batch, head) (S from race_bucket_stats_segments), tables l < L and
+ * corners r < 2^P in the corner order above:
+ *   content  [B*H][S][L][2^P][d]   mass  [B*H][S][L][2^P]
+ *   dcontent [B*H][S][L][2^P][d]   dmass [B*H][S][L][2^P]
+ * Non-causal: content / mass over all keys, content = sum_j phi(K_j) V_j^T;
+ * dcontent = sum_t phi(Q_t) g_t^T and dmass = sum_t phi(Q_t) h_t over all
+ * queries, with g_t = dO_t / Den_t and h_t = -(dO_t . O_t) / Den_t.  Causal:
+ * bank s holds the keys before segment s (content, mass) and the queries
+ * after segment s (dcontent, dmass).  Any output may be NULL; state may be
+ * NULL when content and mass are, bwd_workspace when dcontent and dmass
+ * are.  Device pointers; outputs 4-byte aligned, overlapping nothing else. */
+race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int causal,
+                                    const void* state, size_t state_bytes,
+                                    const void* bwd_workspace, size_t bwd_workspace_bytes,
+                                    float* content, float* mass, float* dcontent, float* dmass,
+                                    race_stream_t stream);
 
 /* Kernel timing for profiling tools.  While enabled, every kernel that the
  * calls above launch is bracketed by two HIP events recorded on the same

@@ -15,17 +15,23 @@ import torch
 __all__ = [
     "RaceError", "lib", "library_path", "race_attn_fwd", "race_attn_bwd", "race_softbucket_debug",
     "race_attn_state_bytes", "race_attn_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode",
-    "race_attn_decode_state_bytes", "EXPORTED_SYMBOLS",
+    "race_attn_decode_state_bytes", "race_bucket_stats_segments",
+    "race_bucket_stats_debug", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "librace_attn.so")
+# RACE_ATTN_LIBRARY selects another build of the same library (the host
+# sanitizer build of the CPU tests); by default the in-place build is loaded.
+library_path = os.environ.get("RACE_ATTN_LIBRARY") or os.path.join(_PKG, "librace_attn.so")
 
 RACE_F32, RACE_BF16 = 0, 1
+RACE_WS_FWD, RACE_WS_BWD, RACE_WS_BWD_DW, RACE_WS_NO_STATE = 0, 1, 2, 4
 EXPORTED_SYMBOLS = ("race_attn_fwd", "race_attn_bwd", "race_attn_state_bytes", "race_attn_workspace_bytes",
                     "race_softbucket_debug", "race_status_string", "race_last_error", "race_profile_enable",
                     "race_profile_reset", "race_profile_report", "race_attn_decode_state_bytes",
-                    "race_attn_decode_prefill_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode")
+                    "race_attn_decode_prefill_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode",
+                    "race_bucket_stats_segments",
+                    "race_bucket_stats_debug")
 
 
 class RaceError(RuntimeError):
@@ -82,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.race_attn_decode_prefill.restype = i32
         L.race_attn_decode.argtypes = [vp, vp, vp, vp, f32, i32, i32, vp, sp, vp, sz, vp]
         L.race_attn_decode.restype = i32
+        L.race_bucket_stats_segments.argtypes = [sp, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.race_bucket_stats_segments.restype = i32
+        L.race_bucket_stats_debug.argtypes = [sp, i32, i32, i32, vp, sz, vp, sz, vp, vp, vp, vp, vp]
+        L.race_bucket_stats_debug.restype = i32
         _LIB = L
     return _LIB
 
@@ -151,6 +161,18 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _torch_stream(stream, device) -> torch.cuda.Stream:
+    """The launch stream as a torch stream: None is the current stream of
+    device; a raw hipStream_t (int) is wrapped without taking ownership."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    if hasattr(stream, "cuda_stream"):
+        return torch.cuda.ExternalStream(stream.cuda_stream, device=device)
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -171,9 +193,20 @@ def _bytes(t):
 
 
 def _buffer(nbytes: int, device, given=None):
+    """Caller's buffer, or a new one.  New buffers are allocated while the
+    launch stream is current (see _on), so the caching allocator hands their
+    memory to no other stream's allocation before the kernels that use it
+    have finished."""
     if given is not None:
         return given
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _on(stream, device):
+    """Context in which the binding allocates the buffers of one call: the
+    launch stream is current, so workspaces freed on return are reused only
+    by later work on that stream."""
+    return torch.cuda.stream(_torch_stream(stream, device))
 
 
 def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, workspace=None, stream=None):
@@ -182,19 +215,19 @@ def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, work
     shape = _shape_of(Q, W, L, P)
     _like(Q, "Q", K=K, V=V, O=O)
     _same_device(Q, W=W, state=state, workspace=workspace)
-    if O is None:
-        O = torch.empty_like(Q)
     sb = race_attn_state_bytes(shape, P, L, causal)
-    wb = race_attn_workspace_bytes(shape, P, L, causal, False)
+    wb = race_attn_workspace_bytes(shape, P, L, causal, RACE_WS_FWD)
     if sb == 0 or wb == 0:
         # surface the library's own diagnosis
         _check(lib().race_attn_fwd(None, None, None, None, float(beta), P, L, int(causal), None,
                                    ctypes.byref(shape), None, 0, None, 0, None))
-    state = _buffer(sb, Q.device, state)
-    workspace = _buffer(wb, Q.device, workspace)
-    _check(lib().race_attn_fwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
-                               int(L), int(causal), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"),
-                               _bytes(state), _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
+    with _on(stream, Q.device):
+        O = torch.empty_like(Q) if O is None else O
+        state = _buffer(sb, Q.device, state)
+        workspace = _buffer(wb, Q.device, workspace)
+        _check(lib().race_attn_fwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                   int(L), int(causal), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"),
+                                   _bytes(state), _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
     return O, state
 
 
@@ -204,35 +237,40 @@ def race_attn_bwd(Q, K, V, W, beta, P, L, causal, dO, state, O=None, dQ=None, dK
     dbeta when dbeta is True (a new float32 tensor of one element) or a
     float32 device tensor to write dL/dbeta into, then by dW when dW is True
     (a new float32 tensor shaped like W) or a float32 device tensor of W's
-    shape to write dL/dW into."""
+    shape to write dL/dW into.  state is race_attn_fwd's state, or None: the
+    library then rebuilds it inside the workspace."""
     shape = _shape_of(Q, W, L, P)
     _like(Q, "Q", K=K, V=V, dO=dO, O=O, dQ=dQ, dK=dK, dV=dV)
     _same_device(Q, W=W, state=state, workspace=workspace)
-    dQ = torch.empty_like(Q) if dQ is None else dQ
-    dK = torch.empty_like(K) if dK is None else dK
-    dV = torch.empty_like(V) if dV is None else dV
     want_dbeta = dbeta is not None and dbeta is not False
-    if dbeta is True:
-        dbeta = torch.zeros(1, dtype=torch.float32, device=Q.device)
-    if want_dbeta and (dbeta.dtype != torch.float32 or not dbeta.is_cuda or dbeta.numel() < 1):
+    if want_dbeta and dbeta is not True and (dbeta.dtype != torch.float32 or not dbeta.is_cuda or
+                                             dbeta.numel() < 1):
         raise ValueError("dbeta must be a float32 device tensor with at least one element")
     want_dW = dW is not None and dW is not False
-    if dW is True:
-        dW = torch.empty_like(W)
-    if want_dW and (dW.dtype != torch.float32 or not dW.is_cuda or dW.shape != W.shape):
+    if want_dW and dW is not True and (dW.dtype != torch.float32 or not dW.is_cuda or dW.shape != W.shape):
         raise ValueError("dW must be a float32 device tensor shaped like W")
-    wb = race_attn_workspace_bytes(shape, P, L, causal, 2 if want_dW else 1)
+    phase = (RACE_WS_BWD_DW if want_dW else RACE_WS_BWD) | (RACE_WS_NO_STATE if state is None else 0)
+    wb = race_attn_workspace_bytes(shape, P, L, causal, phase)
     if wb == 0:
         _check(lib().race_attn_bwd(None, None, None, None, float(beta), P, L, int(causal), None, None, None, None,
                                    None, None, None, ctypes.byref(shape), None, 0, None, 0, None))
-    workspace = _buffer(wb, Q.device, workspace)
-    _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
-                               int(L), int(causal), _dev(O, "O") if O is not None else None, _dev(dO, "dO"),
-                               _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
-                               dbeta.data_ptr() if want_dbeta else None,
-                               _dev(dW, "dW") if want_dW else None, ctypes.byref(shape),
-                               _dev(state, "state"), _bytes(state), _dev(workspace, "workspace"),
-                               _bytes(workspace), _stream(stream)))
+    with _on(stream, Q.device):
+        dQ = torch.empty_like(Q) if dQ is None else dQ
+        dK = torch.empty_like(K) if dK is None else dK
+        dV = torch.empty_like(V) if dV is None else dV
+        if dbeta is True:
+            dbeta = torch.zeros(1, dtype=torch.float32, device=Q.device)
+        if dW is True:
+            dW = torch.empty_like(W)
+        workspace = _buffer(wb, Q.device, workspace)
+        _check(lib().race_attn_bwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                   int(L), int(causal), _dev(O, "O") if O is not None else None, _dev(dO, "dO"),
+                                   _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
+                                   dbeta.data_ptr() if want_dbeta else None,
+                                   _dev(dW, "dW") if want_dW else None, ctypes.byref(shape),
+                                   _dev(state, "state") if state is not None else None,
+                                   _bytes(state), _dev(workspace, "workspace"),
+                                   _bytes(workspace), _stream(stream)))
     return (dQ, dK, dV) + ((dbeta,) if want_dbeta else ()) + ((dW,) if want_dW else ())
 
 
@@ -263,10 +301,43 @@ def race_softbucket_debug(X, W, beta, P, L, stream=None):
     shape = _shape_of(X, W, L, P)
     _same_device(X, W=W)
     B, H, N, d = X.shape
-    out = torch.empty((B, H, N, L, 1 << P), dtype=torch.float32, device=X.device)
-    _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
-                                       ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
+    with _on(stream, X.device):
+        out = torch.empty((B, H, N, L, 1 << P), dtype=torch.float32, device=X.device)
+        _check(lib().race_softbucket_debug(_dev(X, "X"), _dev(W, "W"), float(beta), int(P), int(L),
+                                           ctypes.byref(shape), _dev(out, "phi"), _stream(stream)))
     return out
+
+
+def race_bucket_stats_segments(shape: race_shape, P: int, L: int, causal: bool):
+    """(banks per (batch, head), tokens per segment) of the bank export."""
+    seg = ctypes.c_int64(0)
+    n = lib().race_bucket_stats_segments(ctypes.byref(shape), int(P), int(L), int(causal), ctypes.byref(seg))
+    if n == 0:
+        raise ValueError("invalid or unsupported arguments")
+    return int(n), int(seg.value)
+
+
+def race_bucket_stats_debug(Q, W, P, L, causal, state=None, workspace=None, stream=None):
+    """Banks left by race_attn_fwd in state and by race_attn_bwd in its
+    workspace (test export), as float32 tensors
+    (content [B, H, S, L, 2^P, d], mass [B, H, S, L, 2^P],
+     dcontent, dmass likewise; None where the source is None).  Q gives the
+    shape and dtype of the calls that filled them."""
+    shape = _shape_of(Q, W, L, P)
+    S, _ = race_bucket_stats_segments(shape, P, L, causal)
+    B, H, N, d = Q.shape
+    R = 1 << P
+    mk = lambda *sh: torch.empty(sh, dtype=torch.float32, device=Q.device)
+    with _on(stream, Q.device):
+        c = mk(B, H, S, L, R, d) if state is not None else None
+        m = mk(B, H, S, L, R) if state is not None else None
+        dc = mk(B, H, S, L, R, d) if workspace is not None else None
+        dm = mk(B, H, S, L, R) if workspace is not None else None
+        p = lambda t: t.data_ptr() if t is not None else None
+        _check(lib().race_bucket_stats_debug(ctypes.byref(shape), int(P), int(L), int(causal), p(state), _bytes(state),
+                                             p(workspace), _bytes(workspace), p(c), p(m), p(dc), p(dm),
+                                             _stream(stream)))
+    return c, m, dc, dm
 
 
 def race_attn_decode_state_bytes(shape: race_shape, P: int, L: int) -> int:
@@ -283,13 +354,14 @@ def race_attn_decode_prefill(K, V, W, beta, P, L, state=None, workspace=None, st
     if nb == 0:
         _check(lib().race_attn_decode_prefill(None, None, None, float(beta), int(P), int(L), ctypes.byref(shape),
                                               None, 0, None, 0, None))
-    if state is None:
-        state = torch.empty(nb // 4, dtype=torch.float32, device=K.device)
     wb = lib().race_attn_decode_prefill_workspace_bytes(ctypes.byref(shape), int(P), int(L))
-    workspace = _buffer(wb, K.device, workspace)
-    _check(lib().race_attn_decode_prefill(_dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P), int(L),
-                                          ctypes.byref(shape), _dev(state, "state"), _bytes(state),
-                                          _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
+    with _on(stream, K.device):
+        if state is None:
+            state = torch.empty(nb // 4, dtype=torch.float32, device=K.device)
+        workspace = _buffer(wb, K.device, workspace)
+        _check(lib().race_attn_decode_prefill(_dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                              int(L), ctypes.byref(shape), _dev(state, "state"), _bytes(state),
+                                              _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
     return state
 
 
@@ -299,8 +371,9 @@ def race_attn_decode(Q, K, V, W, beta, P, L, state, O=None, stream=None):
     shape = _shape_of(Q, W, L, P)
     _like(Q, "Q", K=K, V=V, O=O)
     _same_device(Q, W=W, state=state)
-    O = torch.empty_like(Q) if O is None else O
-    _check(lib().race_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
-                                  int(L), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"), _bytes(state),
-                                  _stream(stream)))
+    with _on(stream, Q.device):
+        O = torch.empty_like(Q) if O is None else O
+        _check(lib().race_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                      int(L), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"),
+                                      _bytes(state), _stream(stream)))
     return O

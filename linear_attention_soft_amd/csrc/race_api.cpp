@@ -39,6 +39,57 @@ __global__ void race_bank_finalize(const float* __restrict__ part, int nchunk, i
   else mass[(size_t)bh * LRP + lr] = s;
 }
 
+// Test export of banks in the pages' layout: out_c[b][l][r][c], out_m[b][l][r]
+// for b < nbank, r < 2^P, from internal banks whose row of table l, corner
+// r' is l * 2^PE + r'.  With P < 3 each corner r has 2^(PE - P) widened
+// copies r' = r + e 2^P; they are summed back in a fixed order and scaled by
+// copy_scale.  The zero hyperplanes split a key's assignment evenly over the
+// copies, so a key bank's copies add up to the bank (scale 1); they also
+// shrink Den by the same factor 2^(P - PE), so g and h grow by 2^(PE - P)
+// and each copy of a gradient bank holds the whole gradient bank (scale
+// 2^(P - PE)).  Content of bank b, row lr, column c sits at
+// src_c[b * c_bank + lr * c_row + c], its mass at src_m[b * m_bank + lr * m_row].
+__global__ void race_bank_export(const float* __restrict__ src_c, int64_t c_bank, int c_row,
+                                 const float* __restrict__ src_m, int64_t m_bank, int m_row, int64_t nbank, int L,
+                                 int P, int PE, int D, float copy_scale, float* __restrict__ out_c,
+                                 float* __restrict__ out_m) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int R = 1 << P;
+  const int64_t per = (int64_t)L * R * (D + 1);
+  if (idx >= nbank * per) return;
+  const int64_t b = idx / per, rem = idx % per;
+  const int lr = (int)(rem / (D + 1)), c = (int)(rem % (D + 1));
+  const int l = lr / R, r = lr % R;
+  float s = 0.f;
+  for (int e = 0; e < (1 << (PE - P)); ++e) {
+    const int row = (l << PE) + r + (e << P);
+    s += c < D ? src_c[b * c_bank + (int64_t)row * c_row + c] : src_m[b * m_bank + (int64_t)row * m_row];
+  }
+  s *= copy_scale;
+  if (c < D) {
+    if (out_c) out_c[(b * L * R + lr) * D + c] = s;
+  } else if (out_m) {
+    out_m[b * L * R + lr] = s;
+  }
+}
+
+const KernelSet* all_kernel_sets(int* count) {
+  static const std::vector<KernelSet> all = [] {
+    std::vector<KernelSet> v;
+    int n = 0;
+#define RACE_COLLECT_INSTANCE(name)              \
+  {                                              \
+    const KernelSet* s = inst_##name(&n);        \
+    v.insert(v.end(), s, s + n);                 \
+  }
+    RACE_INSTANCE_FILES(RACE_COLLECT_INSTANCE)
+#undef RACE_COLLECT_INSTANCE
+    return v;
+  }();
+  *count = (int)all.size();
+  return all.data();
+}
+
 }  // namespace race
 
 namespace {
@@ -110,11 +161,11 @@ size_t elem_size(int dtype) { return dtype == RACE_BF16 ? 2 : 4; }
 
 const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool causal) {
   int count = 0;
-  const race::KernelSet* sets = dtype == RACE_BF16 ? race::kernel_sets_bf16(&count) : race::kernel_sets_f32(&count);
+  const race::KernelSet* sets = race::all_kernel_sets(&count);
   const race::KernelSet* best = nullptr;
   for (int i = 0; i < count; ++i) {
     const race::KernelSet& k = sets[i];
-    if (k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
+    if (k.dtype != dtype || k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
     if (causal && (!k.w_fwd || !k.tw_dq)) continue;
     if (!causal && !k.readout) continue;
     if (!best || k.LRP < best->LRP) best = &k;
@@ -126,11 +177,11 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
 // compiled set has them); smallest padded bank first.
 const race::KernelSet* find_decode_set(int dtype, int D, int PE, int LRP_min) {
   int count = 0;
-  const race::KernelSet* sets = dtype == RACE_BF16 ? race::kernel_sets_bf16(&count) : race::kernel_sets_f32(&count);
+  const race::KernelSet* sets = race::all_kernel_sets(&count);
   const race::KernelSet* best = nullptr;
   for (int i = 0; i < count; ++i) {
     const race::KernelSet& k = sets[i];
-    if (k.D != D || k.PE != PE || k.LRP < LRP_min || !k.decode || !k.reduce) continue;
+    if (k.dtype != dtype || k.D != D || k.PE != PE || k.LRP < LRP_min || !k.decode || !k.reduce) continue;
     if (!best || k.LRP < best->LRP) best = &k;
   }
   return best;
@@ -238,7 +289,15 @@ size_t dw_part_bytes(const Plan& p) {
 size_t dw_bytes(const Plan& p) { return 2 * dpre_side_bytes(p) + dw_part_bytes(p); }
 size_t dw_out_floats(const Plan& p) { return (size_t)(p.w_per_head ? p.H : 1) * p.L * p.P * p.D; }
 
-size_t workspace_bytes(const Plan& p, bool bwd, bool dw = false) {
+// Bytes of the state a backward rebuilds itself when the caller passes none
+// (non-causal: the bank; causal: segment banks and Den; the causal segment
+// sums go to the backward's own gradient-sum region first).
+size_t rebuilt_state_bytes(const Plan& p) { return p.causal ? state_bytes(p) : align256(bank_bytes(p)); }
+
+// Workspace layout: the phase's own scratch, then (backward with dW) the
+// table-gradient region, then (backward without a state) the rebuilt state.
+size_t workspace_bytes(const Plan& p, bool bwd, bool dw = false, bool no_state = false) {
+  if (bwd && no_state) return workspace_bytes(p, true, dw, false) + rebuilt_state_bytes(p);
   if (bwd && dw) return workspace_bytes(p, true, false) + dw_bytes(p);
   if (!p.causal) {
     size_t w = align256(part_bytes(p));
@@ -325,13 +384,11 @@ void launch_seg_scan(const Plan& p, const float* part, float* out, int reverse, 
                      per, (int)p.BH, reverse);
 }
 
-race_status causal_forward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
-                           void* O, void* state, char* ws, hipStream_t s) {
+// Segment sums into part, their exclusive scan into prefix, then the forward
+// walk: O (skipped when NULL) and Den.
+race_status causal_forward_into(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                                void* O, float* part, float* prefix, float* den, hipStream_t s) {
   race_status st;
-  float* part = reinterpret_cast<float*>(ws);
-  char* sbase = state ? static_cast<char*>(state) : ws + align256(seg_bank_bytes(p));
-  float* prefix = reinterpret_cast<float*>(sbase);
-  float* den = reinterpret_cast<float*>(sbase + align256(seg_bank_bytes(p)));
   const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
   race::WArgs w = walk_args(p, W, beta);
   w.B_src = K; w.X_src = V; w.bank_out = part;
@@ -352,6 +409,35 @@ race_status causal_forward(const Plan& p, const void* Q, const void* K, const vo
     p.ks->w_fwd(w, grid, s);
   }
   return check_launch("race_causal_fwd");
+}
+
+race_status causal_forward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                           void* O, void* state, char* ws, hipStream_t s) {
+  float* part = reinterpret_cast<float*>(ws);
+  char* sbase = state ? static_cast<char*>(state) : ws + align256(seg_bank_bytes(p));
+  float* prefix = reinterpret_cast<float*>(sbase);
+  float* den = reinterpret_cast<float*>(sbase + align256(seg_bank_bytes(p)));
+  return causal_forward_into(p, Q, K, V, W, beta, O, part, prefix, den, s);
+}
+
+// Non-causal bank of K, V: partial banks into part, fixed-order sums into
+// content / mass.
+race_status noncausal_bank(const Plan& p, const void* K, const void* V, const float* W, float beta, float* part,
+                           float* content, float* mass, hipStream_t s) {
+  race_status st;
+  race::NCArgs a{};
+  a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.part = part;
+  {
+    ProfScope ps(s, "race_bucket_reduce");
+    p.ks->reduce(a, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bucket_reduce")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nchunk, p, content, mass, s);
+  }
+  return check_launch("race_bank_finalize");
 }
 
 race_status causal_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
@@ -440,17 +526,23 @@ size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal) 
 
 size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int causal, int is_bwd) {
   Plan p;
-  if (is_bwd < 0 || is_bwd > 2) return 0;
+  const int phase = is_bwd & ~RACE_WS_NO_STATE;
+  const bool no_state = (is_bwd & RACE_WS_NO_STATE) != 0;
+  if (phase < RACE_WS_FWD || phase > RACE_WS_BWD_DW || (no_state && phase == RACE_WS_FWD)) return 0;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
   const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
   if (ks) p.LRP = ks->LRP;
   p.ks = ks;
-  return workspace_bytes(p, is_bwd != 0, is_bwd == 2);
+  return workspace_bytes(p, phase != RACE_WS_FWD, phase == RACE_WS_BWD_DW, no_state);
 }
 
-race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
-                          int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
-                          void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+race_status fwd_common(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
+                       int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
+                       void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
   g_last_error.clear();
   Plan p;
   race_status st = make_plan(shape, P, L, causal, &p, true);
@@ -480,20 +572,7 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
   float* bank = state ? static_cast<float*>(state) : reinterpret_cast<float*>(ws + align256(part_bytes(p)));
   float* content = bank;
   float* mass = bank + (size_t)p.BH * p.LRP * p.D;
-
-  race::NCArgs a{};
-  a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
-  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.part = part;
-  {
-    ProfScope ps(s, "race_bucket_reduce");
-    p.ks->reduce(a, dim3(p.nchunk, (unsigned)p.BH), s);
-  }
-  if ((st = check_launch("race_bucket_reduce")) != RACE_OK) return st;
-  {
-    ProfScope ps(s, "race_bank_finalize");
-    launch_finalize(part, p.nchunk, p, content, mass, s);
-  }
-  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
+  if ((st = noncausal_bank(p, K, V, W, beta, part, content, mass, s)) != RACE_OK) return st;
   race::NCArgs r{};
   r.X = Q; r.out0 = O; r.W = tables(p, W); r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
   r.st_content = content; r.st_mass = mass; r.chunk_tokens = p.chunk_tokens; r.nchunk = p.nchunk;
@@ -502,6 +581,17 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
     p.ks->readout(r, dim3(p.nchunk, (unsigned)p.BH), s);
   }
   return check_launch("race_readout_norm");
+}
+
+}  // namespace
+
+extern "C" {
+
+race_status race_attn_fwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
+                          int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
+                          void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
+  return fwd_common(Q, K, V, W, beta, P, L, causal, O, shape, state, state_bytes_in, workspace, workspace_bytes_in,
+                    stream);
 }
 
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
@@ -515,9 +605,8 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV)
     return fail(RACE_ERR_INVALID_ARG, "Q, K, V, W, dO, dQ, dK and dV must be non-NULL");
   if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
-  if (!state) return fail(RACE_ERR_INVALID_ARG, "state from race_attn_fwd is required");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(dO) || !aligned16(dQ) ||
-      !aligned16(dK) || !aligned16(dV) || !aligned16(state) || (O && !aligned16(O)) ||
+      !aligned16(dK) || !aligned16(dV) || (state && !aligned16(state)) || (O && !aligned16(O)) ||
       (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   if (dbeta && ((uintptr_t)dbeta & 3u)) return fail(RACE_ERR_INVALID_ARG, "dbeta must be 4-byte aligned");
@@ -542,16 +631,44 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   if (overlaps(dW, dw_out, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dW overlaps dbeta");
   if (overlaps(dW, dw_out, W, dw_out_floats(p) * sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "dW overlaps W");
   const size_t need_state = state_bytes(p);
-  if (state_bytes_in < need_state)
+  if (state && state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
-  const size_t need_ws = workspace_bytes(p, true, dW != nullptr);
+  const size_t need_ws = workspace_bytes(p, true, dW != nullptr, state == nullptr);
   if (!workspace || workspace_bytes_in < need_ws)
     return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes" +
-                                        (dW ? " (backward with dW)" : ""));
-  if (dW && overlaps(dW, dw_out, workspace, need_ws)) return fail(RACE_ERR_INVALID_ARG, "dW overlaps the workspace");
+                                        (dW ? " (backward with dW)" : "") +
+                                        (state ? "" : " (backward without a state)"));
+  if (overlaps(dW, dw_out, workspace, need_ws)) return fail(RACE_ERR_INVALID_ARG, "dW overlaps the workspace");
+  if (overlaps(dbeta, sizeof(float), workspace, need_ws))
+    return fail(RACE_ERR_INVALID_ARG, "dbeta overlaps the workspace");
+  if (state) {
+    for (const void* o : outs)
+      if (overlaps(state, need_state, o, tbytes)) return fail(RACE_ERR_INVALID_ARG, "state overlaps an output");
+    if (overlaps(state, need_state, workspace, need_ws))
+      return fail(RACE_ERR_INVALID_ARG, "state overlaps the workspace");
+    if (overlaps(state, need_state, dbeta, sizeof(float))) return fail(RACE_ERR_INVALID_ARG, "state overlaps dbeta");
+    if (overlaps(state, need_state, dW, dw_out)) return fail(RACE_ERR_INVALID_ARG, "state overlaps dW");
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
+  if (!state) {
+    // rebuild the forward's state at the end of the workspace: the bank of K,
+    // V (non-causal), or the segment banks and Den (causal; O is not written)
+    char* sreg = ws + workspace_bytes(p, true, dW != nullptr, false);
+    if (p.causal) {
+      float* gpart = reinterpret_cast<float*>(ws + causal_bwd_ws(p).gpart);
+      float* prefix = reinterpret_cast<float*>(sreg);
+      float* den = reinterpret_cast<float*>(sreg + align256(seg_bank_bytes(p)));
+      st = causal_forward_into(p, Q, K, V, W, beta, nullptr, gpart, prefix, den, s);
+    } else {
+      float* content = reinterpret_cast<float*>(sreg);
+      st = noncausal_bank(p, K, V, W, beta, reinterpret_cast<float*>(ws), content,
+                          content + (size_t)p.BH * p.LRP * p.D, s);
+    }
+    if (st != RACE_OK) return st;
+    state = sreg;
+  }
   if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
   char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
 
@@ -687,6 +804,78 @@ race_status race_attn_decode(const void* Q, const void* K, const void* V, const 
     p.ks->decode(a, (unsigned)p.BH, s);
   }
   return check_launch("race_decode");
+}
+
+int race_bucket_stats_segments(const race_shape* shape, int P, int L, int causal, int64_t* seg_tokens) {
+  Plan p;
+  if (make_plan(shape, P, L, causal, &p, true) != RACE_OK) return 0;
+  if (seg_tokens) *seg_tokens = p.causal ? p.seg_tokens : p.N;
+  return p.causal ? p.nseg : 1;
+}
+
+race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int causal, const void* state,
+                                    size_t state_bytes_in, const void* bwd_workspace, size_t bwd_workspace_bytes,
+                                    float* content, float* mass, float* dcontent, float* dmass,
+                                    race_stream_t stream) {
+  g_last_error.clear();
+  Plan p;
+  race_status st = make_plan(shape, P, L, causal, &p, true);
+  if (st != RACE_OK) return st;
+  const bool fwd_out = content || mass, bwd_out = dcontent || dmass;
+  if (!fwd_out && !bwd_out) return fail(RACE_ERR_INVALID_ARG, "no output requested");
+  if (fwd_out && !state) return fail(RACE_ERR_INVALID_ARG, "content / mass need the forward's state");
+  if (bwd_out && !bwd_workspace) return fail(RACE_ERR_INVALID_ARG, "dcontent / dmass need the backward's workspace");
+  if (fwd_out && state_bytes_in < state_bytes(p))
+    return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(state_bytes(p)) + " bytes");
+  if (bwd_out && bwd_workspace_bytes < workspace_bytes(p, true))
+    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(workspace_bytes(p, true)) +
+                                        " bytes");
+  for (const void* q : {(const void*)content, (const void*)mass, (const void*)dcontent, (const void*)dmass})
+    if (q && ((uintptr_t)q & 3u)) return fail(RACE_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
+  const int64_t nbank = p.BH * (p.causal ? p.nseg : 1);
+  const int R = 1 << P;
+  const size_t per_c = (size_t)L * R * p.D * sizeof(float), per_m = (size_t)L * R * sizeof(float);
+  const void* outs[] = {content, mass, dcontent, dmass};
+  const size_t sizes[] = {nbank * per_c, nbank * per_m, nbank * per_c, nbank * per_m};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], sizes[i], outs[j], sizes[j])) return fail(RACE_ERR_INVALID_ARG, "outputs overlap");
+    if (overlaps(outs[i], sizes[i], state, state_bytes(p)) ||
+        overlaps(outs[i], sizes[i], bwd_workspace, workspace_bytes(p, true)))
+      return fail(RACE_ERR_INVALID_ARG, "an output overlaps the state or the workspace");
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t total = nbank * L * R * (p.D + 1);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const int DP1 = (int)p.D + 1;
+  const char* ws = static_cast<const char*>(bwd_workspace);
+  const float gscale = 1.f / (float)(1 << (p.PE - P));
+  if (fwd_out) {
+    const float* b = static_cast<const float*>(state);
+    if (p.causal) {   // segment banks [BH][nseg][LRP][d+1]: the bank before each segment
+      hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, b, (int64_t)p.LRP * DP1, DP1,
+                         b + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.D, 1.f, content, mass);
+    } else {          // content [BH][LRP][d], mass [BH][LRP]
+      hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, b, (int64_t)p.LRP * p.D,
+                         (int)p.D, b + (size_t)p.BH * p.LRP * p.D, (int64_t)p.LRP, 1, nbank, L, P, p.PE,
+                         (int)p.D, 1.f, content, mass);
+    }
+    if ((st = check_launch("race_bank_export")) != RACE_OK) return st;
+  }
+  if (bwd_out) {
+    if (p.causal) {   // gradient banks after each segment [BH][nseg][LRP][d+1]
+      const float* g = reinterpret_cast<const float*>(ws + causal_bwd_ws(p).gsuf);
+      hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * DP1, DP1,
+                         g + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.D, gscale, dcontent, dmass);
+    } else {          // gradient bank dcontent [BH][LRP][d], dmass [BH][LRP]
+      const float* g = reinterpret_cast<const float*>(ws + align256(part_bytes(p)));
+      hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * p.D,
+                         (int)p.D, g + (size_t)p.BH * p.LRP * p.D, (int64_t)p.LRP, 1, nbank, L, P, p.PE,
+                         (int)p.D, gscale, dcontent, dmass);
+    }
+    if ((st = check_launch("race_bank_export")) != RACE_OK) return st;
+  }
+  return RACE_OK;
 }
 
 race_status race_softbucket_debug(const void* X, const float* W, float beta, int P, int L, const race_shape* shape,

@@ -307,15 +307,15 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     const bool valid = t0 + n < s1;
     // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
-    float uA[G::NHP], phA[URP / 2];
+    float preA[G::NHP], phA[URP / 2];
     {
       frag xa[G::KD];
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[bb][n * FS + 16 * q + 8 * h]);
-      float pre[G::NHP];
-      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, pre);
-      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, pre);
-      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uA, phA);
+      float uA[G::NHP];
+      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, preA);
+      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
+      soft_assign_rows<G, R0, URP>(preA, beta2, a.L, uA, phA);
     }
     {
       frag xb[G::KD];
@@ -418,7 +418,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
 #pragma unroll
       for (int i = 0; i < G::NHP; ++i) dpre[i] = 0.f;
       if constexpr (C::SPL == 1) {
-        assign_backward_rows<G, R0, URP>(phA, dphi, uA, a.beta, dpre, bterm);
+        assign_backward_rows<G, R0, URP>(phA, dphi, preA, a.beta, dpre, bterm);
         if (valid && h == 0) bsum += bterm;
         if (h == 0) {
 #pragma unroll
@@ -439,9 +439,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
         const float s = S.XS[w & ~1][0][n] + S.XS[w | 1][0][n];
 #pragma unroll
         for (int t = 0; t < G::PE; ++t) {
-          const float uu = uA[l * G::PE + t];
+          float uu, s2;
+          tanh_sech2(preA[l * G::PE + t], uu, s2);
           const float du = (S.XS[w & ~1][1 + t][n] + S.XS[w | 1][1 + t][n]) - s * tanh_f(a.beta * uu);
-          dpre[l * G::PE + t] = a.beta * du * (1.f - uu * uu);
+          dpre[l * G::PE + t] = a.beta * du * s2;
           bterm += uu * du;
         }
         if (LOWER && valid && h == 0) bsum += bterm;

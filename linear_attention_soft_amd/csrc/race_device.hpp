@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace race {
 
 using bf16 = __bf16;
@@ -139,6 +141,16 @@ __device__ __forceinline__ float tanh_f(float x) {
   return copysignf(t, x);
 }
 
+// tanh(x) and its derivative 1 - tanh(x)^2 = 4 e / (1 + e)^2 with e =
+// exp(-2|x|), both to a few ulp of their own size: forming 1 - u^2 from a
+// rounded u = tanh(x) near +-1 would lose the digits the derivative keeps.
+__device__ __forceinline__ void tanh_sech2(float x, float& u, float& s2) {
+  const float e = __expf(-2.f * fabsf(x));
+  const float r = rcp(1.f + e);
+  u = copysignf((1.f - e) * r, x);
+  s2 = 4.f * e * r * r;
+}
+
 // sigma(z) and sigma(-z) without overflow for any finite z.
 __device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
   float e = __expf(-fabsf(z));
@@ -193,10 +205,24 @@ struct Geo {
 // rows per tile; f32: 16 rows), duplicated in both row halves so every lane
 // ends with all pre-activations of its token; columns follow the plain map
 // c = 16*q + 8*h + i of the token's row loads.
+//
+// float32 I/O keeps the plain rows instead, Wr[hp][c] (hp = l * PE + t, zero
+// for l >= L or t >= P), in the same buffer: its projection is accumulated in
+// float64 (project_rows_f64).
 template <typename T, class G>
 __device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
                                  typename Eng<T>::frag* __restrict__ Wf) {
   using E = Eng<T>;
+  if constexpr (std::is_same<T, float>::value) {
+    static_assert(G::NHP * G::D <= G::NPT * G::KD * 64 * 8, "plain rows fit the operand buffer");
+    float* Wr = reinterpret_cast<float*>(Wf);
+    for (int idx = threadIdx.x; idx < G::NHP * G::D; idx += blockDim.x) {
+      const int hp = idx / G::D, c = idx % G::D;
+      const int l = hp / G::PE, t = hp % G::PE;
+      Wr[idx] = (l < L && t < P) ? W[(size_t)(l * P + t) * G::D + c] : 0.f;
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < G::NPT * G::KD * 64; idx += blockDim.x) {
     const int lane = idx & 63;
     const int q = (idx >> 6) % G::KD;
@@ -225,6 +251,7 @@ __device__ void build_table_frags(const float* __restrict__ W, int L, int P,
                                   typename Eng<T>::frag* __restrict__ Wt) {
   using E = Eng<T>;
   static_assert(G::PE <= (E::NSPLIT == 2 ? 8 : 16), "one tile per table");
+  static_assert(!std::is_same<T, float>::value, "float32 I/O projects from plain rows");
   for (int idx = threadIdx.x; idx < G::LMAX * G::KD * 64; idx += blockDim.x) {
     const int lane = idx & 63;
     const int q = (idx >> 6) % G::KD;
@@ -319,6 +346,38 @@ __device__ __forceinline__ void load_row_frags(const T* __restrict__ x, typename
   }
 }
 
+// float32 I/O: pre[hp] = W_hp . x for slots [HP0, HP1) from the plain rows
+// Wr (build_proj_frags), accumulated in float64 and rounded once.  In float32
+// the partial sums of a d-term dot product grow to about sqrt(d) |w| |x|, so
+// their rounding leaves an absolute error of ~1e-6 on pre at d = 128, which
+// beta carries into the logits; in float64 only the final rounding remains.
+// Each lane half sums its 8 KD columns of the token, then the halves are added.
+template <class G, int HP0, int HP1>
+__device__ __forceinline__ void project_rows_f64(const float* __restrict__ Wr, const f32x8 (&xf)[G::KD],
+                                                 float (&pre)[G::NHP]) {
+  const int h = lane_id() >> 5;
+  constexpr int NH = HP1 > HP0 ? HP1 - HP0 : 1;
+  double s[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) s[j] = 0.0;
+  // columns outer, one float64 sum per hyperplane: only the current step's
+  // row pieces are live
+#pragma unroll
+  for (int q = 0; q < G::KD; ++q) {
+#pragma unroll
+    for (int j = 0; j < HP1 - HP0; ++j) {
+      const f32x8 w = *reinterpret_cast<const f32x8*>(Wr + (HP0 + j) * G::D + 16 * q + 8 * h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[j] = fma((double)w[i], (double)xf[q][i], s[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
+#pragma unroll
+  for (int j = 0; j < HP1 - HP0; ++j) pre[HP0 + j] = (float)(s[j] + __shfl_xor(s[j], 32, 64));
+}
+
 // Projection tiles [PT0, PT1) that hold the hyperplanes of the tables
 // overlapping bucket rows [R0, R0 + NROWS).
 template <class G, int R0, int NROWS>
@@ -336,6 +395,11 @@ __device__ __forceinline__ void project_tiles(const typename Eng<T>::frag* __res
                                               const typename Eng<T>::frag (&xf)[G::KD],
                                               float (&pre)[G::NHP]) {
   using E = Eng<T>;
+  if constexpr (std::is_same<T, float>::value) {
+    project_rows_f64<G, E::HPT * PT0, (E::HPT * PT1 < G::NHP ? E::HPT * PT1 : G::NHP)>(
+        reinterpret_cast<const float*>(Wf), xf, pre);
+    return;
+  }
   const int lane = lane_id();
 #pragma unroll
   for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
@@ -362,6 +426,10 @@ __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict_
                                         const typename Eng<T>::frag (&xf)[G::KD],
                                         float (&pre)[G::NHP]) {
   using E = Eng<T>;
+  if constexpr (std::is_same<T, float>::value) {
+    project_rows_f64<G, 0, G::NHP>(reinterpret_cast<const float*>(Wf), xf, pre);
+    return;
+  }
   const int lane = lane_id();
 #pragma unroll
   for (int pt = 0; pt < G::NPT; ++pt) {
@@ -464,14 +532,15 @@ __device__ __forceinline__ void tl_frag_split(const float (&x)[M / 2], int q,
 
 // Backward through softmax, beta, corners and tanh for one token (TLAYOUT).
 // dLambda = phi * (dphi - sum_r phi dphi) per table; dU_t = beta sum_r dLambda_r v_{r,t};
-// dPre = dU * (1 - u^2).  Both lane halves end with every dPre value.  Works on
+// dPre = dU * (1 - u^2) with u = tanh(pre), the derivative taken from pre
+// (tanh_sech2).  Both lane halves end with every dPre value.  Works on
 // bucket rows [R0, R0 + NROWS), which must hold whole tables; dPre slots of
 // tables outside the window are left untouched.  bterm receives the token's
 // share of dL/dbeta over these tables: sum_r dLambda_r (u . v_r)
 // = sum_t u_t sum_r dLambda_r v_{r,t} (the logits are beta u . v_r).
 template <class G, int R0, int NROWS>
 __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 2], const float (&dphi)[NROWS / 2],
-                                                     const float (&u)[G::NHP], float beta,
+                                                     const float (&pre)[G::NHP], float beta,
                                                      float (&dpre)[G::NHP], float& bterm) {
   const int h = lane_id() >> 5;
   const float sgn2 = h ? 1.f : -1.f;
@@ -509,8 +578,9 @@ __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 
 #pragma unroll
     for (int t = 0; t < G::PE; ++t) {
       const float d = du[t] + xor32(du[t]);
-      const float uu = u[l * G::PE + t];
-      dpre[l * G::PE + t] = beta * d * (1.f - uu * uu);
+      float uu, s2;
+      tanh_sech2(pre[l * G::PE + t], uu, s2);
+      dpre[l * G::PE + t] = beta * d * s2;
       bterm += uu * d;
     }
   }
@@ -560,10 +630,10 @@ __device__ __forceinline__ void store_dpre_half(float* __restrict__ row, const f
 
 template <class G, int R0, int NROWS>
 __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 2], const float (&dphi)[NROWS / 2],
-                                                     const float (&u)[G::NHP], float beta,
+                                                     const float (&pre)[G::NHP], float beta,
                                                      float (&dpre)[G::NHP]) {
   float unused = 0.f;
-  assign_backward_rows<G, R0, NROWS>(phi, dphi, u, beta, dpre, unused);
+  assign_backward_rows<G, R0, NROWS>(phi, dphi, pre, beta, dpre, unused);
 }
 
 // Sum over the 64 lanes of a wave (every lane ends with the total).
@@ -575,9 +645,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <class G>
 __device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], const float (&dphi)[G::LRP / 2],
-                                                const float (&u)[G::NHP], float beta, float (&dpre)[G::NHP],
+                                                const float (&pre)[G::NHP], float beta, float (&dpre)[G::NHP],
                                                 float& bterm) {
-  assign_backward_rows<G, 0, G::LRP>(phi, dphi, u, beta, dpre, bterm);
+  assign_backward_rows<G, 0, G::LRP>(phi, dphi, pre, beta, dpre, bterm);
 }
 
 // Order this wave's LDS writes before its later LDS reads of other lanes'

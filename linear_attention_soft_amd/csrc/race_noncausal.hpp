@@ -36,11 +36,6 @@ struct NCArgs {
   int64_t N;
   int64_t chunk_tokens;     // tokens per workgroup
   int nchunk;
-  // race_bucket_reduce only: when tok_den is set, the value rows Y are divided by
-  // tok_den[token] (g = dO / Den) and the extra column holds tok_extra[token]
-  // instead of ones (the causal backward's gradient sums Phi_Q^T [g | h]).
-  const float* tok_den;
-  const float* tok_extra;
   // backward kernels: when set, each wave writes its share of dL/dbeta to
   // dbeta_part[(bh * nchunk + chunk) * 4 + wave]
   float* dbeta_part;
@@ -269,7 +264,6 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   __shared__ frag Wf[G::NPT * G::KD * 64];
   __shared__ T PhiT[G::LRP * TTP];
   __shared__ T Bs[TT * BSP];
-  __shared__ float hsv[TT];
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
@@ -287,9 +281,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   for (int j = 0; j < NTW; ++j) acc[j] = zero16();
 
   constexpr int CPR = G::D * (int)sizeof(T) / 16;      // 16-byte chunks per row
-  constexpr int EPC = 16 / (int)sizeof(T);              // elements per chunk
   constexpr int NCH = 32 * CPR / 64;                    // chunks per lane per tile
-  const float* den = a.tok_den ? a.tok_den + (size_t)bh * a.N : nullptr;
   const int tl = 32 * w + n;
   const int64_t last = t_end - 1;
   // one register set per operand: the next tile's key rows are loaded as
@@ -329,19 +321,12 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const int64_t trow = base + 32 * w + row;
-      uint4 val = trow < t_end ? ya[it] : make_uint4(0, 0, 0, 0);
-      if (den && trow < t_end) {
-        const float inv = 1.f / den[trow];
-        T* e = reinterpret_cast<T*>(&val);
-#pragma unroll
-        for (int k = 0; k < EPC; ++k) e[k] = (T)((float)e[k] * inv);
-      }
+      const uint4 val = trow < t_end ? ya[it] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Bs + (32 * w + row) * BSP) + 16 * ch) = val;
     }
     load_y(base + step);
-    if (a.tok_extra && h == 0) hsv[tl] = valid ? a.tok_extra[(size_t)bh * a.N + tok] : 0.f;
     __syncthreads();
-    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, a.tok_extra ? hsv : nullptr, acc);
+    reduce_tile_mma<T, G, TTP, BSP, NTW>(PhiT, Bs, nullptr, acc);
     __syncthreads();
   }
   write_partials<T, G, NTW>(a.part + ((size_t)bh * a.nchunk + chunk) * G::LRP * (G::D + 1), acc);
@@ -503,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
         dphi[16 * at + v] = av[16 * at + v] * inv + massL[lr] * hval;
       }
     float dpre[G::NHP], bterm = 0.f;
-    assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
+    assign_backward<G>(phi, dphi, pre, a.beta, dpre, bterm);
     if (valid && h == 0) bsum += bterm;
     if (a.dpre_out && valid) store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + tok) * G::NHP, dpre, h);
     // the wave's 32 rows of Bs are free until the dO rows are staged below
@@ -607,7 +592,7 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
       }
     }
     float dpre[G::NHP], bterm = 0.f;
-    assign_backward<G>(phi, dphi, u, a.beta, dpre, bterm);
+    assign_backward<G>(phi, dphi, pre, a.beta, dpre, bterm);
     if (valid && h == 0) bsum += bterm;
     if (a.dpre_out && valid) store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + tok) * G::NHP, dpre, h);
     dx_mma_stage<T, G>(WTf, dpre, OS[w]);

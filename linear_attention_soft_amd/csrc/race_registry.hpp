@@ -36,7 +36,21 @@ struct KernelSet {
   void (*dw_partial)(const DWArgs&, dim3 grid, hipStream_t);
 };
 
-const KernelSet* kernel_sets_f32(int* count);
-const KernelSet* kernel_sets_bf16(int* count);
+// Compiled kernel sets, one instance file per entry (race_inst_<name>.hip
+// defines inst_<name>); the build lists exactly these files.
+#define RACE_INSTANCE_FILES(X) \
+  X(bf16_d64)                   \
+  X(bf16_d128_p3)               \
+  X(bf16_d128_p4)               \
+  X(bf16_d128_p6)               \
+  X(f32_d64)                    \
+  X(f32_d128)
+
+#define RACE_DECLARE_INSTANCE(name) const KernelSet* inst_##name(int* count);
+RACE_INSTANCE_FILES(RACE_DECLARE_INSTANCE)
+#undef RACE_DECLARE_INSTANCE
+
+// Every compiled set, in instance-file order (built once, thread-safe).
+const KernelSet* all_kernel_sets(int* count);
 
 }  // namespace race

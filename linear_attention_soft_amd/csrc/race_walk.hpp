@@ -44,7 +44,7 @@ struct WArgs {
   const void* B_src;      // state-role token rows (SEGSUM, FWD, H: K; GSUM, DV: Q)
   const void* X_src;      // state-role values (V; GSUM, DV: dO, divided by den)
   const void* dO;         // H: dO rows of the output role
-  void* out;              // FWD: O; DV: dV
+  void* out;              // FWD: O (NULL: only Den is written); DV: dV
   float* bank_out;        // SEGSUM, GSUM: [BH][nseg][LRP][d+1]
   const float* bank_in;   // FWD, H, DV: [BH][nseg][LRP][d+1], bank before (after, DV) the segment
   const float* den;       // [BH][N]: GSUM, H, DV
@@ -443,13 +443,16 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
           *reinterpret_cast<typename E::vec4*>(xs + n * XSP + 8 * j + 4 * h) = o;
         }
         wave_lds_sync();
-        T* og = static_cast<T*>(a.out) + rb * G::D + 32 * ct;
+        // FWD with out == NULL: Den only (the backward rebuilding its state)
+        if (a.out) {
+          T* og = static_cast<T*>(a.out) + rb * G::D + 32 * ct;
 #pragma unroll
-        for (int it = 0; it < XIT; ++it) {
-          const int flat = it * 64 + lane;
-          const int row = flat / CPR, ch = flat % CPR;
-          const uint4 v = *reinterpret_cast<const uint4*>(xs + row * XSP + ch * EPC);
-          if (t0 + row < s1) *reinterpret_cast<uint4*>(og + (t0 + row) * G::D + ch * EPC) = v;
+          for (int it = 0; it < XIT; ++it) {
+            const int flat = it * 64 + lane;
+            const int row = flat / CPR, ch = flat % CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(xs + row * XSP + ch * EPC);
+            if (t0 + row < s1) *reinterpret_cast<uint4*>(og + (t0 + row) * G::D + ch * EPC) = v;
+          }
         }
       } else if (MODE == W_H) {
         float part = 0.f;

@@ -227,6 +227,48 @@ def causal_forward_head(Q, K, V, W, beta, block=256, return_den=False, content0=
     return (O, Den) if return_den else O
 
 
+def causal_forward_head_kernel_blocks(Q, K, V, W, beta, block=256, content0=None, mass0=None):
+    """Causal RACE output of one head, evaluated a block of tokens at a time
+    through the two equal forms the pages give for one readout (slides frame
+    "Normalize after combining the tables": bucket statistics read out by
+    phi(Q), or the implicit kernel S_tj = sum_l phi^(l)(Q_t) . phi^(l)(K_j)
+    applied to the keys; reading notes section 2.5).  The causal readout of
+    token t sums over the keys j <= t (slides frame "Causality is a prefix
+    update of the same statistics"); here the keys before t's block enter
+    through their statistics (content0 / mass0 plus earlier blocks) and the
+    block's own keys j <= t through S_tj [V_j | 1].  Every key is counted
+    once, so O and Den equal those of ``causal_forward_head``, without one
+    bank per token (long sequences stay affordable).
+
+    Returns (O, Den, content, mass); content / mass are the statistics of all
+    keys seen, content0 / mass0 included.
+    """
+    Phi_Q = soft_assign(Q, W, beta)
+    Phi_K = soft_assign(K, W, beta)
+    V = np.asarray(V, dtype=np.float64)
+    L, N, R = Phi_K.shape
+    dv = V.shape[1]
+    content = np.zeros((L, R, dv)) if content0 is None else np.array(content0, dtype=np.float64)
+    mass = np.zeros((L, R)) if mass0 is None else np.array(mass0, dtype=np.float64)
+    O = np.empty((N, dv))
+    Den = np.empty(N)
+    for t0 in range(0, N, block):
+        t1 = min(N, t0 + block)
+        pq, pk = Phi_Q[:, t0:t1], Phi_K[:, t0:t1]
+        # keys before the block: their statistics, read out as in the non-causal layer
+        num = np.matmul(pq, content).sum(axis=0)
+        den = np.matmul(pq, mass[:, :, None])[:, :, 0].sum(axis=0)
+        # keys of the block: the implicit kernel, keys j <= t only
+        S = np.tril(np.matmul(pq, pk.transpose(0, 2, 1)).sum(axis=0))
+        num = num + S @ V[t0:t1]
+        den = den + S.sum(axis=1)
+        O[t0:t1] = num / den[:, None]
+        Den[t0:t1] = den
+        content = content + np.matmul(pk.transpose(0, 2, 1), V[t0:t1])
+        mass = mass + pk.sum(axis=1)
+    return O, Den, content, mass
+
+
 def brute_force_head(Q, K, V, W, beta, causal=False):
     """Explicit N x N kernel S_hat = (1/L) sum_l Phi_Q^(l) Phi_K^(l)^T, masked
     to j <= i when causal, then row-normalised: O = diag(S_hat 1)^-1 S_hat V.

@@ -69,9 +69,19 @@ int main(void) {
   const void* st = (const void*)(base + ((uintptr_t)10 << 24));
   float* dW = (float*)(base + ((uintptr_t)11 << 24));
   void* wsb = (void*)(base + ((uintptr_t)12 << 24));
+  /* without a state the backward rebuilds it in a larger workspace */
+  const size_t wns = race_attn_workspace_bytes(&s, 4, 2, 0, RACE_WS_BWD | RACE_WS_NO_STATE);
+  EXPECT(wns > wb, "workspace of the backward without a state");
+  EXPECT(race_attn_workspace_bytes(&s, 4, 2, 0, RACE_WS_NO_STATE) == 0, "no-state flag needs a backward phase");
   EXPECT(race_attn_bwd(Q, K, V, W, 1.0f, 4, 2, 0, NULL, dO, dQ, dK, dV, NULL, NULL, &s, NULL, 0, wsb, wb, NULL) ==
-             RACE_ERR_INVALID_ARG,
-         "backward without state");
+             RACE_ERR_WORKSPACE,
+         "backward without state needs the larger workspace");
+  EXPECT(race_attn_bwd(Q, K, V, W, 1.0f, 4, 2, 0, NULL, dO, dQ, dK, dV, NULL, NULL, &s, dQ, 1 << 30, wsb, wb,
+                       NULL) == RACE_ERR_INVALID_ARG,
+         "state overlaps dQ");
+  EXPECT(race_attn_bwd(Q, K, V, W, 1.0f, 4, 2, 0, NULL, dO, dQ, dK, dV, NULL, NULL, &s, wsb, 1 << 20, wsb, wb,
+                       NULL) == RACE_ERR_INVALID_ARG,
+         "state overlaps the workspace");
   EXPECT(race_attn_bwd(Q, K, V, W, 1.0f, 4, 2, 0, NULL, dO, dQ, dK, dV, NULL, dW, &s, st, 1 << 30, wsb, wb, NULL) ==
              RACE_ERR_WORKSPACE,
          "dW needs the larger workspace");

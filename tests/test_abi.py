@@ -63,6 +63,11 @@ def test_size_queries():
                  - race.race_attn_workspace_bytes(s, 4, 2, causal, 1))
         assert extra >= 2 * 2 * 4096 * 8 * 4
     assert race.race_attn_workspace_bytes(s, 4, 2, False, 3) == 0
+    assert race.race_attn_workspace_bytes(s, 4, 2, False, 4) == 0     # no-state flag without a backward phase
+    for causal in (False, True):
+        for ph in (1, 2):
+            assert (race.race_attn_workspace_bytes(s, 4, 2, causal, ph | 4)
+                    > race.race_attn_workspace_bytes(s, 4, 2, causal, ph))
     # invalid arguments give 0
     assert race.race_attn_state_bytes(s, 0, 2, False) == 0
     assert race.race_attn_state_bytes(s, 4, 0, False) == 0
@@ -116,7 +121,12 @@ def test_backward_rejects_bad_arguments():
         return Lb.race_attn_bwd(base[0], base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, 0, None, base[5],
                                 dq, base[7], base[8], dbeta, dW, ctypes.byref(s), state, stateb, ws, wsb, None)
 
-    assert call(state=None) == 1
+    wb_st = race.race_attn_workspace_bytes(s, 3, 2, False, 1)
+    wb_nost = race.race_attn_workspace_bytes(s, 3, 2, False, 1 | 4)
+    assert wb_nost > wb_st
+    assert call(state=None, wsb=wb_st) == 3     # backward without a state needs the larger workspace
+    assert call(state=base[6]) == 1             # state is dQ
+    assert call(state=base[10]) == 1            # state is the workspace
     assert call(beta=math.nan) == 1
     assert call(stateb=4) == 3
     assert call(wsb=4) == 3
@@ -207,3 +217,25 @@ def test_binding_rejects_mismatched_token_tensors():
         race.race_attn_decode_prefill(Q, short, W, 1.0, 3, 2)
     with pytest.raises(ValueError, match="O must have Q's shape"):
         race.race_attn_decode(Q, Q, Q, W, 1.0, 3, 2, None, O=wrong_dtype)
+
+
+def test_build_lists_exactly_the_instance_files(tmp_path, monkeypatch):
+    """build.py compiles the instance files the registry names; a missing
+    listed file, or an instance file the registry does not name, is an error
+    (a library silently missing kernel sets would only fail at run time)."""
+    from linear_attention_soft_amd import build as B
+    srcs = B.sources()
+    assert srcs[-1] == "race_api.cpp"
+    assert [f"race_inst_{n}.hip" for n in B.instance_names()] == srcs[:-1]
+    fake = tmp_path / "csrc"
+    fake.mkdir()
+    for name in os.listdir(B.CSRC):
+        (fake / name).write_bytes(open(os.path.join(B.CSRC, name), "rb").read())
+    monkeypatch.setattr(B, "CSRC", str(fake))
+    os.remove(fake / srcs[0])
+    with pytest.raises(RuntimeError, match="missing"):
+        B.sources()
+    (fake / srcs[0]).write_text("// restored\n")
+    (fake / "race_inst_unlisted.hip").write_text("// not in the registry\n")
+    with pytest.raises(RuntimeError, match="not named"):
+        B.sources()

@@ -66,4 +66,9 @@ def test_cpu_baseline_sample_is_sized_by_a_probe():
     w = ri.WORKLOADS[1]
     inp = ri.make_inputs(w, device="cpu")
     rec = bench.cpu_baseline(inp, w, target_s=0.5)
-    assert f"first {w.N} tokens" in rec["sample"]
+    # workload 1 is one sequence of 1024 tokens: the sample is the whole workload
+    assert rec["sample"].startswith("the whole workload") and rec["extrapolated"] is False
+    w2 = ri.WORKLOADS[2].with_size(N=300, B=1, H=2)
+    rec2 = bench.cpu_baseline(ri.make_inputs(w2, device="cpu"), w2, target_s=0.3)
+    assert rec2["extrapolated"] is True and "extrapolated" in rec2["sample"]
+    assert re.search(r"first \d+ of 300 tokens", rec2["sample"])

@@ -1,11 +1,15 @@
 """GPU parity of dL/dbeta (the inverse temperature the pages train: corner
 logits beta * u . v_r) against the fp64 oracle.
 
-dbeta is one float summed over both sides, every head, table and token, so
-the bar is stated against the scale of its summands: |dbeta - ref| <= tol *
-sum_i |term_i| over the oracle's per-token terms (tol 1e-5 for fp32 I/O,
-2e-2 for bf16 I/O, as for the tensors).  Two runs must give the same bits
-(the per-wave shares are summed in a fixed order).
+The bar is the one of every gradient: |dbeta - ref| <= tol * |ref| (tol 1e-5
+for fp32 I/O, 2e-2 for bf16 I/O).  dbeta sums one term per token, side,
+head and table; with an upstream gradient dO drawn independently of O those
+terms have random signs and their sum is a small remainder of large parts
+(|ref| / sum |terms| about 1e-2), so the test takes dO = O (the oracle's
+output rounded to the I/O dtype: the gradient of sum |O|^2 / 2), whose terms
+mostly share a sign (|ref| / sum |terms| between 0.47 and 1 in these cases).
+The scale sum |terms| is printed beside the error.  Two runs must give the
+same bits (the per-wave shares are summed in a fixed order).
 """
 from dataclasses import replace
 
@@ -29,8 +33,8 @@ def _gpu():
     race.lib()
 
 
-def _ref(inp, w):
-    Q, K, V, dO = (to64(inp[k]) for k in ("Q", "K", "V", "dO"))
+def _ref(inp, w, dO):
+    Q, K, V = (to64(inp[k]) for k in ("Q", "K", "V"))
     Wn = inp["W"].double().numpy()
     tot, scale = 0.0, 0.0
     for b in range(w.B):
@@ -44,6 +48,7 @@ def _ref(inp, w):
 @pytest.mark.parametrize("key,N,B,H,dtype,causal,give_o", [
     (1, 700, 1, 1, "f32", False, False),
     (3, 3000, 2, 2, "bf16", False, False),
+    (4, 4000, 1, 2, "bf16", False, False),
     (2, 600, 1, 2, "f32", True, False),
     (2, 600, 1, 2, "f32", True, True),
     (5, 1100, 1, 2, "bf16", True, True),
@@ -51,7 +56,11 @@ def _ref(inp, w):
 ])
 def test_dbeta_parity(key, N, B, H, dtype, causal, give_o):
     w = replace(ri.WORKLOADS[key].with_size(N=N, B=B, H=H), causal=causal, dtype=dtype)
-    inp = ri.make_inputs(w, device="cpu", with_grad_out=True)
+    inp = ri.make_inputs(w, device="cpu", with_grad_out=False)
+    # upstream gradient dO = O from the oracle, rounded to the I/O dtype
+    Wn = inp["W"].double().numpy()
+    O_ref = orc.forward(to64(inp["Q"]), to64(inp["K"]), to64(inp["V"]), Wn, w.beta, causal)
+    inp["dO"] = torch.from_numpy(O_ref).to(inp["Q"].dtype)
     dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     say(f"dbeta key={key} N={N} B={B} H={H} {dtype} causal={causal} O given={give_o} P={w.P} L={w.L} beta={w.beta}")
     O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal)
@@ -62,11 +71,12 @@ def test_dbeta_parity(key, N, B, H, dtype, causal, give_o):
         torch.cuda.synchronize()
         got.append(db.cpu())
     assert torch.equal(got[0], got[1]), "dbeta differs between two runs"
-    ref, scale = _ref(inp, w)
+    ref, scale = _ref(inp, w, to64(inp["dO"]))
     err = abs(float(got[0][0]) - ref)
-    say(f"  dbeta gpu {float(got[0][0]):.6e} ref {ref:.6e} |err| {err:.3e} scale {scale:.3e} "
-        f"err/scale {err / scale:.3e} tol {TOL[dtype]:g}")
-    assert err <= TOL[dtype] * scale
+    say(f"  dbeta gpu {float(got[0][0]):.6e} ref {ref:.6e} |err| {err:.3e} |err|/|ref| {err / abs(ref):.3e} "
+        f"(sum |terms| {scale:.3e}, |ref|/sum {abs(ref) / scale:.3f}) tol {TOL[dtype]:g}")
+    assert abs(ref) >= 0.3 * scale, "case chosen so that dbeta is not a small remainder"
+    assert err <= TOL[dtype] * abs(ref)
 
 
 def test_dbeta_absent_leaves_gradients_unchanged():

@@ -1,13 +1,21 @@
 """Parity at the full workload sizes, on the inputs and in the launch
 configuration that bench.py times.
 
-The fp64 oracle streams every token once or twice (bucket banks are sums over
-the whole sequence), then checks: the whole bucket bank (every entry), and
-sampled output / gradient rows that the oracle evaluates one by one from its
-own banks.  Causal: sampled rows read the oracle's prefix bank at their
-position; the final 2048-token block is checked element by element from the
-bank of everything before it; sum_j dV_j = sum_t dO_t holds at any size.
+The fp64 oracle streams the sequences chunk by chunk (bucket banks are sums
+over whole sequences) and checks every head:
+
+* non-causal, 12M tokens: the whole bucket bank and the whole gradient bank
+  (every entry, through the bank export), and sampled O / dQ / dK / dV rows
+  that the oracle evaluates one by one from its own banks;
+* causal, 1M tokens, 64 corners per table: O at every token (the oracle's
+  block-wise evaluation of the prefix readout), the bank before every
+  sequence segment and the gradient bank after it (every entry, through the
+  bank export), sampled dQ / dK / dV rows spread over the whole sequence
+  (each from the oracle's prefix or suffix bank at that row), the final
+  2048-token block element by element, and sum_j dV_j = sum_t dO_t.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -36,127 +44,180 @@ def rel(got, ref):
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
 
 
+# each soft assignment is rounded to bf16 once before it is summed, so bank
+# masses can deviate by at most 2^-9 relative (round-to-nearest-even of these
+# assignments is biased: an fp64 emulation gives 8.7e-4 at 12M tokens)
+MASS_TOL = 2.0 ** -9
+
+
 def _run(w):
     say(f"full-size {w.name}: inputs on the GPU")
     inp = ri.make_inputs(w, device="cuda")
     Wd = inp["W"].cuda()
-    O, state = race.race_attn_fwd(inp["Q"], inp["K"], inp["V"], Wd, w.beta, w.P, w.L, w.causal)
-    dQ, dK, dV = race.race_attn_bwd(inp["Q"], inp["K"], inp["V"], Wd, w.beta, w.P, w.L, w.causal, inp["dO"], state,
-                                    O=O)
+    Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
+    O, state = race.race_attn_fwd(Q, K, V, Wd, w.beta, w.P, w.L, w.causal)
+    shape = race._shape_of(Q, Wd, w.L, w.P)
+    ws = torch.empty(race.race_attn_workspace_bytes(shape, w.P, w.L, w.causal, race.RACE_WS_BWD), dtype=torch.uint8,
+                     device="cuda")
+    dQ, dK, dV = race.race_attn_bwd(Q, K, V, Wd, w.beta, w.P, w.L, w.causal, dO, state, O=O, workspace=ws)
+    banks = race.race_bucket_stats_debug(Q, Wd, w.P, w.L, w.causal, state=state, workspace=ws)
     torch.cuda.synchronize()
     say("  GPU forward + backward done")
-    return inp, O, state, dQ, dK, dV
+    return inp, O, dQ, dK, dV, [f64(b) for b in banks]
 
 
-@pytest.mark.timeout(1200)
+@pytest.mark.timeout(1500)
 def test_noncausal_12m_tokens_full_size():
     w = ri.WORKLOADS[4]
-    inp, O, state, dQ, dK, dV = _run(w)
+    inp, O, dQ, dK, dV, (cont_g, mass_g, dcont_g, dmass_g) = _run(w)
     Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
     Wn = inp["W"].double().numpy()
-    N, d, L, R = w.N, w.d, w.L, w.R
-    LRP = 32
-    st = state.view(torch.float32)
-    nb = w.B * w.H * LRP * d
-    cont_gpu = f64(st[:nb]).reshape(w.H, LRP, d)
-    mass_gpu = f64(st[nb:nb + w.B * w.H * LRP]).reshape(w.H, LRP)
+    N, L, R = w.N, w.L, w.R
     rng = np.random.default_rng(404)
     step = 1 << 20
     tol = TOL["bf16"]
-    # heads 0 and H-1 sampled for the bank, O and dQ; head H-1 for the gradient bank, dK and dV
-    for h in (0, w.H - 1):
-        content = np.zeros((L, R, d))
+    for h in range(w.H):
+        t_start = time.time()
+        content = np.zeros((L, R, w.d))
         mass = np.zeros((L, R))
         for t0 in range(0, N, step):
             c, m = orc.state_head(f64(K[0, h, t0:t0 + step]), f64(V[0, h, t0:t0 + step]), Wn, w.beta)
             content += c
             mass += m
-        e_c = rel(cont_gpu[h, :L * R].reshape(L, R, d), content)
-        e_m = rel(mass_gpu[h, :L * R].reshape(L, R), mass)
+        e_c, e_m = rel(cont_g[0, h, 0], content), rel(mass_g[0, h, 0], mass)
         say(f"  head {h}: bank content rel {e_c:.2e}, mass rel {e_m:.2e}")
-        # each assignment is rounded to bf16 once before it is summed, so the
-        # masses can deviate by at most 2^-9 relative (round-to-nearest-even of
-        # this distribution is biased: an fp64 emulation gives 8.7e-4 here)
-        assert e_c <= tol and e_m <= 2.0 ** -9
+        assert e_c <= tol and e_m <= MASS_TOL
         idx = np.sort(rng.choice(N, 2048, replace=False))
         it = torch.from_numpy(idx).cuda()
-        Qs, dOs = f64(Q[0, h][it]), f64(dO[0, h][it])
-        dq_ref, o_ref, _, _, _ = orc.query_grads(Qs, dOs, Wn, w.beta, content, mass)
-        e_o = rel(f64(O[0, h][it]), o_ref)
-        e_q = rel(f64(dQ[0, h][it]), dq_ref)
-        vmax = float(f64(V[0, h, :step]).__abs__().max())
-        say(f"  head {h}: sampled O rel {e_o:.2e} (abs/max|V| {np.abs(f64(O[0, h][it]) - o_ref).max() / vmax:.2e}),"
-            f" dQ rel {e_q:.2e}")
-        assert e_o <= tol and e_q <= tol
-        if h != w.H - 1:
-            continue
-        dc = np.zeros((L, R, d))
+        dq_ref, o_ref, _, _, _ = orc.query_grads(f64(Q[0, h][it]), f64(dO[0, h][it]), Wn, w.beta, content, mass)
+        e_o, e_q = rel(f64(O[0, h][it]), o_ref), rel(f64(dQ[0, h][it]), dq_ref)
+        vmax = float(np.abs(f64(V[0, h, :step])).max())
+        e_ov = float(np.abs(f64(O[0, h][it]) - o_ref).max() / vmax)
+        say(f"  head {h}: sampled O rel {e_o:.2e} (abs / max|V| {e_ov:.2e}), dQ rel {e_q:.2e}")
+        assert e_o <= tol and e_ov <= tol and e_q <= tol
+        dc = np.zeros((L, R, w.d))
         dm = np.zeros((L, R))
         for t0 in range(0, N, step):
-            Phi_Q, _, _, g, hh = orc.query_terms(f64(Q[0, h, t0:t0 + step]), f64(dO[0, h, t0:t0 + step]), Wn, w.beta,
-                                                 content, mass)
+            Phi_Q, _, _, g, hh = orc.query_terms(f64(Q[0, h, t0:t0 + step]), f64(dO[0, h, t0:t0 + step]), Wn,
+                                                 w.beta, content, mass)
             a, b = orc.grad_banks(None, Wn, w.beta, g, hh, Phi_Q=Phi_Q)
             dc += a
             dm += b
+        e_dc, e_dm = rel(dcont_g[0, h, 0], dc), rel(dmass_g[0, h, 0], dm)
+        say(f"  head {h}: gradient bank dcontent rel {e_dc:.2e}, dmass rel {e_dm:.2e}")
+        assert e_dc <= tol and e_dm <= tol
         idx = np.sort(rng.choice(N, 2048, replace=False))
         it = torch.from_numpy(idx).cuda()
         dk_ref, dv_ref = orc.key_grads(f64(K[0, h][it]), f64(V[0, h][it]), Wn, w.beta, dc, dm)
         e_k, e_v = rel(f64(dK[0, h][it]), dk_ref), rel(f64(dV[0, h][it]), dv_ref)
-        say(f"  head {h}: sampled dK rel {e_k:.2e}, dV rel {e_v:.2e}")
+        say(f"  head {h}: sampled dK rel {e_k:.2e}, dV rel {e_v:.2e} ({time.time() - t_start:.0f} s)")
         assert e_k <= tol and e_v <= tol
 
 
-@pytest.mark.timeout(1200)
+@pytest.mark.timeout(1500)
 def test_causal_1m_tokens_wide_buckets_full_size():
     w = ri.WORKLOADS[5]
-    inp, O, state, dQ, dK, dV = _run(w)
+    inp, O, dQ, dK, dV, (cont_g, mass_g, dcont_g, dmass_g) = _run(w)
     Q, K, V, dO = inp["Q"], inp["K"], inp["V"], inp["dO"]
     Wn = inp["W"].double().numpy()
     N, d, L, R = w.N, w.d, w.L, w.R
+    shape = race._shape_of(Q, inp["W"], w.L, w.P)
+    nseg, seg = race.race_bucket_stats_segments(shape, w.P, w.L, True)
+    assert cont_g.shape == (1, w.H, nseg, L, R, d)
+    say(f"  {nseg} segments of {seg} tokens per head")
     TAIL = 2048
     rng = np.random.default_rng(505)
     tol = TOL["bf16"]
-    step = 1 << 16
     for h in range(w.H):
-        samples = np.sort(rng.choice(N - TAIL, 512, replace=False))
-        content = np.zeros((L, R, d))
-        mass = np.zeros((L, R))
-        pos = 0
-        got_o, ref_o, got_q, ref_q = [], [], [], []
-        si = 0
-        for t0 in range(0, N - TAIL, step):
-            t1 = min(N - TAIL, t0 + step)
-            Kc, Vc = f64(K[0, h, t0:t1]), f64(V[0, h, t0:t1])
-            while si < len(samples) and samples[si] < t1:
-                t = int(samples[si])
-                c, m = orc.state_head(Kc[pos - t0:t + 1 - t0], Vc[pos - t0:t + 1 - t0], Wn, w.beta)
-                content += c
-                mass += m
+        t_start = time.time()
+        samples = np.sort(rng.choice(N, 512, replace=False))
+        # forward sweep: O at every token, the bank before every segment,
+        # and dQ at the sampled rows from the prefix bank at each of them
+        c = np.zeros((L, R, d))
+        m = np.zeros((L, R))
+        Den = np.empty(N)
+        dodo = np.empty(N)
+        err_o, max_o, err_ov, vmax = 0.0, 0.0, 0.0, 0.0
+        err_bc, max_bc, err_bm, max_bm = 0.0, 0.0, 0.0, 0.0
+        got_q, ref_q = [], []
+        for s in range(nseg):
+            t0, t1 = s * seg, min(N, (s + 1) * seg)
+            err_bc = max(err_bc, float(np.abs(cont_g[0, h, s] - c).max()))
+            max_bc = max(max_bc, float(np.abs(c).max()))
+            err_bm = max(err_bm, float((np.abs(mass_g[0, h, s] - m) / np.maximum(m, 1e-300)).max()) if s else 0.0)
+            assert s or (np.all(cont_g[0, h, 0] == 0) and np.all(mass_g[0, h, 0] == 0))
+            Qc, Kc, Vc, dOc = (f64(x[0, h, t0:t1]) for x in (Q, K, V, dO))
+            o, den, c1, m1 = orc.causal_forward_head_kernel_blocks(Qc, Kc, Vc, Wn, w.beta, content0=c, mass0=m)
+            og = f64(O[0, h, t0:t1])
+            err_o = max(err_o, float(np.abs(og - o).max()))
+            max_o = max(max_o, float(np.abs(o).max()))
+            vmax = max(vmax, float(np.abs(Vc).max()))
+            Den[t0:t1] = den
+            dodo[t0:t1] = np.sum(dOc * o, axis=1)
+            # prefix banks at the sampled rows of this segment (keys j <= t)
+            cr, mr, pos = c.copy(), m.copy(), t0
+            for t in samples[(samples >= t0) & (samples < t1)]:
+                a, b = orc.state_head(Kc[pos - t0:t + 1 - t0], Vc[pos - t0:t + 1 - t0], Wn, w.beta)
+                cr += a
+                mr += b
                 pos = t + 1
-                dq, o, _, _, _ = orc.query_grads(f64(Q[0, h, t:t + 1]), f64(dO[0, h, t:t + 1]), Wn, w.beta,
-                                                 content, mass)
-                ref_o.append(o[0]); ref_q.append(dq[0])
-                got_o.append(f64(O[0, h, t])); got_q.append(f64(dQ[0, h, t]))
-                si += 1
-            if pos < t1:
-                c, m = orc.state_head(Kc[pos - t0:], Vc[pos - t0:], Wn, w.beta)
-                content += c
-                mass += m
-                pos = t1
-        e_o = rel(np.array(got_o), np.array(ref_o))
-        e_q = rel(np.array(got_q), np.array(ref_q))
-        say(f"  head {h}: sampled causal O rel {e_o:.2e}, dQ rel {e_q:.2e}")
-        assert e_o <= tol and e_q <= tol
+                dq, _, _, _, _ = orc.query_grads(Qc[t - t0:t + 1 - t0], dOc[t - t0:t + 1 - t0], Wn, w.beta, cr, mr)
+                ref_q.append(dq[0])
+                got_q.append(f64(dQ[0, h, int(t)]))
+            c, m = c1, m1
+        e_o, e_ov, e_q = err_o / max_o, err_o / vmax, rel(np.array(got_q), np.array(ref_q))
+        e_bc = err_bc / max_bc
+        say(f"  head {h}: O at all {N} tokens rel {e_o:.2e} (abs / max|V| {e_ov:.2e}); banks before each segment "
+            f"content rel {e_bc:.2e}, mass rel {err_bm:.2e}; sampled dQ rel {e_q:.2e} ({time.time() - t_start:.0f} s)")
+        assert e_o <= tol and e_ov <= tol and e_bc <= tol and err_bm <= MASS_TOL and e_q <= tol
+        # backward sweep: the gradient bank after every segment, and dK, dV at
+        # the sampled rows from the suffix bank at each of them (queries t >= j)
+        dc = np.zeros((L, R, d))
+        dm = np.zeros((L, R))
+        err_gc, max_gc, err_gm, max_gm = 0.0, 0.0, 0.0, 0.0
+        got_k, ref_k, got_v, ref_v = [], [], [], []
+        for s in reversed(range(nseg)):
+            t0, t1 = s * seg, min(N, (s + 1) * seg)
+            err_gc = max(err_gc, float(np.abs(dcont_g[0, h, s] - dc).max()))
+            max_gc = max(max_gc, float(np.abs(dc).max()))
+            err_gm = max(err_gm, float(np.abs(dmass_g[0, h, s] - dm).max()))
+            max_gm = max(max_gm, float(np.abs(dm).max()))
+            Qc, Kc, Vc, dOc = (f64(x[0, h, t0:t1]) for x in (Q, K, V, dO))
+            g = dOc / Den[t0:t1, None]
+            hh = -dodo[t0:t1] / Den[t0:t1]
+            Phi_Q = orc.soft_assign(Qc, Wn, w.beta)
+            dcr, dmr, pos = dc.copy(), dm.copy(), t1
+            for j in samples[(samples >= t0) & (samples < t1)][::-1]:
+                a, b = orc.grad_banks(None, Wn, w.beta, g[j - t0:pos - t0], hh[j - t0:pos - t0],
+                                      Phi_Q=Phi_Q[:, j - t0:pos - t0])
+                dcr += a
+                dmr += b
+                pos = j
+                dk, dv = orc.key_grads(Kc[j - t0:j + 1 - t0], Vc[j - t0:j + 1 - t0], Wn, w.beta, dcr, dmr)
+                ref_k.append(dk[0]); ref_v.append(dv[0])
+                got_k.append(f64(dK[0, h, int(j)])); got_v.append(f64(dV[0, h, int(j)]))
+            a, b = orc.grad_banks(None, Wn, w.beta, g[:pos - t0], hh[:pos - t0], Phi_Q=Phi_Q[:, :pos - t0])
+            dc, dm = dcr + a, dmr + b
+        e_gc, e_gm = err_gc / max_gc, err_gm / max_gm
+        e_k, e_v = rel(np.array(got_k), np.array(ref_k)), rel(np.array(got_v), np.array(ref_v))
+        say(f"  head {h}: gradient banks after each segment dcontent rel {e_gc:.2e}, dmass rel {e_gm:.2e}; "
+            f"sampled dK rel {e_k:.2e}, dV rel {e_v:.2e} ({time.time() - t_start:.0f} s)")
+        assert e_gc <= tol and e_gm <= tol and e_k <= tol and e_v <= tol
+        # the final block element by element, from the oracle's bank of everything before it
+        c0, m0 = np.zeros((L, R, d)), np.zeros((L, R))
+        for t0 in range(0, N - TAIL, 1 << 16):
+            t1 = min(N - TAIL, t0 + (1 << 16))
+            a, b = orc.state_head(f64(K[0, h, t0:t1]), f64(V[0, h, t0:t1]), Wn, w.beta)
+            c0 += a
+            m0 += b
         sl = slice(N - TAIL, N)
         Qt, Kt, Vt, dOt = (f64(x[0, h, sl]) for x in (Q, K, V, dO))
-        ot = orc.causal_forward_head(Qt, Kt, Vt, Wn, w.beta, content0=content, mass0=mass)
-        tq, tk, tv = orc.backward_head(Qt, Kt, Vt, Wn, w.beta, dOt, True, content0=content, mass0=mass)
-        errs = [rel(f64(O[0, h, sl]), ot), rel(f64(dQ[0, h, sl]), tq), rel(f64(dK[0, h, sl]), tk),
-                rel(f64(dV[0, h, sl]), tv)]
-        say(f"  head {h}: final {TAIL}-token block O/dQ/dK/dV rel " + " ".join(f"{e:.2e}" for e in errs))
+        tq, tk, tv = orc.backward_head(Qt, Kt, Vt, Wn, w.beta, dOt, True, content0=c0, mass0=m0)
+        errs = [rel(f64(dQ[0, h, sl]), tq), rel(f64(dK[0, h, sl]), tk), rel(f64(dV[0, h, sl]), tv)]
+        say(f"  head {h}: final {TAIL}-token block dQ/dK/dV rel " + " ".join(f"{e:.2e}" for e in errs))
         assert max(errs) <= tol
         sdv = dV[0, h].double().sum(0).cpu().numpy()
         sdo = dO[0, h].double().sum(0).cpu().numpy()
         e_s = float(np.abs(sdv - sdo).max() / np.abs(sdo).max())
-        say(f"  head {h}: sum_j dV_j vs sum_t dO_t rel {e_s:.2e}")
+        say(f"  head {h}: sum_j dV_j vs sum_t dO_t rel {e_s:.2e} ({time.time() - t_start:.0f} s)")
         assert e_s <= 1e-2

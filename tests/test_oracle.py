@@ -443,6 +443,32 @@ def test_causal_blocks_with_initial_bank_equal_whole_sequence():
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * np.abs(b).max())
 
 
+def test_causal_kernel_blocks_equal_prefix_readout():
+    """The block-wise causal evaluation (statistics of the keys before a
+    block plus the implicit kernel over the block's keys j <= t) gives the
+    O and Den of the per-token prefix readout, the one-token loop and the
+    masked brute-force kernel, for blocks that do not divide N, with and
+    without a starting bank; its final statistics are those of all keys."""
+    rng = np.random.default_rng(62)
+    for (N, d, L, P, beta, block) in [(37, 5, 2, 3, 2.0, 8), (130, 6, 3, 2, 6.0, 32), (64, 4, 2, 4, 1.0, 64)]:
+        Q, K, V, W = _rand_head(rng, N, d, L, P)
+        O_ref, Den_ref = orc.causal_forward_head(Q, K, V, W, beta, return_den=True)
+        O, Den, c, m = orc.causal_forward_head_kernel_blocks(Q, K, V, W, beta, block=block)
+        np.testing.assert_allclose(O, O_ref, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Den, Den_ref, rtol=1e-12)
+        np.testing.assert_allclose(O, orc.causal_forward_head_loop(Q, K, V, W, beta), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(O, orc.brute_force_head(Q, K, V, W, beta, True)[0], rtol=1e-12, atol=1e-13)
+        c_all, m_all = orc.state_head(K, V, W, beta)
+        np.testing.assert_allclose(c, c_all, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(m, m_all, rtol=1e-12)
+        cut = N // 3
+        c0, m0 = orc.state_head(K[:cut], V[:cut], W, beta)
+        Ot, Dt, _, _ = orc.causal_forward_head_kernel_blocks(Q[cut:], K[cut:], V[cut:], W, beta, block=block,
+                                                             content0=c0, mass0=m0)
+        np.testing.assert_allclose(Ot, O_ref[cut:], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Dt, Den_ref[cut:], rtol=1e-12)
+
+
 def test_bank_level_pieces_compose_to_backward():
     """query_grads / grad_banks / key_grads evaluated in two halves and summed
     give the single-call gradients (bank sums are additive over rows)."""
