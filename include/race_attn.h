@@ -103,6 +103,24 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
                           const race_shape* shape, void* state, size_t state_bytes,
                           void* workspace, size_t workspace_bytes, race_stream_t stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as race_attn_fwd without the
+ * workspace: its scratch is a device array inside the library, one copy per
+ * GPU, of race_attn_fwd_noalloc_scratch_bytes() bytes (64 MiB), held until
+ * the process ends.  A call needs the partial banks (non-causal) or
+ * segment sums (causal) in it, plus room for the state when state is NULL;
+ * a call needing more returns RACE_ERR_WORKSPACE and enqueues nothing.
+ * The call allocates nothing; the first call on a device looks up that
+ * device's scratch address.  Every call on a GPU shares its scratch, so
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race: serialise them. */
+size_t race_attn_fwd_noalloc_scratch_bytes(void);
+race_status race_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const float* W,
+                                  float beta, int P, int L, int causal, void* O,
+                                  const race_shape* shape, void* state, size_t state_bytes,
+                                  race_stream_t stream);
+
 /* Backward pass: the exact gradients dQ, dK, dV of sum(O * dO) with W
  * held fixed (softmax, tanh and projection backward on both sides), and,
  * when dbeta (a device pointer to one float, 4-byte aligned) is not NULL,

@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "RaceError", "lib", "library_path", "race_attn_fwd", "race_attn_bwd", "race_softbucket_debug",
     "race_attn_state_bytes", "race_attn_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode",
-    "race_attn_decode_state_bytes", "race_bucket_stats_segments",
+    "race_attn_decode_state_bytes", "race_attn_fwd_noalloc", "race_bucket_stats_segments",
     "race_bucket_stats_debug", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = ("race_attn_fwd", "race_attn_bwd", "race_attn_state_bytes", "
                     "race_softbucket_debug", "race_status_string", "race_last_error", "race_profile_enable",
                     "race_profile_reset", "race_profile_report", "race_attn_decode_state_bytes",
                     "race_attn_decode_prefill_workspace_bytes", "race_attn_decode_prefill", "race_attn_decode",
-                    "race_bucket_stats_segments",
+                    "race_attn_fwd_noalloc", "race_attn_fwd_noalloc_scratch_bytes", "race_bucket_stats_segments",
                     "race_bucket_stats_debug")
 
 
@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.race_bucket_stats_segments.restype = i32
         L.race_bucket_stats_debug.argtypes = [sp, i32, i32, i32, vp, sz, vp, sz, vp, vp, vp, vp, vp]
         L.race_bucket_stats_debug.restype = i32
+        L.race_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp, sp, vp, sz, vp]
+        L.race_attn_fwd_noalloc.restype = i32
+        L.race_attn_fwd_noalloc_scratch_bytes.argtypes = []
+        L.race_attn_fwd_noalloc_scratch_bytes.restype = sz
         _LIB = L
     return _LIB
 
@@ -228,6 +232,20 @@ def race_attn_fwd(Q, K, V, W, beta, P, L, causal=False, O=None, state=None, work
         _check(lib().race_attn_fwd(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
                                    int(L), int(causal), _dev(O, "O"), ctypes.byref(shape), _dev(state, "state"),
                                    _bytes(state), _dev(workspace, "workspace"), _bytes(workspace), _stream(stream)))
+    return O, state
+
+
+def race_attn_fwd_noalloc(Q, K, V, W, beta, P, L, causal, O, state, stream=None):
+    """The allocation-free forward: O and state are the caller's tensors
+    (state sized by race_attn_state_bytes, or None); the library's own
+    device scratch replaces the workspace.  Nothing is allocated."""
+    shape = _shape_of(Q, W, L, P)
+    _like(Q, "Q", K=K, V=V, O=O)
+    _same_device(Q, W=W, state=state)
+    _check(lib().race_attn_fwd_noalloc(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(W, "W"), float(beta), int(P),
+                                       int(L), int(causal), _dev(O, "O"), ctypes.byref(shape),
+                                       _dev(state, "state") if state is not None else None, _bytes(state),
+                                       _stream(stream)))
     return O, state
 
 

@@ -540,9 +540,46 @@ size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int caus
 
 namespace {
 
+// ---- scratch of the allocation-free forward: one copy per GPU, held by
+// the code object until the process ends.  In host code the name `scratch`
+// is only a stand-in for the symbol; every use goes through the device
+// address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device ordinal; null until looked up
+
+race_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RACE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RACE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RACE_OK;
+}
+
+// Workspace the forward touches: the partial banks (non-causal) or segment
+// sums (causal), plus the state's own room when the caller passes no state.
+size_t fwd_workspace_used(const Plan& p, bool have_state) {
+  if (have_state) return p.causal ? align256(seg_bank_bytes(p)) : align256(part_bytes(p));
+  return workspace_bytes(p, false);
+}
+
+// Shared by race_attn_fwd (caller's workspace, at least the documented
+// race_attn_workspace_bytes) and race_attn_fwd_noalloc (the library's own
+// scratch, at least what this call touches).
 race_status fwd_common(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,
                        int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
-                       void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
+                       void* workspace, size_t workspace_bytes_in, race_stream_t stream, bool own_scratch) {
   g_last_error.clear();
   Plan p;
   race_status st = make_plan(shape, P, L, causal, &p, true);
@@ -555,14 +592,27 @@ race_status fwd_common(const void* Q, const void* K, const void* V, const float*
   const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
   if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) || overlaps(O, tbytes, V, tbytes))
     return fail(RACE_ERR_INVALID_ARG, "O overlaps an input");
-  const size_t need_ws = workspace_bytes(p, false);
-  if (!workspace || workspace_bytes_in < need_ws)
-    return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+  if (own_scratch) {
+    const size_t used = fwd_workspace_used(p, state != nullptr);
+    if (used > workspace_bytes_in)
+      return fail(RACE_ERR_WORKSPACE, "this call needs " + std::to_string(used) +
+                                          " bytes of scratch, above the " + std::to_string(workspace_bytes_in) +
+                                          " bytes the allocation-free forward holds");
+  } else {
+    const size_t need_ws = workspace_bytes(p, false);
+    if (!workspace || workspace_bytes_in < need_ws)
+      return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
+  }
+  const size_t need_ws = own_scratch ? 0 : workspace_bytes(p, false);
   const size_t need_state = state_bytes(p);
   if (state && state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
   if (state && (overlaps(state, need_state, O, tbytes) || overlaps(state, need_state, workspace, need_ws)))
     return fail(RACE_ERR_INVALID_ARG, "state overlaps O or the workspace");
+  if (own_scratch) {
+    // every argument check has passed: look up this device's scratch
+    if ((st = scratch_address(&workspace)) != RACE_OK) return st;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
@@ -591,7 +641,16 @@ race_status race_attn_fwd(const void* Q, const void* K, const void* V, const flo
                           int causal, void* O, const race_shape* shape, void* state, size_t state_bytes_in,
                           void* workspace, size_t workspace_bytes_in, race_stream_t stream) {
   return fwd_common(Q, K, V, W, beta, P, L, causal, O, shape, state, state_bytes_in, workspace, workspace_bytes_in,
-                    stream);
+                    stream, false);
+}
+
+size_t race_attn_fwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+race_status race_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const float* W, float beta, int P,
+                                  int L, int causal, void* O, const race_shape* shape, void* state,
+                                  size_t state_bytes_in, race_stream_t stream) {
+  return fwd_common(Q, K, V, W, beta, P, L, causal, O, shape, state, state_bytes_in, nullptr, kScratchBytes, stream,
+                    true);
 }
 
 race_status race_attn_bwd(const void* Q, const void* K, const void* V, const float* W, float beta, int P, int L,

@@ -89,6 +89,13 @@ int main(void) {
                        NULL) == RACE_ERR_INVALID_ARG,
          "dW overlaps W");
 
+  /* allocation-free forward: argument checks run before any device call */
+  EXPECT(race_attn_fwd_noalloc_scratch_bytes() == (size_t)64 << 20, "allocation-free scratch size");
+  EXPECT(race_attn_fwd_noalloc(NULL, K, V, W, 1.0f, 4, 2, 0, O, &s, NULL, 0, NULL) == RACE_ERR_INVALID_ARG,
+         "allocation-free forward: NULL Q");
+  EXPECT(race_attn_fwd_noalloc(Q, K, V, W, 1.0f, 9, 2, 0, O, &s, NULL, 0, NULL) == RACE_ERR_INVALID_ARG,
+         "allocation-free forward: P = 9");
+
   EXPECT(race_attn_decode_state_bytes(&s, 4, 2) == (size_t)4 * 32 * 129 * 4, "decode state bytes");
   EXPECT(strcmp(race_status_string(RACE_OK), "RACE_OK") == 0, "status string");
   EXPECT(strcmp(race_status_string(RACE_ERR_WORKSPACE), "RACE_ERR_WORKSPACE") == 0, "status string");
