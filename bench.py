@@ -92,6 +92,10 @@ def parse():
                     help="also compute dL/dW in every backward (tables learned)")
     ap.add_argument("--per-head", action="store_true",
                     help="one set of tables per head (W is [H][L][P][d])")
+    ap.add_argument("--P", type=int, default=None,
+                    help="hyperplanes per table instead of the workload's (e.g. the scaling settings (2, 2), (3, 3), "
+                         "(4, 4) of the single-layer runs at d = 128)")
+    ap.add_argument("--L", type=int, default=None, help="tables instead of the workload's")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="oracle sample length (default: sized for about 20 s of CPU work)")
     ap.add_argument("--graph", action="store_true",
@@ -268,6 +272,11 @@ def main():
     if args.decode:
         return bench_decode(args)
     w = ri.WORKLOADS[4 if args.workload is None else args.workload]
+    if args.P is not None or args.L is not None:
+        from dataclasses import replace
+        P = w.P if args.P is None else args.P
+        L = w.L if args.L is None else args.L
+        w = replace(w, P=P, L=L, name=f"{w.name}_p{P}l{L}")
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     race.lib()
     dev = "cuda"
@@ -366,7 +375,7 @@ def main():
         print("# timing the fp64 oracle on a CPU sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, w, args.cpu_sample_tokens)
 
-    if w.key == 4:
+    if w.key == 4 and args.P is None and args.L is None:
         metric = "RACE layer fwd+bwd tokens/s at N=12M, H=4, d=128; % of HBM roofline"
     else:
         metric = f"RACE layer {'fwd+bwd' if train else 'fwd'} tokens/s, workload {w.name}; % of HBM roofline"

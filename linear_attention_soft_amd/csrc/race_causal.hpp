@@ -154,8 +154,9 @@ __device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int L,
 //   B[c][lr] += sum_b X_b[c] phi_B,b[lr],  m[lr] += sum_b phi_B,b[lr] xe_b
 // and, one chunk behind, dX = dPre . W for the wave's column tiles.  Rows of
 // the next chunk are staged into double-buffered LDS by the whole workgroup
-// (one barrier per chunk); X^T tiles for the bank update come out of an MFMA
-// with an identity operand.
+// (one barrier per chunk); X^T operands of the bank update come from the
+// staged rows through transposing LDS loads (bf16; float32 I/O multiplies the
+// rows by an identity operand).
 template <typename T, class G, bool REV, int TG>
 __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
   using C = TWCfg<T, G, REV>;
@@ -476,20 +477,32 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
         }
 #pragma unroll
       for (int sp = 0; sp < C::NXS; ++sp) {
-        const T* xf = S.XF[bb][sp] + n * FS + 8 * h;
+        if constexpr (std::is_same<T, bf16>::value) {
+          // X^T operands straight from the staged rows: transposing LDS loads
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
-          f32x16 xt = zero16();
-          E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct)), idn[0], xt);
-          E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct + 1)), idn[1], xt);
+          for (int ct = 0; ct < G::CT; ++ct)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            float x8[8];
+            for (int s = 0; s < 2; ++s) {
+              const frag xa = load_kcol_tr(S.XF[bb][sp], FS, 16 * s, 32 * ct, kmap_run_pos);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x8[i] = xt[8 * s + i];
-            const frag xa = E::pack(x8);
+              for (int at = 0; at < ATU; ++at) E::mma(xa, pb[s][at], acc[at][ct]);
+            }
+        } else {
+          const T* xf = S.XF[bb][sp] + n * FS + 8 * h;
 #pragma unroll
-            for (int at = 0; at < ATU; ++at) E::mma(xa, pb[s][at], acc[at][ct]);
+          for (int ct = 0; ct < G::CT; ++ct) {
+            f32x16 xt = zero16();
+            E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct)), idn[0], xt);
+            E::mma(*reinterpret_cast<const frag*>(xf + 16 * (2 * ct + 1)), idn[1], xt);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              float x8[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) x8[i] = xt[8 * s + i];
+              const frag xa = E::pack(x8);
+#pragma unroll
+              for (int at = 0; at < ATU; ++at) E::mma(xa, pb[s][at], acc[at][ct]);
+            }
           }
         }
       }

@@ -598,19 +598,37 @@ __device__ __forceinline__ void assign_partials_half(const float (&phi)[16], con
                                                      float (&out)[1 + G::PE]) {
   static_assert(R0 % 32 == 0 && G::R == 64, "half tables of 64 corners");
   const int h = lane_id() >> 5;
-  const float sgn2 = h ? 1.f : -1.f;
+  // register v holds corner r = R0 % 64 + 8 (v / 4) + 4 h + v % 4: bits 0, 1
+  // of r are bits 0, 1 of v, bits 3, 4 of r bits 2, 3 of v, bit 2 is h and
+  // bit 5 is fixed per half.  Signed sums over one bit at a time by a
+  // butterfly over the bits of v.
+  float a[8], m0 = 0.f;
 #pragma unroll
-  for (int i = 0; i <= G::PE; ++i) out[i] = 0.f;
+  for (int j = 0; j < 8; ++j) {
+    const float lo = phi[2 * j] * dphi[2 * j], hi = phi[2 * j + 1] * dphi[2 * j + 1];
+    a[j] = lo + hi;
+    m0 += hi - lo;                       // bit 0 of v set: +, clear: -
+  }
+  float b[4], m1 = 0.f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r0 = (R0 + 8 * (v >> 2) + (v & 3)) % G::R;
-    const float pd = phi[v] * dphi[v];
-    out[0] += pd;
+  for (int j = 0; j < 4; ++j) {
+    b[j] = a[2 * j] + a[2 * j + 1];
+    m1 += a[2 * j + 1] - a[2 * j];       // bit 1 of v
+  }
+  const float c0 = b[0] + b[1], c1 = b[2] + b[3];
+  const float m2 = (b[1] - b[0]) + (b[3] - b[2]);   // bit 2 of v
+  const float sum = c0 + c1, m3 = c1 - c0;          // bit 3 of v
+  out[0] = sum;
 #pragma unroll
-    for (int t = 0; t < G::PE; ++t) {
-      if (t == 2) out[1 + t] += sgn2 * pd;
-      else out[1 + t] += ((r0 >> t) & 1) ? pd : -pd;
-    }
+  for (int t = 0; t < G::PE; ++t) {
+    float v;
+    if (t == 0) v = m0;
+    else if (t == 1) v = m1;
+    else if (t == 2) v = h ? sum : -sum;
+    else if (t == 3) v = m2;
+    else if (t == 4) v = m3;
+    else v = ((R0 % G::R) >> t) & 1 ? sum : -sum;
+    out[1 + t] = v;
   }
 #pragma unroll
   for (int i = 0; i <= G::PE; ++i) out[i] += xor32(out[i]);
@@ -648,6 +666,37 @@ __device__ __forceinline__ void assign_backward(const float (&phi)[G::LRP / 2], 
                                                 const float (&pre)[G::NHP], float beta, float (&dpre)[G::NHP],
                                                 float& bterm) {
   assign_backward_rows<G, 0, G::LRP>(phi, dphi, pre, beta, dpre, bterm);
+}
+
+// MFMA operand (bf16) with k over 16 consecutive rows of a row-major LDS tile
+// and one column per lane: lane (n, h) receives M[r0 + kmap(0, h, i)][col0 + n]
+// for i = 0..7.  Two transposing LDS loads (ds_read_b64_tr_b16): within each
+// group of 16 lanes, lane 4a + b receives element b of the 8-byte pieces that
+// lanes a, a + 4, a + 8 and a + 12 address (measured on gfx950).  So lane L
+// addresses row r0 + 4 (L / 32) + (L / 4) % 4 (+ 8 for the second load) at
+// the run of 4 columns col0 + 16 ((L / 16) % 2) + 4 (L % 4); pos(c) is the
+// storage position of the run that starts at column c (c a multiple of 4).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <class Pos>
+__device__ __forceinline__ bf16x8 load_kcol_tr(const bf16* tile, int stride, int r0, int col0, Pos pos) {
+  const int L = lane_id();
+  const int row = r0 + 4 * (L >> 5) + ((L >> 2) & 3);
+  const int col = col0 + 16 * ((L >> 4) & 1) + 4 * (L & 3);
+  const bf16* p0 = tile + row * stride + pos(col);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * stride));
+  // whole-vector reinterpretation (per-element casts were packed wrongly)
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Storage position of a run of 4 columns starting at c in a row kept in kmap
+// frag order (column 16 q + 8 hh + e at 16 q + 8 (e / 4) + 4 hh + e % 4):
+// runs 0, 1, 2, 3 of a 16-column group sit at runs 0, 2, 1, 3.
+__device__ __forceinline__ int kmap_run_pos(int c) {
+  const int r = (c >> 2) & 3;
+  return (c & ~15) + 4 * (((r & 1) << 1) | (r >> 1));
 }
 
 // Order this wave's LDS writes before its later LDS reads of other lanes'

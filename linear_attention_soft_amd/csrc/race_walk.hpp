@@ -79,10 +79,19 @@ struct RWCfg {
   static constexpr bool XSPLIT = (MODE == W_GSUM || MODE == W_DV) && Eng<T>::NSPLIT == 2;
   static constexpr bool MASS = MODE == W_SEGSUM || MODE == W_GSUM || MODE == W_FWD;
   static constexpr bool XDEN = MODE == W_GSUM || MODE == W_DV;   // X rows divided by den
-  static constexpr int FR = G::KL * 16 + 8;     // frag-ordered feature row per token (elements)
+  // frag-ordered feature row per token and bank-wave X tile row (elements):
+  // with bf16, rows 12 dwords apart (mod 64 banks) keep both the 16-byte row
+  // reads and the transposing loads (4 rows x 8 dwords per 16 lanes) free
+  // of bank conflicts
+  static constexpr int FR = G::KL * 16 + (std::is_same<T, bf16>::value ? 24 : 8);
   static constexpr int TS = WC + 8;             // transposed feature row per bucket (elements)
-  static constexpr int XSP = 32 + 8;            // bank-wave X tile row (elements)
+  static constexpr int XSP = 32 + (std::is_same<T, bf16>::value ? 24 : 8);
   static constexpr int NXS = XSPLIT ? 2 : 1;
+  // bf16: the state-role features are kept in token-major rows only (PhiB)
+  // and read transposed (bank-update operands, bucket masses) with
+  // transposing LDS loads; float32 keeps a transposed copy (PhiBT)
+  static constexpr bool TRLOAD = std::is_same<T, bf16>::value;
+  static constexpr bool ROWS_B = HAS_A || TRLOAD;   // PhiB rows are written
   // The float32 bank enters the readout rounded once to the MFMA type (its
   // relative error 2^-9 matches the rounding of the bf16 outputs); with
   // BANK_LO the rounding residual is contracted as well.
@@ -142,30 +151,53 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
     }
     return;
   }
-  if (C::HAS_A) {
+  if constexpr (C::ROWS_B) {
     T* dst = PhiB + b * WC * C::FR + n * C::FR + (R0 / 16) * 16 + h * 8;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) *reinterpret_cast<frag*>(dst + 16 * q) = fq[q];
   }
-  T* bt = PhiBT + b * G::LRP * C::TS;
+  if constexpr (!C::TRLOAD) {
+    T* bt = PhiBT + b * G::LRP * C::TS;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bt[(R0 + kmap(q, h, i)) * C::TS + n] = fq[q][i];
+      for (int i = 0; i < 8; ++i) bt[(R0 + kmap(q, h, i)) * C::TS + n] = fq[q][i];
+  }
   if (C::MASS) {
     if (MODE == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv : 0.f;
     wave_lds_sync();
     // mass after the chunk = mass before + column sums of the rounded phi_B
     // (GSUM: weighted by h)
+    if constexpr (C::TRLOAD) {
+      // lane (n, h) sums the tokens kmap(s, h, i) of bucket row R0 + 32 at + n;
+      // the two halves then add their sums
+      const T* rows = PhiB + b * WC * C::FR;
 #pragma unroll
-    for (int r = 0; r < cdiv(WROWS, 64); ++r) {
-      const int row = R0 + 64 * r + lane;
-      if (64 * r + lane < WROWS) {
-        const T* src = bt + row * C::TS;
-        float s = 0.f;
+      for (int at = 0; at < WROWS / 32; ++at) {
+        float sm = 0.f;
 #pragma unroll
-        for (int t = 0; t < WC; ++t) s += (MODE == W_GSUM) ? (float)src[t] * hw[fw * WC + t] : (float)src[t];
-        mbuf[b * G::LRP + row] = mbuf[(b ^ 1) * G::LRP + row] + s;
+        for (int sidx = 0; sidx < 2; ++sidx) {
+          const frag v = load_kcol_tr(rows, C::FR, 16 * sidx, R0 + 32 * at, kmap_run_pos);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            sm += (MODE == W_GSUM) ? (float)v[i] * hw[fw * WC + 16 * sidx + kmap(0, h, i)] : (float)v[i];
+        }
+        sm += xor32(sm);
+        const int row = R0 + 32 * at + n;
+        if (h == 0) mbuf[b * G::LRP + row] = mbuf[(b ^ 1) * G::LRP + row] + sm;
+      }
+    } else {
+      const T* bt = PhiBT + b * G::LRP * C::TS;
+#pragma unroll
+      for (int r = 0; r < cdiv(WROWS, 64); ++r) {
+        const int row = R0 + 64 * r + lane;
+        if (64 * r + lane < WROWS) {
+          const T* src = bt + row * C::TS;
+          float s = 0.f;
+#pragma unroll
+          for (int t = 0; t < WC; ++t) s += (MODE == W_GSUM) ? (float)src[t] * hw[fw * WC + t] : (float)src[t];
+          mbuf[b * G::LRP + row] = mbuf[(b ^ 1) * G::LRP + row] + s;
+        }
       }
     }
   }
@@ -201,8 +233,8 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
 
   __shared__ frag Wf[G::NPT * G::KD * 64];
   __shared__ __attribute__((aligned(16))) T PhiA[C::HAS_A ? 2 * WC * FR : 8];
-  __shared__ __attribute__((aligned(16))) T PhiB[C::HAS_A ? 2 * WC * FR : 8];
-  __shared__ __attribute__((aligned(16))) T PhiBT[2 * G::LRP * TS];
+  __shared__ __attribute__((aligned(16))) T PhiB[C::ROWS_B ? 2 * WC * FR : 8];
+  __shared__ __attribute__((aligned(16))) T PhiBT[C::TRLOAD ? 8 : 2 * G::LRP * TS];
   __shared__ __attribute__((aligned(16))) T Xs[C::NM * C::NXS * WC * XSP];
   __shared__ float mbuf[C::MASS ? 2 * G::LRP : 1];
   __shared__ float dpart[MODE == W_FWD ? 2 * C::NWIN * WC : 1];
@@ -367,13 +399,22 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     wave_lds_sync();
     // X frags, k over tokens by kmap: lane (c, h) holds X[kmap(s, h, i)][c]
     frag xk[2], xl[2];
+    if constexpr (C::TRLOAD) {
+      auto plain = [](int c) { return c; };
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xk[s][i] = xs[kmap(s, h, i) * XSP + n];
-        if (C::XSPLIT) xl[s][i] = xs[WC * XSP + kmap(s, h, i) * XSP + n];
+      for (int s = 0; s < 2; ++s) {
+        xk[s] = load_kcol_tr(xs, XSP, 16 * s, 0, plain);
+        if (C::XSPLIT) xl[s] = load_kcol_tr(xs + WC * XSP, XSP, 16 * s, 0, plain);
       }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          xk[s][i] = xs[kmap(s, h, i) * XSP + n];
+          if (C::XSPLIT) xl[s][i] = xs[WC * XSP + kmap(s, h, i) * XSP + n];
+        }
+    }
 
     if constexpr (C::HAS_A) {
       const T* pA = PhiA + b * WC * FR + n * FR + h * 8;
@@ -473,13 +514,17 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
         frag af[G::AT];
 #pragma unroll
         for (int at = 0; at < G::AT; ++at) {
-          const T* r = bt + (32 * at + n) * TS + 16 * s + 4 * h;
-          const T4 lo4 = *reinterpret_cast<const T4*>(r);
-          const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
+          if constexpr (C::TRLOAD) {
+            af[at] = load_kcol_tr(PhiB + b * WC * FR, FR, 16 * s, 32 * at, kmap_run_pos);
+          } else {
+            const T* r = bt + (32 * at + n) * TS + 16 * s + 4 * h;
+            const T4 lo4 = *reinterpret_cast<const T4*>(r);
+            const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            af[at][i] = lo4[i];
-            af[at][4 + i] = hi4[i];
+            for (int i = 0; i < 4; ++i) {
+              af[at][i] = lo4[i];
+              af[at][4 + i] = hi4[i];
+            }
           }
         }
 #pragma unroll
