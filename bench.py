@@ -46,13 +46,19 @@ ROW_PASSES = {
     "race_causal_dv": 4,       # read K, Q, dO, write dV
     "race_causal_dq": 5,       # read Q, K, V, dO, write dQ
     "race_causal_dk": 5,       # read K, Q, dO, V, write dK
+    "race_static_fwd": 2,      # read Q, write O (one fixed bank)
+    "race_static_h": 2,        # read Q, dO
+    "race_static_dv": 2,       # read K, write dV
+    "race_static_dq": 3,       # read Q, dO, write dQ
+    "race_static_dk": 3,       # read K, V, write dK
 }
 
 
 # algorithmic flops per (token, head) of the causal walks' contractions, with
 # LR = L * 2^P buckets: the bank read out or contracted over columns (2 LR d),
 # the bank update (2 LR (d + 1)), and for the transposed walks dX = dPre W
-# (2 L P d); the chunked intra terms and the soft assignments are not counted
+# (2 L P d); the chunked intra terms and the soft assignments are not counted.
+# The static-bank walks (non-causal layer, wide tables) have no bank update.
 def causal_flops(kernel: str, L: int, P: int, d: int):
     LR = L << P
     upd = 2 * LR * (d + 1)
@@ -60,7 +66,11 @@ def causal_flops(kernel: str, L: int, P: int, d: int):
             "race_causal_fwd": 2 * LR * (d + 1) + upd, "race_causal_h": 2 * LR * (d + 1) + upd,
             "race_causal_dv": 2 * LR * d + upd,
             "race_causal_dq": 2 * LR * d + upd + 2 * L * P * d,
-            "race_causal_dk": 2 * LR * d + upd + 2 * L * P * d}.get(kernel)
+            "race_causal_dk": 2 * LR * d + upd + 2 * L * P * d,
+            "race_static_fwd": 2 * LR * (d + 1), "race_static_h": 2 * LR * (d + 1),
+            "race_static_dv": 2 * LR * d,
+            "race_static_dq": 2 * LR * d + 2 * L * P * d,
+            "race_static_dk": 2 * LR * d + 2 * L * P * d}.get(kernel)
 
 
 def source_hash() -> str:
@@ -96,6 +106,8 @@ def parse():
                     help="hyperplanes per table instead of the workload's (e.g. the scaling settings (2, 2), (3, 3), "
                          "(4, 4) of the single-layer runs at d = 128)")
     ap.add_argument("--L", type=int, default=None, help="tables instead of the workload's")
+    ap.add_argument("--variant", choices=("causal", "noncausal"), default=None,
+                    help="the other variant of the workload's layer (e.g. the non-causal layer at P = 6, L = 4)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="oracle sample length (default: sized for about 20 s of CPU work)")
     ap.add_argument("--graph", action="store_true",
@@ -277,6 +289,9 @@ def main():
         P = w.P if args.P is None else args.P
         L = w.L if args.L is None else args.L
         w = replace(w, P=P, L=L, name=f"{w.name}_p{P}l{L}")
+    if args.variant is not None and (args.variant == "causal") != w.causal:
+        from dataclasses import replace
+        w = replace(w, causal=args.variant == "causal", name=f"{w.name}_as_{args.variant}")
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     race.lib()
     dev = "cuda"
@@ -375,7 +390,7 @@ def main():
         print("# timing the fp64 oracle on a CPU sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, w, args.cpu_sample_tokens)
 
-    if w.key == 4 and args.P is None and args.L is None:
+    if w.key == 4 and args.P is None and args.L is None and args.variant in (None, "noncausal"):
         metric = "RACE layer fwd+bwd tokens/s at N=12M, H=4, d=128; % of HBM roofline"
     else:
         metric = f"RACE layer {'fwd+bwd' if train else 'fwd'} tokens/s, workload {w.name}; % of HBM roofline"
@@ -411,9 +426,9 @@ def main():
     if graph_ms is not None:
         out["graph_ms_per_step"] = graph_ms
         out["graph_tokens_per_s"] = tokens / (graph_ms * 1e-3)
-    fl = causal_flops(dname, w.L, w.P, w.d) if w.causal else None
+    fl = causal_flops(dname, w.L, w.P, w.d)
     if fl:
-        # the causal walks also sit far below the MFMA roofline: bf16 dense peak
+        # the walks also sit far below the MFMA roofline: bf16 dense peak
         tf = fl * w.B * w.H * w.N / (avg_ms * 1e-3) / 1e12
         peak = 2500.0 if w.dtype == "bf16" else 157.3
         out["roofline_mfma"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",

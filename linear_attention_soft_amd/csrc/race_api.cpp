@@ -147,6 +147,7 @@ struct Plan {
   int64_t B = 0, H = 0, N = 0, D = 0, BH = 0;
   int P = 0, L = 0, PE = 0, LR = 0, LRP = 0;
   bool causal = false;
+  bool nc_static = false;    // non-causal layer through the static-bank walks
   bool w_per_head = false;   // W is [H][L][P][d] instead of [L][P][d]
   // non-causal chunking
   int nchunk = 0;
@@ -167,10 +168,19 @@ const race::KernelSet* find_set(int dtype, int D, int PE, int LRP_min, bool caus
     const race::KernelSet& k = sets[i];
     if (k.dtype != dtype || k.D != D || k.PE != PE || k.LRP < LRP_min) continue;
     if (causal && (!k.w_fwd || !k.tw_dq)) continue;
-    if (!causal && !k.readout) continue;
-    if (!best || k.LRP < best->LRP) best = &k;
+    if (!causal && !k.readout && !k.w_fwd_st) continue;
+    // smallest padded bank; at equal size the non-causal kernels before the
+    // static-bank walks
+    if (!best || k.LRP < best->LRP || (k.LRP == best->LRP && !causal && k.readout && !best->readout)) best = &k;
   }
   return best;
+}
+
+void bind_set(Plan* p, const race::KernelSet* ks) {
+  p->ks = ks;
+  if (!ks) return;
+  p->LRP = ks->LRP;
+  p->nc_static = !p->causal && !ks->readout;
 }
 
 // Decode and prefill need the bucket reduce and the decode kernel only (every
@@ -232,9 +242,8 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
   p->w_per_head = s->w_per_head != 0;
   if (p->D != 64 && p->D != 128) return fail(RACE_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
   if (need_kernels) {
-    p->ks = find_set(p->dtype, (int)p->D, p->PE, p->LRP, p->causal);
+    bind_set(p, find_set(p->dtype, (int)p->D, p->PE, p->LRP, p->causal));
     if (!p->ks) return fail(RACE_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, d, P, L, causal)");
-    p->LRP = p->ks->LRP;
   }
   chunking(p->N, p->BH, kMinTilesPerWG, &p->nchunk, &p->chunk_tokens);
   race::causal_segmentation(p->N, p->BH, &p->nseg, &p->seg_tokens);
@@ -245,6 +254,8 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
 size_t bank_bytes(const Plan& p) { return (size_t)p.BH * p.LRP * (p.D + 1) * sizeof(float); }
 size_t part_bytes(const Plan& p) { return (size_t)p.BH * p.nchunk * p.LRP * (p.D + 1) * sizeof(float); }
 size_t seg_bank_bytes(const Plan& p) { return (size_t)p.BH * p.nseg * p.LRP * (p.D + 1) * sizeof(float); }
+// Non-causal partial banks: one per chunk, or per segment (static-bank walks).
+size_t nc_part_bytes(const Plan& p) { return p.nc_static ? seg_bank_bytes(p) : part_bytes(p); }
 size_t tok_bytes(const Plan& p) { return (size_t)p.BH * p.N * sizeof(float); }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -257,10 +268,10 @@ size_t state_bytes(const Plan& p) {
 // Causal backward workspace: h [BH][N], gradient segment sums and their
 // reverse scan [BH][nseg][LRP][d+1] each.
 // Per-wave shares of dL/dbeta: query side then key side.  Non-causal: 4
-// waves per (chunk, head); causal: one wave per 32 bucket rows per (segment,
-// head) (the transposed walks' waves).
+// waves per (chunk, head); causal and static-bank walks: one wave per 32
+// bucket rows per (segment, head) (the transposed walks' waves).
 int64_t dbeta_parts_per_side(const Plan& p) {
-  if (!p.causal) return (int64_t)p.BH * p.nchunk * 4;
+  if (!p.causal && !p.nc_static) return (int64_t)p.BH * p.nchunk * 4;
   return (int64_t)p.BH * p.nseg * (p.LRP / 32);
 }
 size_t dbeta_bytes(const Plan& p) { return align256(2 * (size_t)dbeta_parts_per_side(p) * sizeof(float)); }
@@ -300,9 +311,10 @@ size_t workspace_bytes(const Plan& p, bool bwd, bool dw = false, bool no_state =
   if (bwd && no_state) return workspace_bytes(p, true, dw, false) + rebuilt_state_bytes(p);
   if (bwd && dw) return workspace_bytes(p, true, false) + dw_bytes(p);
   if (!p.causal) {
-    size_t w = align256(part_bytes(p));
-    if (!bwd) w += align256(bank_bytes(p));          // bank when no state buffer is given
-    else w += align256(bank_bytes(p)) + dbeta_bytes(p);   // gradient bank dcontent, dmass; dbeta shares
+    size_t w = align256(nc_part_bytes(p));
+    if (!bwd) return w + align256(bank_bytes(p));   // bank when no state buffer is given
+    w += align256(bank_bytes(p)) + dbeta_bytes(p);  // gradient bank dcontent, dmass; dbeta shares
+    if (p.nc_static) w += 2 * align256(tok_bytes(p));   // h and Den of every query
     return w;
   }
   // forward: segment sums, and (when no state buffer is given) the segment
@@ -425,6 +437,21 @@ race_status causal_forward(const Plan& p, const void* Q, const void* K, const vo
 race_status noncausal_bank(const Plan& p, const void* K, const void* V, const float* W, float beta, float* part,
                            float* content, float* mass, hipStream_t s) {
   race_status st;
+  if (p.nc_static) {
+    // segment sums from the segment-sum walk, then their fixed-order sum
+    race::WArgs w = walk_args(p, W, beta);
+    w.B_src = K; w.X_src = V; w.bank_out = part;
+    {
+      ProfScope ps(s, "race_causal_segsum");
+      p.ks->w_segsum(w, dim3((unsigned)p.nseg, (unsigned)p.BH), s);
+    }
+    if ((st = check_launch("race_causal_segsum")) != RACE_OK) return st;
+    {
+      ProfScope ps(s, "race_bank_finalize");
+      launch_finalize(part, p.nseg, p, content, mass, s);
+    }
+    return check_launch("race_bank_finalize");
+  }
   race::NCArgs a{};
   a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.part = part;
@@ -512,6 +539,83 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
 }
 
+// Non-causal backward through the static-bank walks: Den and h from a
+// readout of the bank, the gradient bank as segment sums of Phi_Q^T [g | h]
+// and their fixed-order sum, then dV = Phi_K dcontent and the transposed
+// walks for dQ (bank of K, V) and dK (gradient bank).
+race_status static_backward(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                            const void* dO, void* dQ, void* dK, void* dV, float* dbeta, float* dW,
+                            const void* state, char* ws, hipStream_t s) {
+  race_status st;
+  const float* content = static_cast<const float*>(state);
+  const float* mass = content + (size_t)p.BH * p.LRP * p.D;
+  float* part = reinterpret_cast<float*>(ws);
+  char* after_part = ws + align256(nc_part_bytes(p));
+  float* dcontent = reinterpret_cast<float*>(after_part);
+  float* dmass = dcontent + (size_t)p.BH * p.LRP * p.D;
+  char* after_bank = after_part + align256(bank_bytes(p));
+  float* bparts = dbeta ? reinterpret_cast<float*>(after_bank) : nullptr;
+  float* h = reinterpret_cast<float*>(after_bank + dbeta_bytes(p));
+  float* den = reinterpret_cast<float*>(after_bank + dbeta_bytes(p) + align256(tok_bytes(p)));
+  char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
+  const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
+
+  // 1. Den and h = -(dO . Phi_Q content) / Den^2 of every query
+  race::WArgs w = walk_args(p, W, beta);
+  w.A_src = Q; w.dO = dO; w.bank_in = content; w.mass_in = mass; w.h_out = h; w.den_out = den;
+  {
+    ProfScope ps(s, "race_static_h");
+    p.ks->w_h_st(w, grid, s);
+  }
+  if ((st = check_launch("race_static_h")) != RACE_OK) return st;
+  // 2. gradient bank: segment sums of Phi_Q^T [g | h], summed in segment order
+  w = walk_args(p, W, beta);
+  w.B_src = Q; w.X_src = dO; w.den = den; w.hvec = h; w.bank_out = part;
+  {
+    ProfScope ps(s, "race_causal_gradsum");
+    p.ks->w_gsum(w, grid, s);
+  }
+  if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nseg, p, dcontent, dmass, s);
+  }
+  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
+  // 3. dV = Phi_K dcontent
+  w = walk_args(p, W, beta);
+  w.A_src = K; w.bank_in = dcontent; w.mass_in = dmass; w.out = dV;
+  {
+    ProfScope ps(s, "race_static_dv");
+    p.ks->w_dv_st(w, grid, s);
+  }
+  if ((st = check_launch("race_static_dv")) != RACE_OK) return st;
+  // 4. dQ, dK: transposed walks against the fixed banks
+  race::TWArgs t{};
+  t.W = tables(p, W); t.beta = beta; t.L = p.L; t.P = p.P; t.N = p.N; t.seg_tokens = p.seg_tokens; t.nseg = p.nseg;
+  t.den = den; t.hvec = h;
+  t.A_src = Q; t.U_src = dO; t.bank_in = content; t.mass_in = mass; t.dX = dQ; t.dbeta_part = bparts;
+  t.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
+  {
+    ProfScope ps(s, "race_static_dq");
+    p.ks->tw_dq_st(t, grid, s);
+  }
+  if ((st = check_launch("race_static_dq")) != RACE_OK) return st;
+  t.A_src = K; t.U_src = V; t.bank_in = dcontent; t.mass_in = dmass; t.dX = dK;
+  t.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
+  t.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
+  {
+    ProfScope ps(s, "race_static_dk");
+    p.ks->tw_dk_st(t, grid, s);
+  }
+  if ((st = check_launch("race_static_dk")) != RACE_OK) return st;
+  if (dbeta) {
+    ProfScope ps(s, "race_dbeta_finalize");
+    launch_dbeta_finalize(p, bparts, dbeta, s);
+  }
+  if ((st = check_launch("race_dbeta_finalize")) != RACE_OK) return st;
+  return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -519,8 +623,7 @@ extern "C" {
 size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal) {
   Plan p;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
-  const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
-  if (ks) p.LRP = ks->LRP;
+  bind_set(&p, find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal));
   return state_bytes(p);
 }
 
@@ -530,9 +633,7 @@ size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int caus
   const bool no_state = (is_bwd & RACE_WS_NO_STATE) != 0;
   if (phase < RACE_WS_FWD || phase > RACE_WS_BWD_DW || (no_state && phase == RACE_WS_FWD)) return 0;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
-  const race::KernelSet* ks = find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal);
-  if (ks) p.LRP = ks->LRP;
-  p.ks = ks;
+  bind_set(&p, find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal));
   return workspace_bytes(p, phase != RACE_WS_FWD, phase == RACE_WS_BWD_DW, no_state);
 }
 
@@ -570,7 +671,7 @@ race_status scratch_address(void** out) {
 // Workspace the forward touches: the partial banks (non-causal) or segment
 // sums (causal), plus the state's own room when the caller passes no state.
 size_t fwd_workspace_used(const Plan& p, bool have_state) {
-  if (have_state) return p.causal ? align256(seg_bank_bytes(p)) : align256(part_bytes(p));
+  if (have_state) return p.causal ? align256(seg_bank_bytes(p)) : align256(nc_part_bytes(p));
   return workspace_bytes(p, false);
 }
 
@@ -619,10 +720,19 @@ race_status fwd_common(const void* Q, const void* K, const void* V, const float*
   if (p.causal) return causal_forward(p, Q, K, V, W, beta, O, state, ws, s);
 
   float* part = reinterpret_cast<float*>(ws);
-  float* bank = state ? static_cast<float*>(state) : reinterpret_cast<float*>(ws + align256(part_bytes(p)));
+  float* bank = state ? static_cast<float*>(state) : reinterpret_cast<float*>(ws + align256(nc_part_bytes(p)));
   float* content = bank;
   float* mass = bank + (size_t)p.BH * p.LRP * p.D;
   if ((st = noncausal_bank(p, K, V, W, beta, part, content, mass, s)) != RACE_OK) return st;
+  if (p.nc_static) {
+    race::WArgs w = walk_args(p, W, beta);
+    w.A_src = Q; w.out = O; w.bank_in = content; w.mass_in = mass;
+    {
+      ProfScope ps(s, "race_static_fwd");
+      p.ks->w_fwd_st(w, dim3((unsigned)p.nseg, (unsigned)p.BH), s);
+    }
+    return check_launch("race_static_fwd");
+  }
   race::NCArgs r{};
   r.X = Q; r.out0 = O; r.W = tables(p, W); r.beta = beta; r.L = p.L; r.P = p.P; r.N = p.N;
   r.st_content = content; r.st_mass = mass; r.chunk_tokens = p.chunk_tokens; r.nchunk = p.nchunk;
@@ -729,6 +839,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
     state = sreg;
   }
   if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
+  if (p.nc_static) return static_backward(p, Q, K, V, W, beta, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
   char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
 
   const float* content = static_cast<const float*>(state);
@@ -927,7 +1038,7 @@ race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int c
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * DP1, DP1,
                          g + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.D, gscale, dcontent, dmass);
     } else {          // gradient bank dcontent [BH][LRP][d], dmass [BH][LRP]
-      const float* g = reinterpret_cast<const float*>(ws + align256(part_bytes(p)));
+      const float* g = reinterpret_cast<const float*>(ws + align256(nc_part_bytes(p)));
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * p.D,
                          (int)p.D, g + (size_t)p.BH * p.LRP * p.D, (int64_t)p.LRP, 1, nbank, L, P, p.PE,
                          (int)p.D, gscale, dcontent, dmass);

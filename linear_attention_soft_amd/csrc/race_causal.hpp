@@ -53,7 +53,9 @@ struct TWArgs {
   const void* X_src;      // state-role values: forward V; reverse dO (divided by den: g)
   const void* U_src;      // output-role values: forward dO; reverse V
   void* dX;               // dQ (forward) or dK (reverse)
-  const float* bank_in;   // [BH][nseg][LRP][d+1]: bank before (forward) / after (reverse) the segment
+  const float* bank_in;   // [BH][nseg][LRP][d+1]: bank before (forward) / after (reverse) the segment;
+                          // static walks: content [BH][LRP][d]
+  const float* mass_in;   // static walks: mass [BH][LRP]
   const float* den;       // [BH][N]
   const float* hvec;      // [BH][N]
   Tables W;
@@ -70,15 +72,19 @@ struct TWArgs {
 // a table at 2^PE = 64 (SPL = 2 waves per table, which exchange their
 // softmax-backward sums once per chunk).  The workgroup walks one (segment,
 // batch x head).
-template <typename T, class G, bool REV>
+template <typename T, class G, bool REV, bool STATIC = false>
 struct TWCfg {
+  // STATIC: the non-causal layer for wide banks: every token of the
+  // (batch, head) reads one fixed bank (segment index ignored); no state-role
+  // rows, no intra-chunk term, no bank update
+  static constexpr bool ST = STATIC;
   static constexpr int URP = 32;
   static constexpr int SPL = G::R > 32 ? G::R / 32 : 1;   // waves per table
   static_assert(SPL <= 2 && G::PE + 1 <= 8, "tables of at most 64 corners");
   static constexpr int NM = G::LRP / URP;             // waves
   static constexpr int ATU = URP / 32;                // 32-row tiles per wave
   static constexpr int NT = 64 * NM;
-  static constexpr bool XSPLIT = REV && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
+  static constexpr bool XSPLIT = REV && !STATIC && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
   static constexpr int NXS = XSPLIT ? 2 : 1;
   static constexpr int FS = G::D + 16 / (int)sizeof(T);   // staged row (elements)
   // Phi_B^T row (elements): an 88-byte stride keeps both its 2-byte transposed
@@ -96,17 +102,18 @@ struct TWCfg {
   static_assert(G::LRP % URP == 0, "windows of 32 rows");
 };
 
-template <typename T, class G, bool REV>
+template <typename T, class G, bool REV, bool STATIC = false>
 struct TWLds {
-  using C = TWCfg<T, G, REV>;
+  using C = TWCfg<T, G, REV, STATIC>;
+  static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
   typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
-  alignas(16) T PhiBT[C::NM][C::URP * C::TSP];   // wave-private Phi_B^T of the current chunk
+  alignas(16) T PhiBT[C::NM][STATIC ? 8 : C::URP * C::TSP];   // wave-private Phi_B^T of the current chunk
   alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
   alignas(16) T AR[2][WC * C::FS];               // output-role rows (projection operands)
-  alignas(16) T BR[2][WC * C::FS];               // state-role rows
+  alignas(16) T BR[2][SROWS];                    // state-role rows
   alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
-  alignas(16) T XF[2][C::NXS][WC * C::FS];       // X rows, kmap frag order (hi, lo)
+  alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
   alignas(16) float XS[C::SPL > 1 ? C::NM : 1][8][WC];   // half-table softmax-backward sums (SPL = 2)
@@ -157,9 +164,9 @@ __device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int L,
 // (one barrier per chunk); X^T operands of the bank update come from the
 // staged rows through transposing LDS loads (bf16; float32 I/O multiplies the
 // rows by an identity operand).
-template <typename T, class G, bool REV, int TG>
-__device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
-  using C = TWCfg<T, G, REV>;
+template <typename T, class G, bool REV, int TG, bool STATIC = false>
+__device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC>& S) {
+  using C = TWCfg<T, G, REV, STATIC>;
   using E = Eng<T>;
   using frag = typename E::frag;
   constexpr int R0 = TG * C::URP;
@@ -176,7 +183,9 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
   const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
   const int64_t nch = (s1 - s0 + WC - 1) / WC;
   const size_t rb = (size_t)bh * a.N;
-  const size_t bank_off = ((size_t)bh * a.nseg + seg) * G::LRP * DP1;
+  // bank rows: [d+1] per segment bank, or content rows [d] of the static bank
+  constexpr int BS = STATIC ? G::D : DP1;
+  const size_t bank_off = (STATIC ? (size_t)bh : (size_t)bh * a.nseg + seg) * G::LRP * BS;
   const T* Ag = static_cast<const T*>(a.A_src) + rb * G::D;
   const T* Bg = static_cast<const T*>(a.B_src) + rb * G::D;
   const T* Xg = static_cast<const T*>(a.X_src) + rb * G::D;
@@ -202,12 +211,13 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
   f32x16 acc[ATU][G::CT];
 #pragma unroll
   for (int at = 0; at < ATU; ++at) {
-    const size_t rowo = bank_off + (size_t)(R0 + 32 * at + n) * DP1;
+    const size_t rowo = bank_off + (size_t)(R0 + 32 * at + n) * BS;
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[at][ct][v] = a.bank_in[rowo + 32 * ct + 8 * (v >> 2) + 4 * h + (v & 3)];
-    if (h == 0) S.Mw[w][32 * at + n] = a.bank_in[rowo + G::D];
+    if (h == 0)
+      S.Mw[w][32 * at + n] = STATIC ? a.mass_in[(size_t)bh * G::LRP + R0 + 32 * at + n] : a.bank_in[rowo + G::D];
   }
 
   // ---- staging loads (chunk index clamped: loads never sit behind a branch)
@@ -221,11 +231,11 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
       const int idx = min(tid + C::NT * i, WC * CPR - 1);
       const int64_t row = min(t0 + idx / CPR, s1 - 1);
       const int cc = idx % CPR;
-      px[i] = *reinterpret_cast<const uint4*>(Xg + row * G::D + cc * EPC);
+      if (!STATIC) px[i] = *reinterpret_cast<const uint4*>(Xg + row * G::D + cc * EPC);
       pu[i] = *reinterpret_cast<const uint4*>(Ug + row * G::D + cc * EPC);
       pa[i] = *reinterpret_cast<const uint4*>(Ag + row * G::D + cc * EPC);
-      pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
-      pd[i] = den[row];
+      if (!STATIC) pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
+      if (!STATIC) pd[i] = den[row];
     }
     const int64_t row = min(t0 + n, s1 - 1);
     tk_h = hv[row];
@@ -241,10 +251,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
         const int r = idx / CPR, cc = idx % CPR;
         const bool ok = t0 + r < s1;
         *reinterpret_cast<uint4*>(&S.AR[bb][r * FS + cc * EPC]) = pa[i];
-        *reinterpret_cast<uint4*>(&S.BR[bb][r * FS + cc * EPC]) = pb[i];
+        if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[bb][r * FS + cc * EPC]) = pb[i];
         const T* xe8 = reinterpret_cast<const T*>(&px[i]);
         const T* ue8 = reinterpret_cast<const T*>(&pu[i]);
-        const float sc = REV ? 1.f / pd[i] : 1.f;
+        const float sc = (REV && !STATIC) ? 1.f / pd[i] : 1.f;
         // kmap frag order: column 16 q + 8 hh + e sits at 16 q + 8 (e / 4) + 4 hh + e % 4,
         // so a 16-byte chunk of bf16 goes out as two 8-byte halves
         T xh[EPC], xl[EPC], uu[EPC];
@@ -261,7 +271,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
           const int q = col >> 4, o = col & 15, hh = o >> 3, ee = o & 7;
           const int pos = r * FS + 16 * q + 8 * (ee >> 2) + 4 * hh;
           *reinterpret_cast<T4*>(&S.UF[bb][pos]) = *reinterpret_cast<const T4*>(&uu[4 * g4]);
-          *reinterpret_cast<T4*>(&S.XF[bb][0][pos]) = *reinterpret_cast<const T4*>(&xh[4 * g4]);
+          if (!STATIC) *reinterpret_cast<T4*>(&S.XF[bb][0][pos]) = *reinterpret_cast<const T4*>(&xh[4 * g4]);
           if (C::XSPLIT) *reinterpret_cast<T4*>(&S.XF[bb][1][pos]) = *reinterpret_cast<const T4*>(&xl[4 * g4]);
         }
       }
@@ -318,7 +328,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
       soft_assign_rows<G, R0, URP>(preA, beta2, a.L, uA, phA);
     }
-    {
+    if constexpr (!STATIC) {
       frag xb[G::KD];
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[bb][n * FS + 16 * q + 8 * h]);
@@ -365,16 +375,18 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
             E::mma(E::pack(v8), ub, dp[at]);
           }
         }
-        E::mma(*reinterpret_cast<const frag*>(xf + 16 * q), ub, mf);
+        if (!STATIC) E::mma(*reinterpret_cast<const frag*>(xf + 16 * q), ub, mf);
         if (C::XSPLIT) E::mma(*reinterpret_cast<const frag*>(xl + 16 * q), ub, mf);
       }
     }
     const float ue = S.TK[bb][1][n];
+    if constexpr (!STATIC) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
-      const bool keep = REV ? (tb >= n) : (tb <= n);
-      mf[v] = keep ? mf[v] + S.TK[bb][0][tb] * ue : 0.f;
+      for (int v = 0; v < 16; ++v) {
+        const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
+        const bool keep = REV ? (tb >= n) : (tb <= n);
+        mf[v] = keep ? mf[v] + S.TK[bb][0][tb] * ue : 0.f;
+      }
     }
     // mass term and intra part: dp[lr][a] += m[lr] ue_a + sum_b phi_B,b[lr] mf[b][a]
     {
@@ -385,7 +397,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
         for (int v = 0; v < 16; ++v) dp[at][v] += S.Mw[w][32 * at + 8 * (v >> 2) + 4 * h + (v & 3)] * ue;
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < (STATIC ? 0 : 2); ++s) {
         float m8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) m8[i] = mf[8 * s + i];
@@ -459,7 +471,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
     __builtin_amdgcn_sched_barrier(0);
     // bank update: B[c][lr] += sum_b X_b[c] phi_B,b[lr]; X^T tiles (lane = column,
     // registers = tokens in kmap order) from X rows times the identity
-    {
+    if constexpr (!STATIC) {
       const T* pt = S.PhiBT[w];
       frag pb[2][ATU];
 #pragma unroll
@@ -529,19 +541,19 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV>& S) {
   }
 }
 
-template <typename T, class G, bool REV, int TG>
-__device__ __forceinline__ void tw_dispatch(int w, const TWArgs& a, TWLds<T, G, REV>& S) {
+template <typename T, class G, bool REV, bool STATIC, int TG>
+__device__ __forceinline__ void tw_dispatch(int w, const TWArgs& a, TWLds<T, G, REV, STATIC>& S) {
   if (w == TG) {
-    tw_body<T, G, REV, TG>(a, S);
-  } else if constexpr (TG + 1 < TWCfg<T, G, REV>::NM) {
-    tw_dispatch<T, G, REV, TG + 1>(w, a, S);
+    tw_body<T, G, REV, TG, STATIC>(a, S);
+  } else if constexpr (TG + 1 < TWCfg<T, G, REV, STATIC>::NM) {
+    tw_dispatch<T, G, REV, STATIC, TG + 1>(w, a, S);
   }
 }
 
-template <typename T, class G, bool REV>
-__global__ __launch_bounds__((TWCfg<T, G, REV>::NT)) void race_walk_tw(TWArgs a) {
-  __shared__ TWLds<T, G, REV> S;
-  tw_dispatch<T, G, REV, 0>(threadIdx.x >> 6, a, S);
+template <typename T, class G, bool REV, bool STATIC = false>
+__global__ __launch_bounds__((TWCfg<T, G, REV, STATIC>::NT)) void race_walk_tw(TWArgs a) {
+  __shared__ TWLds<T, G, REV, STATIC> S;
+  tw_dispatch<T, G, REV, STATIC, 0>(threadIdx.x >> 6, a, S);
 }
 
 // ------------------------------------------------------------------ small kernels

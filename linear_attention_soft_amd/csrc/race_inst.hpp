@@ -71,9 +71,9 @@ struct Inst {
   static void walk(const WArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_walk_rw<T, G, MODE>), g, dim3(RWCfg<T, G, MODE>::NT), 0, s, a);
   }
-  template <bool REV>
+  template <bool REV, bool STATIC = false>
   static void tw(const TWArgs& a, dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_walk_tw<T, G, REV>), g, dim3(TWCfg<T, G, REV>::NT), 0, s, a);
+    hipLaunchKernelGGL((race_walk_tw<T, G, REV, STATIC>), g, dim3(TWCfg<T, G, REV, STATIC>::NT), 0, s, a);
   }
   static void h_from_o(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t s) {
     constexpr int LPT = D / (16 / (int)sizeof(T));
@@ -87,8 +87,9 @@ struct Inst {
   static void dw_partial(const DWArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_dw_partial<T, G>), g, dim3(256), 0, s, a);
   }
-  // nc: compile the non-causal kernels; causal: compile the causal ones
-  template <bool NC, bool CAUSAL>
+  // NC: compile the non-causal kernels; CAUSAL: the causal ones; NCST: the
+  // non-causal layer as static-bank walks (with the segment-sum walks)
+  template <bool NC, bool CAUSAL, bool NCST = false>
   static KernelSet set(int dtype) {
     KernelSet k{};
     k.dtype = dtype; k.D = D; k.PE = PE; k.LRP = LRP; k.NHP = G::NHP;
@@ -101,6 +102,11 @@ struct Inst {
       k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;
       k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>; k.w_fwd = walk<W_FWD>; k.w_h = walk<W_H>;
       k.w_dv = walk<W_DV>;
+    }
+    if constexpr (NCST) {
+      k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>;
+      k.w_fwd_st = walk<W_FWD_ST>; k.w_h_st = walk<W_H_ST>; k.w_dv_st = walk<W_DV_ST>;
+      k.tw_dq_st = tw<false, true>; k.tw_dk_st = tw<true, true>;
     }
     return k;
   }

@@ -4,7 +4,7 @@
 namespace race {
 const KernelSet* inst_bf16_d128_p6(int* count) {
   static const KernelSet sets[] = {
-      Inst<bf16, 128, 6, 256>::template set<false, true>(1),
+      Inst<bf16, 128, 6, 256>::template set<false, true, true>(1),
   };
   *count = (int)(sizeof(sets) / sizeof(sets[0]));
   return sets;

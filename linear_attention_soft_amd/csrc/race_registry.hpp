@@ -29,6 +29,11 @@ struct KernelSet {
   // causal walks (grid: segments x BH): readout layout, then transposed layout
   w_launch_fn w_segsum, w_gsum, w_fwd, w_h, w_dv;
   tw_launch_fn tw_dq, tw_dk;
+  // non-causal layer through static-bank walks (tables too wide for the
+  // non-causal kernels' waves; the segment-sum walks come with them); null
+  // when not compiled
+  w_launch_fn w_fwd_st, w_h_st, w_dv_st;
+  tw_launch_fn tw_dq_st, tw_dk_st;
   void (*h_from_o)(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t);
   // recurrent decode step (grid: BH)
   void (*decode)(const DArgs&, unsigned grid, hipStream_t);

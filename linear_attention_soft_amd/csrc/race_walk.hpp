@@ -30,6 +30,13 @@
 //   W_H       h = -(dO . y) / den^2 (y = O den), without O
 //   W_DV      reverse walk, output role K, state role Q, X = g:
 //             dV_j = sum_{t >= j} (phi_K,j . phi_Q,t) g_t
+// Static modes (the non-causal layer for bucket counts whose whole bank does
+// not fit one wave): every token reads one fixed bank per (batch, head) (the
+// segment index is ignored), with no intra-chunk term and no bank update,
+// so only output-role feature waves run:
+//   W_FWD_ST  O = Phi_Q content / Phi_Q mass
+//   W_H_ST    Den = Phi_Q mass and h = -(dO . Phi_Q content) / Den^2, both written
+//   W_DV_ST   dV = Phi_K dcontent
 #pragma once
 #include "race_device.hpp"
 
@@ -37,7 +44,7 @@ namespace race {
 
 constexpr int WC = 32;   // tokens per chunk
 
-enum { W_SEGSUM = 0, W_GSUM = 1, W_FWD = 2, W_H = 3, W_DV = 4 };
+enum { W_SEGSUM = 0, W_GSUM = 1, W_FWD = 2, W_H = 3, W_DV = 4, W_FWD_ST = 5, W_H_ST = 6, W_DV_ST = 7 };
 
 struct WArgs {
   const void* A_src;      // output-role token rows (FWD, H: Q; DV: K)
@@ -46,7 +53,9 @@ struct WArgs {
   const void* dO;         // H: dO rows of the output role
   void* out;              // FWD: O (NULL: only Den is written); DV: dV
   float* bank_out;        // SEGSUM, GSUM: [BH][nseg][LRP][d+1]
-  const float* bank_in;   // FWD, H, DV: [BH][nseg][LRP][d+1], bank before (after, DV) the segment
+  const float* bank_in;   // FWD, H, DV: [BH][nseg][LRP][d+1], bank before (after, DV) the segment;
+                          // static modes: content [BH][LRP][d]
+  const float* mass_in;   // static modes: mass [BH][LRP]
   const float* den;       // [BH][N]: GSUM, H, DV
   float* den_out;         // FWD: [BH][N]
   const float* hvec;      // GSUM: h [BH][N]
@@ -69,16 +78,22 @@ __host__ __device__ constexpr int div_le(int n, int cap) {
 
 template <typename T, class G, int MODE>
 struct RWCfg {
-  static constexpr bool HAS_A = MODE >= W_FWD;              // an output role is read out
-  static constexpr bool REV = MODE == W_DV;                 // walk from the segment end
-  static constexpr int NWIN = div_le(G::LRP / 32, HAS_A ? 2 : 4);   // row windows per role
+  static constexpr bool STATIC = MODE >= W_FWD_ST;          // one fixed bank, no update
+  static constexpr int BM = STATIC ? MODE - 3 : MODE;       // the walk's readout mode
+  static constexpr bool HAS_A = BM >= W_FWD;                // an output role is read out
+  static constexpr bool REV = BM == W_DV;                   // walk from the segment end
+  static constexpr int ROLES = (HAS_A && !STATIC) ? 2 : 1;  // feature roles
+  static constexpr int NWIN = div_le(G::LRP / 32, ROLES == 2 ? 2 : 4);   // row windows per role
   static constexpr int WROWS = G::LRP / NWIN;
-  static constexpr int NF = (HAS_A ? 2 : 1) * NWIN;         // feature waves
+  static constexpr int NF = ROLES * NWIN;                   // feature waves
   static constexpr int NM = G::CT;                          // bank waves
   static constexpr int NT = 64 * (NF + NM);
-  static constexpr bool XSPLIT = (MODE == W_GSUM || MODE == W_DV) && Eng<T>::NSPLIT == 2;
-  static constexpr bool MASS = MODE == W_SEGSUM || MODE == W_GSUM || MODE == W_FWD;
-  static constexpr bool XDEN = MODE == W_GSUM || MODE == W_DV;   // X rows divided by den
+  static constexpr bool XSPLIT = (BM == W_GSUM || BM == W_DV) && !STATIC && Eng<T>::NSPLIT == 2;
+  static constexpr bool MASS = (BM == W_SEGSUM || BM == W_GSUM || BM == W_FWD) && !STATIC;   // mass updates
+  static constexpr bool MBUF = MASS || (STATIC && BM != W_DV);   // a bucket mass is kept in LDS
+  static constexpr bool DEN = BM == W_FWD || (STATIC && BM == W_H);   // feature waves form Phi_A mass
+  static constexpr bool XDEN = (BM == W_GSUM || BM == W_DV) && !STATIC;   // X rows divided by den
+  static constexpr bool XROWS = !STATIC;                    // bank waves read X rows
   // frag-ordered feature row per token and bank-wave X tile row (elements):
   // with bf16, rows 12 dwords apart (mod 64 banks) keep both the 16-byte row
   // reads and the transposing loads (4 rows x 8 dwords per 16 lanes) free
@@ -91,7 +106,7 @@ struct RWCfg {
   // and read transposed (bank-update operands, bucket masses) with
   // transposing LDS loads; float32 keeps a transposed copy (PhiBT)
   static constexpr bool TRLOAD = std::is_same<T, bf16>::value;
-  static constexpr bool ROWS_B = HAS_A || TRLOAD;   // PhiB rows are written
+  static constexpr bool ROWS_B = !STATIC && (HAS_A || TRLOAD);   // PhiB rows are written
   // The float32 bank enters the readout rounded once to the MFMA type (its
   // relative error 2^-9 matches the rounding of the bf16 outputs); with
   // BANK_LO the rounding residual is contracted as well.
@@ -138,9 +153,10 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
     T* dst = PhiA + b * WC * C::FR + n * C::FR + (R0 / 16) * 16 + h * 8;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) *reinterpret_cast<frag*>(dst + 16 * q) = fq[q];
-    if (MODE == W_FWD) {
-      // den (inter part) over this window: rounded phi_A . mass before the chunk
-      const float* m = mbuf + (b ^ 1) * G::LRP + R0;
+    if (C::DEN) {
+      // den (inter part) over this window: rounded phi_A . mass before the
+      // chunk (static modes: the fixed mass, kept in buffer 1)
+      const float* m = mbuf + (C::STATIC ? 1 : (b ^ 1)) * G::LRP + R0;
       float d = 0.f;
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
@@ -151,6 +167,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
     }
     return;
   }
+  if constexpr (C::STATIC) return;   // static modes have no state role
   if constexpr (C::ROWS_B) {
     T* dst = PhiB + b * WC * C::FR + n * C::FR + (R0 / 16) * 16 + h * 8;
 #pragma unroll
@@ -164,7 +181,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
       for (int i = 0; i < 8; ++i) bt[(R0 + kmap(q, h, i)) * C::TS + n] = fq[q][i];
   }
   if (C::MASS) {
-    if (MODE == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv : 0.f;
+    if (C::BM == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv : 0.f;
     wave_lds_sync();
     // mass after the chunk = mass before + column sums of the rounded phi_B
     // (GSUM: weighted by h)
@@ -180,7 +197,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
           const frag v = load_kcol_tr(rows, C::FR, 16 * sidx, R0 + 32 * at, kmap_run_pos);
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            sm += (MODE == W_GSUM) ? (float)v[i] * hw[fw * WC + 16 * sidx + kmap(0, h, i)] : (float)v[i];
+            sm += (C::BM == W_GSUM) ? (float)v[i] * hw[fw * WC + 16 * sidx + kmap(0, h, i)] : (float)v[i];
         }
         sm += xor32(sm);
         const int row = R0 + 32 * at + n;
@@ -195,7 +212,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
           const T* src = bt + row * C::TS;
           float s = 0.f;
 #pragma unroll
-          for (int t = 0; t < WC; ++t) s += (MODE == W_GSUM) ? (float)src[t] * hw[fw * WC + t] : (float)src[t];
+          for (int t = 0; t < WC; ++t) s += (C::BM == W_GSUM) ? (float)src[t] * hw[fw * WC + t] : (float)src[t];
           mbuf[b * G::LRP + row] = mbuf[(b ^ 1) * G::LRP + row] + s;
         }
       }
@@ -234,30 +251,34 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   __shared__ frag Wf[G::NPT * G::KD * 64];
   __shared__ __attribute__((aligned(16))) T PhiA[C::HAS_A ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiB[C::ROWS_B ? 2 * WC * FR : 8];
-  __shared__ __attribute__((aligned(16))) T PhiBT[C::TRLOAD ? 8 : 2 * G::LRP * TS];
+  __shared__ __attribute__((aligned(16))) T PhiBT[(C::TRLOAD || C::STATIC) ? 8 : 2 * G::LRP * TS];
   __shared__ __attribute__((aligned(16))) T Xs[C::NM * C::NXS * WC * XSP];
-  __shared__ float mbuf[C::MASS ? 2 * G::LRP : 1];
-  __shared__ float dpart[MODE == W_FWD ? 2 * C::NWIN * WC : 1];
-  __shared__ float hpart[MODE == W_H ? 2 * C::NM * WC : 1];
-  __shared__ float hw[MODE == W_GSUM ? C::NF * WC : 1];
+  __shared__ float mbuf[C::MBUF ? 2 * G::LRP : 1];
+  __shared__ float dpart[C::DEN ? 2 * C::NWIN * WC : 1];
+  __shared__ float hpart[C::BM == W_H ? 2 * C::NM * WC : 1];
+  __shared__ float hw[C::BM == W_GSUM ? C::NF * WC : 1];
 
   const int64_t seg = blockIdx.x, bh = blockIdx.y;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const int64_t s0 = seg * a.seg_tokens, s1 = min(a.N, s0 + a.seg_tokens);
   const int64_t nch = (s1 - s0 + WC - 1) / WC;
   const size_t rb = (size_t)bh * a.N;
-  const size_t bank_off = ((size_t)bh * a.nseg + seg) * G::LRP * DP1;
+  // bank rows: [d+1] per segment bank, or content rows [d] of the static bank
+  constexpr int BS = C::STATIC ? G::D : DP1;
+  const size_t bank_off = (C::STATIC ? (size_t)bh : (size_t)bh * a.nseg + seg) * G::LRP * BS;
   const bool is_f = w < C::NF;
   // feature wave: role and window; bank wave: column tile
-  const bool role_b = C::HAS_A ? (w >= C::NWIN) : true;
+  const bool role_b = C::STATIC ? false : (C::HAS_A ? (w >= C::NWIN) : true);
   const int win = w % C::NWIN;
   const int ct = w - C::NF;
 
   build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
-  if (C::MASS && is_f && role_b) {
+  if ((C::MASS && is_f && role_b) || (C::STATIC && C::MBUF && is_f)) {
     for (int r = lane; r < C::WROWS; r += 64) {
       const int row = win * C::WROWS + r;
-      mbuf[G::LRP + row] = (MODE == W_FWD) ? a.bank_in[bank_off + (size_t)row * DP1 + G::D] : 0.f;
+      mbuf[G::LRP + row] = C::STATIC            ? a.mass_in[(size_t)bh * G::LRP + row]
+                           : (C::BM == W_FWD) ? a.bank_in[bank_off + (size_t)row * DP1 + G::D]
+                                              : 0.f;
     }
   }
 
@@ -273,7 +294,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     auto load = [&](int64_t k, frag(&xf)[G::KD], float& hv) {
       const int64_t t0 = chunk_t0<C::REV>(s0, nch, k < nch ? k : nch - 1);
       const int64_t row = min(t0 + n, s1 - 1);
-      if (MODE == W_GSUM) hv = hsrc[row];
+      if (C::BM == W_GSUM) hv = hsrc[row];
       load_row_frags_nb<T, G>(src + row * G::D, xf);
     };
     auto feat = [&](int64_t k, const frag(&xf)[G::KD], float hv) {
@@ -298,7 +319,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       if (k + 2 < nch) feat(k + 2, xa, ha);
       __syncthreads();
     }
-    if (C::MASS && role_b && (MODE == W_SEGSUM || MODE == W_GSUM)) {
+    if (C::MASS && role_b && (C::BM == W_SEGSUM || C::BM == W_GSUM)) {
       const int fb = (int)((nch - 1) & 1);
       for (int r = lane; r < C::WROWS; r += 64) {
         const int row = win * C::WROWS + r;
@@ -312,19 +333,19 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   f32x16 st[G::AT];
 #pragma unroll
   for (int at = 0; at < G::AT; ++at) {
-    if (MODE == W_SEGSUM || MODE == W_GSUM) {
+    if (C::BM == W_SEGSUM || C::BM == W_GSUM) {
       st[at] = zero16();
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-        st[at][v] = a.bank_in[bank_off + (size_t)lr * DP1 + 32 * ct + n];
+        st[at][v] = a.bank_in[bank_off + (size_t)lr * BS + 32 * ct + n];
       }
     }
   }
   T* xs = Xs + ct * C::NXS * WC * XSP;
   const T* Xg = static_cast<const T*>(a.X_src) + rb * G::D + 32 * ct;
-  const T* dOg = (MODE == W_H) ? static_cast<const T*>(a.dO) + rb * G::D + 32 * ct : nullptr;
+  const T* dOg = (C::BM == W_H) ? static_cast<const T*>(a.dO) + rb * G::D + 32 * ct : nullptr;
   const float* den = a.den + rb;
 
   // prefetch registers: X row slices (+ den of their rows), dO slices (H)
@@ -333,14 +354,16 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   typename E::vec4 dor[4];
   auto prefetch = [&](int64_t k) {
     const int64_t t0 = chunk_t0<C::REV>(s0, nch, k);
+    if constexpr (C::XROWS) {
 #pragma unroll
-    for (int it = 0; it < XIT; ++it) {
-      const int flat = it * 64 + lane;
-      const int64_t row = min(t0 + flat / CPR, s1 - 1);
-      xr[it] = *reinterpret_cast<const uint4*>(Xg + row * G::D + (flat % CPR) * EPC);
-      if (C::XDEN) xd[it] = den[row];
+      for (int it = 0; it < XIT; ++it) {
+        const int flat = it * 64 + lane;
+        const int64_t row = min(t0 + flat / CPR, s1 - 1);
+        xr[it] = *reinterpret_cast<const uint4*>(Xg + row * G::D + (flat % CPR) * EPC);
+        if (C::XDEN) xd[it] = den[row];
+      }
     }
-    if (MODE == W_H) {
+    if (C::BM == W_H) {
       const int64_t row = min(t0 + n, s1 - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -351,25 +374,26 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   __syncthreads();   // projection frags, initial mass
   __syncthreads();   // stage of chunk 0
 
+  float dn_prev = 1.f;   // static H: Den of the previous chunk's token (ct = 0 wave)
   for (int64_t k = 0; k < nch; ++k) {
     const int b = (int)(k & 1);
     const int64_t t0 = chunk_t0<C::REV>(s0, nch, k);
     const int64_t tok = t0 + n;
     const bool valid = tok < s1;
     // H: finish h of the previous chunk from the column-slice partial dots
-    if (MODE == W_H && ct == 0 && k > 0 && h == 0) {
+    if (C::BM == W_H && ct == 0 && k > 0 && h == 0) {
       const int64_t pt = chunk_t0<C::REV>(s0, nch, k - 1) + n;
       if (pt < s1) {
         float s = 0.f;
 #pragma unroll
         for (int m = 0; m < C::NM; ++m) s += hpart[((b ^ 1) * C::NM + m) * WC + n];
-        const float dd = den[pt];
+        const float dd = C::STATIC ? dn_prev : den[pt];
         a.h_out[rb + pt] = -s / (dd * dd);
       }
     }
     // stage this chunk's X slice (rows past the segment end are zero)
 #pragma unroll
-    for (int it = 0; it < XIT; ++it) {
+    for (int it = 0; it < (C::XROWS ? XIT : 0); ++it) {
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const bool ok = t0 + row < s1;
@@ -390,7 +414,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       }
     }
     typename E::vec4 dcur[4];
-    if (MODE == W_H) {
+    if (C::BM == W_H) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) dcur[j] = dor[j];
     }
@@ -399,7 +423,9 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     wave_lds_sync();
     // X frags, k over tokens by kmap: lane (c, h) holds X[kmap(s, h, i)][c]
     frag xk[2], xl[2];
-    if constexpr (C::TRLOAD) {
+    if constexpr (!C::XROWS) {
+      // static modes read no X rows
+    } else if constexpr (C::TRLOAD) {
       auto plain = [](int c) { return c; };
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -425,13 +451,13 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
 #pragma unroll
       for (int q = 0; q < 2 && q < G::KL; ++q) {
         fa[q] = *reinterpret_cast<const frag*>(pA + 16 * q);
-        fb[q] = *reinterpret_cast<const frag*>(pB + 16 * q);
+        if (!C::STATIC) fb[q] = *reinterpret_cast<const frag*>(pB + 16 * q);
       }
 #pragma unroll
       for (int q = 0; q < G::KL; ++q) {
         if (q + 2 < G::KL) {
           fa[(q + 2) % 3] = *reinterpret_cast<const frag*>(pA + 16 * (q + 2));
-          fb[(q + 2) % 3] = *reinterpret_cast<const frag*>(pB + 16 * (q + 2));
+          if (!C::STATIC) fb[(q + 2) % 3] = *reinterpret_cast<const frag*>(pB + 16 * (q + 2));
         }
         float v8[8];
 #pragma unroll
@@ -444,36 +470,46 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
         } else {
           E::mma(E::pack(v8), fa[q % 3], y);
         }
-        E::mma(fb[q % 3], fa[q % 3], sc);
+        if (!C::STATIC) E::mma(fb[q % 3], fa[q % 3], sc);
       }
       // intra: sc[tok_b][tok_a] = phi_B . phi_A, kept for tok_b <= tok_a (>= on reverse walks)
       float dsum = 0.f;
+      if constexpr (!C::STATIC) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool keep = C::REV ? (tb >= n) : (tb <= n);
-        sc[v] = keep ? sc[v] : 0.f;
-        dsum += sc[v];
+        for (int v = 0; v < 16; ++v) {
+          const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
+          const bool keep = C::REV ? (tb >= n) : (tb <= n);
+          sc[v] = keep ? sc[v] : 0.f;
+          dsum += sc[v];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          float s8[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8[i] = sc[8 * s + i];
+          const frag sb = E::pack(s8);
+          E::mma(xk[s], sb, y);
+          if (C::XSPLIT) E::mma(xl[s], sb, y);
+        }
       }
+      // static H: Den of this chunk's tokens from the feature waves' parts
+      if (C::STATIC && C::BM == W_H && ct == 0 && h == 0) {
+        float dn = 0.f;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float s8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s8[i] = sc[8 * s + i];
-        const frag sb = E::pack(s8);
-        E::mma(xk[s], sb, y);
-        if (C::XSPLIT) E::mma(xl[s], sb, y);
+        for (int p = 0; p < C::NWIN; ++p) dn += dpart[(b * C::NWIN + p) * WC + n];
+        dn_prev = dn;
+        if (valid) a.den_out[rb + tok] = dn;
       }
       // y: lane (tok, h) holds columns 32 ct + 8 j + 4 h + kk
-      if (MODE == W_FWD || MODE == W_DV) {
+      if (C::BM == W_FWD || C::BM == W_DV) {
         float scale = 1.f;
-        if (MODE == W_FWD) {
+        if (C::BM == W_FWD) {
           dsum += xor32(dsum);
           float dn = dsum;
 #pragma unroll
           for (int p = 0; p < C::NWIN; ++p) dn += dpart[(b * C::NWIN + p) * WC + n];
           scale = 1.f / dn;
-          if (ct == 0 && h == 0 && valid) a.den_out[rb + tok] = dn;
+          if (a.den_out && ct == 0 && h == 0 && valid) a.den_out[rb + tok] = dn;
         }
         // stage the 32 x 32 output tile in the X tile, then store 64-byte row pieces
 #pragma unroll
@@ -495,7 +531,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
             if (t0 + row < s1) *reinterpret_cast<uint4*>(og + (t0 + row) * G::D + ch * EPC) = v;
           }
         }
-      } else if (MODE == W_H) {
+      } else if (C::BM == W_H) {
         float part = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -506,7 +542,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       }
     }
     // bank update: S[lr][c] += sum_tok Phi_B[tok][lr] X[tok][c]
-    {
+    if constexpr (!C::STATIC) {
       const T* bt = PhiBT + b * G::LRP * TS;
       typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -536,18 +572,18 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     }
     __syncthreads();
   }
-  if (MODE == W_H && ct == 0 && h == 0) {
+  if (C::BM == W_H && ct == 0 && h == 0) {
     const int b = (int)((nch - 1) & 1);
     const int64_t pt = chunk_t0<C::REV>(s0, nch, nch - 1) + n;
     if (pt < s1) {
       float s = 0.f;
 #pragma unroll
       for (int m = 0; m < C::NM; ++m) s += hpart[(b * C::NM + m) * WC + n];
-      const float dd = den[pt];
+      const float dd = C::STATIC ? dn_prev : den[pt];
       a.h_out[rb + pt] = -s / (dd * dd);
     }
   }
-  if (MODE == W_SEGSUM || MODE == W_GSUM) {
+  if (C::BM == W_SEGSUM || C::BM == W_GSUM) {
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
 #pragma unroll

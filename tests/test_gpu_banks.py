@@ -59,7 +59,7 @@ def _cmp(name, got, ref, tol, mass=False):
 
 @pytest.mark.parametrize("key,N,B,H,dtype,P,L", [
     (1, 1000, 1, 2, "f32", 3, 2), (4, 3000, 2, 1, "bf16", 4, 2), (3, 2100, 1, 2, "bf16", 3, 3),
-    (4, 2000, 1, 2, "bf16", 2, 2), (4, 1500, 1, 2, "f32", 4, 4),
+    (4, 2000, 1, 2, "bf16", 2, 2), (4, 1500, 1, 2, "f32", 4, 4), (5, 2113, 1, 2, "bf16", 6, 4),
 ])
 def test_noncausal_banks(key, N, B, H, dtype, P, L):
     w = replace(ri.WORKLOADS[key].with_size(N=N, B=B, H=H), causal=False, dtype=dtype, P=P, L=L)

@@ -48,6 +48,7 @@ def _inputs(w, per_head):
     (2, 650, 2, 2, "f32", True, True),
     (5, 1100, 1, 2, "bf16", True, True),
     (5, 1553, 1, 1, "bf16", True, False),
+    (5, 1200, 1, 2, "bf16", False, True),
 ])
 def test_dW_parity(key, N, B, H, dtype, causal, per_head):
     w = replace(ri.WORKLOADS[key].with_size(N=N, B=B, H=H), causal=causal, dtype=dtype)
@@ -125,9 +126,8 @@ def test_dW_edge_cases(causal):
     (the layer returns V whatever the assignments are, so dW = 0 up to the
     float32 rounding of terms that cancel) and beta = 0 (uniform assignments
     whatever W is: dW is exactly zero)."""
-    wide = 5 if causal else 4          # the P = 6, L = 4 kernels are compiled for the causal variant only
     for key, N, B, H, dtype, beta in [(1, 2, 1, 2, "f32", None), (2, 131, 2, 1, "f32", None),
-                                       (wide, 67, 1, 1, "bf16", None), (1, 1, 1, 2, "f32", None),
+                                       (5, 67, 1, 1, "bf16", None), (1, 1, 1, 2, "f32", None),
                                        (1, 300, 1, 1, "f32", 0.0)]:
         w = replace(ri.WORKLOADS[key].with_size(N=N, B=B, H=H), causal=causal, dtype=dtype)
         if beta is not None:

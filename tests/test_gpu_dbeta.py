@@ -49,6 +49,7 @@ def _ref(inp, w, dO):
     (1, 700, 1, 1, "f32", False, False),
     (3, 3000, 2, 2, "bf16", False, False),
     (4, 4000, 1, 2, "bf16", False, False),
+    (5, 2500, 1, 2, "bf16", False, False),
     (2, 600, 1, 2, "f32", True, False),
     (2, 600, 1, 2, "f32", True, True),
     (5, 1100, 1, 2, "bf16", True, True),
