@@ -34,7 +34,13 @@
  *  - Argument checks run on the host before anything is enqueued.  On any
  *    error nothing is enqueued and no output is written.
  *  - Supported: P in [1, 8]; L >= 1 with L * 2^max(P,3) <= 256;
- *    N >= 1; B*H >= 1; d in {64, 128}.  Other valid shapes return
+ *    N >= 1; B*H >= 1; d a multiple of 8 up to 128, for the (dtype, P, L,
+ *    causal) combinations with a compiled kernel set.  The kernels are
+ *    compiled for head dims D = 64 and 128; a smaller d runs on the next
+ *    one up with its token rows padded by zero columns in the workspace
+ *    (zero columns add nothing to a projection and give zero output
+ *    columns, so the results are the layer at d; the padding costs one more
+ *    pass over each token tensor).  Other valid shapes return
  *    RACE_ERR_UNSUPPORTED.
  */
 #ifndef RACE_ATTN_H
@@ -67,10 +73,11 @@ typedef struct {
 } race_shape;
 
 /* Bytes of the state buffer the forward pass fills and the backward pass
- * reads.  Non-causal: the bucket bank, content[B*H][LRP][d] float32
+ * reads.  Non-causal: the bucket bank, content[B*H][LRP][D] float32
  * followed by mass[B*H][LRP] float32, where LRP = L * 2^max(P,3) rounded up
- * to a multiple of 32 (rows past L*2^max(P,3) are zero; for P < 3 each table
- * is widened with zero hyperplanes, which leaves O unchanged).  Causal: the
+ * to the compiled bank size (rows past L*2^max(P,3) are zero; for P < 3 each
+ * table is widened with zero hyperplanes, which leaves O unchanged) and D is
+ * the kernels' head dim (columns past d are zero).  Causal: the
  * inclusive bucket bank at each segment end, plus one float32 per token.
  * Returns 0 for invalid arguments. */
 size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal);
@@ -155,8 +162,11 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
 /* Recurrent decode (slides, frame "Causality is a prefix update of the same
  * statistics"): the causal layer as a fixed-size state per (batch, head),
  * the bucket bank after the tokens seen so far: float32 content
- * [B*H][LRP][d] followed by mass [B*H][LRP] (LRP = L * 2^max(P,3) padded to
- * the compiled size; the same layout as the non-causal forward's state).
+ * [B*H][LRP][D] followed by mass [B*H][LRP] (LRP = L * 2^max(P,3) padded to
+ * the compiled size, D the kernels' head dim; the same layout as the
+ * non-causal forward's state).  The decode kernel reads and writes rows of
+ * the caller's d directly; the prefill pads K and V in its workspace when d
+ * is below D.
  * shape->N is the number of tokens of the call; the state size does not
  * depend on it. */
 size_t race_attn_decode_state_bytes(const race_shape* shape, int P, int L);

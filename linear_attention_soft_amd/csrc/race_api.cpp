@@ -73,6 +73,28 @@ __global__ void race_bank_export(const float* __restrict__ src_c, int64_t c_bank
   }
 }
 
+// Token rows copied between the caller's head dim and the kernels' (16-byte
+// units): each destination row takes copy_w units from its source row and is
+// zero past them.  Up to 8 tensors per launch (grid y); a NULL source skips.
+struct RowCopies {
+  const void* src[8];
+  void* dst[8];
+  int64_t rows;
+  int src_w, dst_w, copy_w;
+};
+__global__ void race_copy_rows(RowCopies a) {
+  const uint4* src = static_cast<const uint4*>(a.src[blockIdx.y]);
+  uint4* dst = static_cast<uint4*>(a.dst[blockIdx.y]);
+  if (!src) return;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.rows * a.dst_w) return;
+  const int64_t r = idx / a.dst_w;
+  const int c = (int)(idx % a.dst_w);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (c < a.copy_w) v = src[r * a.src_w + c];
+  dst[r * a.dst_w + c] = v;
+}
+
 const KernelSet* all_kernel_sets(int* count) {
   static const std::vector<KernelSet> all = [] {
     std::vector<KernelSet> v;
@@ -144,7 +166,9 @@ race_status fail(race_status s, const std::string& msg) {
 
 struct Plan {
   int dtype = 0;
-  int64_t B = 0, H = 0, N = 0, D = 0, BH = 0;
+  int64_t B = 0, H = 0, N = 0, BH = 0;
+  int64_t d = 0;   // the caller's head dim
+  int64_t D = 0;   // the kernels' head dim (d rounded up to a compiled one; token rows padded when larger)
   int P = 0, L = 0, PE = 0, LR = 0, LRP = 0;
   bool causal = false;
   bool nc_static = false;    // non-causal layer through the static-bank walks
@@ -181,6 +205,23 @@ void bind_set(Plan* p, const race::KernelSet* ks) {
   if (!ks) return;
   p->LRP = ks->LRP;
   p->nc_static = !p->causal && !ks->readout;
+}
+
+// Compiled head dims, smallest first: a caller's d runs on the smallest one at
+// or above it that has a kernel set for (dtype, P, L, causal), its token rows
+// padded with zero columns.
+constexpr int kHeadDims[] = {64, 128};
+
+void pick_set(Plan* p) {
+  for (int D : kHeadDims) {
+    if (D < p->d) continue;
+    if (const race::KernelSet* ks = find_set(p->dtype, D, p->PE, p->LRP, p->causal)) {
+      p->D = D;
+      bind_set(p, ks);
+      return;
+    }
+  }
+  bind_set(p, nullptr);
 }
 
 // Decode and prefill need the bucket reduce and the decode kernel only (every
@@ -232,7 +273,7 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
   if (s->B > (int64_t)1 << 31 || s->H > (int64_t)1 << 31 || s->N > (int64_t)1 << 40 || s->d > 4096)
     return fail(RACE_ERR_INVALID_ARG, "shape out of range");
   p->dtype = s->dtype;
-  p->B = s->B; p->H = s->H; p->N = s->N; p->D = s->d; p->BH = s->B * s->H;
+  p->B = s->B; p->H = s->H; p->N = s->N; p->d = s->d; p->BH = s->B * s->H;
   if (p->BH > 65535) return fail(RACE_ERR_UNSUPPORTED, "B*H above 65535 is not supported");
   p->P = P; p->L = L; p->PE = P < 3 ? 3 : P;
   if ((int64_t)L << p->PE > 256) return fail(RACE_ERR_UNSUPPORTED, "L * 2^max(P,3) above 256 is not supported");
@@ -240,9 +281,10 @@ race_status make_plan(const race_shape* s, int P, int L, int causal, Plan* p, bo
   p->LRP = (p->LR + 31) / 32 * 32;
   p->causal = causal != 0;
   p->w_per_head = s->w_per_head != 0;
-  if (p->D != 64 && p->D != 128) return fail(RACE_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  if (p->d % 8 != 0 || p->d > 128) return fail(RACE_ERR_UNSUPPORTED, "head dim d must be a multiple of 8, at most 128");
+  p->D = p->d <= 64 ? 64 : 128;
   if (need_kernels) {
-    bind_set(p, find_set(p->dtype, (int)p->D, p->PE, p->LRP, p->causal));
+    pick_set(p);
     if (!p->ks) return fail(RACE_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, d, P, L, causal)");
   }
   chunking(p->N, p->BH, kMinTilesPerWG, &p->nchunk, &p->chunk_tokens);
@@ -298,7 +340,7 @@ size_t dw_part_bytes(const Plan& p) {
   return align256(2 * (size_t)p.BH * p.nchunk * nhp(p) * p.D * sizeof(float));
 }
 size_t dw_bytes(const Plan& p) { return 2 * dpre_side_bytes(p) + dw_part_bytes(p); }
-size_t dw_out_floats(const Plan& p) { return (size_t)(p.w_per_head ? p.H : 1) * p.L * p.P * p.D; }
+size_t dw_out_floats(const Plan& p) { return (size_t)(p.w_per_head ? p.H : 1) * p.L * p.P * p.d; }
 
 // Bytes of the state a backward rebuilds itself when the caller passes none
 // (non-causal: the bank; causal: segment banks and Den; the causal segment
@@ -323,6 +365,16 @@ size_t workspace_bytes(const Plan& p, bool bwd, bool dw = false, bool no_state =
   return causal_bwd_ws(p).total;
 }
 
+// When the caller's head dim d is below the kernels' D, the entry points
+// work on zero-padded copies of the token tensors, appended to the
+// workspace: forward Q, K, V, O (4), backward Q, K, V, dO, O, dQ, dK, dV (8),
+// prefill K, V (2).
+size_t padded_tensor_bytes(const Plan& p) { return align256((size_t)p.BH * p.N * p.D * elem_size(p.dtype)); }
+size_t pad_bytes(const Plan& p, int tensors) { return p.d == p.D ? 0 : (size_t)tensors * padded_tensor_bytes(p); }
+size_t total_workspace_bytes(const Plan& p, bool bwd, bool dw = false, bool no_state = false) {
+  return workspace_bytes(p, bwd, dw, no_state) + pad_bytes(p, bwd ? 8 : 4);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -335,6 +387,24 @@ race_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RACE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
   return RACE_OK;
+}
+
+// Copies n token tensors [BH][N][row] between the caller's head dim and the
+// kernels' (to_kernel: caller -> zero-padded kernel rows; else back).
+race_status copy_rows(const Plan& p, const void* const* src, void* const* dst, int n, bool to_kernel, hipStream_t s) {
+  race::RowCopies a{};
+  for (int i = 0; i < n; ++i) { a.src[i] = src[i]; a.dst[i] = dst[i]; }
+  const int cw = (int)(p.d * (int64_t)elem_size(p.dtype) / 16), kw = (int)(p.D * (int64_t)elem_size(p.dtype) / 16);
+  a.rows = p.BH * p.N;
+  a.src_w = to_kernel ? cw : kw;
+  a.dst_w = to_kernel ? kw : cw;
+  a.copy_w = cw;
+  const int64_t blocks = (a.rows * a.dst_w + 255) / 256;
+  {
+    ProfScope ps(s, "race_copy_rows");
+    hipLaunchKernelGGL(race::race_copy_rows, dim3((unsigned)blocks, (unsigned)n), dim3(256), 0, s, a);
+  }
+  return check_launch("race_copy_rows");
 }
 
 void launch_finalize(const float* part, int nchunk, const Plan& p, float* content, float* mass, hipStream_t st) {
@@ -350,7 +420,8 @@ void launch_finalize(const float* part, int nchunk, const Plan& p, float* conten
 race::Tables tables(const Plan& p, const float* W) {
   race::Tables t;
   t.W = W;
-  t.hstride = p.w_per_head ? (int64_t)p.L * p.P * p.D : 0;
+  t.hstride = p.w_per_head ? (int64_t)p.L * p.P * p.d : 0;
+  t.ld = (int)p.d;
   t.H = (int)p.H;
   return t;
 }
@@ -384,7 +455,7 @@ race_status launch_dw(const Plan& p, const void* Q, const void* K, float* dW, ch
   {
     ProfScope ps(s, "race_dw_finalize");
     hipLaunchKernelGGL(race::race_dw_finalize, dim3(rows), dim3(1024), 0, s, a.part, (int)p.B, (int)p.H,
-                       p.w_per_head ? 1 : 0, p.nchunk, nhp(p), p.PE, p.L, p.P, (int)p.D, dW);
+                       p.w_per_head ? 1 : 0, p.nchunk, nhp(p), p.PE, p.L, p.P, (int)p.D, (int)p.d, dW);
   }
   return check_launch("race_dw_finalize");
 }
@@ -623,7 +694,7 @@ extern "C" {
 size_t race_attn_state_bytes(const race_shape* shape, int P, int L, int causal) {
   Plan p;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
-  bind_set(&p, find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal));
+  pick_set(&p);
   return state_bytes(p);
 }
 
@@ -633,8 +704,8 @@ size_t race_attn_workspace_bytes(const race_shape* shape, int P, int L, int caus
   const bool no_state = (is_bwd & RACE_WS_NO_STATE) != 0;
   if (phase < RACE_WS_FWD || phase > RACE_WS_BWD_DW || (no_state && phase == RACE_WS_FWD)) return 0;
   if (make_plan(shape, P, L, causal, &p, false) != RACE_OK) return 0;
-  bind_set(&p, find_set(p.dtype, (int)p.D, p.PE, p.LRP, p.causal));
-  return workspace_bytes(p, phase != RACE_WS_FWD, phase == RACE_WS_BWD_DW, no_state);
+  pick_set(&p);
+  return total_workspace_bytes(p, phase != RACE_WS_FWD, phase == RACE_WS_BWD_DW, no_state);
 }
 
 }  // extern "C"
@@ -671,9 +742,80 @@ race_status scratch_address(void** out) {
 // Workspace the forward touches: the partial banks (non-causal) or segment
 // sums (causal), plus the state's own room when the caller passes no state.
 size_t fwd_workspace_used(const Plan& p, bool have_state) {
-  if (have_state) return p.causal ? align256(seg_bank_bytes(p)) : align256(nc_part_bytes(p));
-  return workspace_bytes(p, false);
+  if (have_state) return (p.causal ? align256(seg_bank_bytes(p)) : align256(nc_part_bytes(p))) + pad_bytes(p, 4);
+  return total_workspace_bytes(p, false);
 }
+
+// The backward on token tensors of the kernels' head dim: the state rebuilt
+// first when the caller passes none, then the variant's kernels.
+race_status bwd_run(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta,
+                    const void* O, const void* dO, void* dQ, void* dK, void* dV, float* dbeta, float* dW,
+                    const void* state, char* ws, hipStream_t s) {
+  race_status st;
+  if (!state) {
+    // rebuild the forward's state at the end of the workspace: the bank of K,
+    // V (non-causal), or the segment banks and Den (causal; O is not written)
+    char* sreg = ws + workspace_bytes(p, true, dW != nullptr, false);
+    if (p.causal) {
+      float* gpart = reinterpret_cast<float*>(ws + causal_bwd_ws(p).gpart);
+      float* prefix = reinterpret_cast<float*>(sreg);
+      float* den = reinterpret_cast<float*>(sreg + align256(seg_bank_bytes(p)));
+      st = causal_forward_into(p, Q, K, V, W, beta, nullptr, gpart, prefix, den, s);
+    } else {
+      float* content = reinterpret_cast<float*>(sreg);
+      st = noncausal_bank(p, K, V, W, beta, reinterpret_cast<float*>(ws), content,
+                          content + (size_t)p.BH * p.LRP * p.D, s);
+    }
+    if (st != RACE_OK) return st;
+    state = sreg;
+  }
+  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
+  if (p.nc_static) return static_backward(p, Q, K, V, W, beta, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
+  char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
+
+  const float* content = static_cast<const float*>(state);
+  const float* mass = content + (size_t)p.BH * p.LRP * p.D;
+  float* part = reinterpret_cast<float*>(ws);
+  float* dbank = reinterpret_cast<float*>(ws + align256(part_bytes(p)));
+  float* dcontent = dbank;
+  float* dmass = dbank + (size_t)p.BH * p.LRP * p.D;
+  float* bparts = dbeta ? reinterpret_cast<float*>(ws + align256(part_bytes(p)) + align256(bank_bytes(p))) : nullptr;
+
+  race::NCArgs a{};
+  a.X = Q; a.Y = dO; a.out0 = dQ; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.st_content = content; a.st_mass = mass; a.part = part;
+  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.dbeta_part = bparts;
+  a.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
+  {
+    ProfScope ps(s, "race_bwd_q");
+    p.ks->bwd_q(a, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bwd_q")) != RACE_OK) return st;
+  {
+    ProfScope ps(s, "race_bank_finalize");
+    launch_finalize(part, p.nchunk, p, dcontent, dmass, s);
+  }
+  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
+  race::NCArgs b{};
+  b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = tables(p, W); b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
+  b.st_content = dcontent; b.st_mass = dmass; b.chunk_tokens = p.chunk_tokens; b.nchunk = p.nchunk;
+  b.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
+  b.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
+  {
+    ProfScope ps(s, "race_bwd_kv");
+    p.ks->bwd_kv(b, dim3(p.nchunk, (unsigned)p.BH), s);
+  }
+  if ((st = check_launch("race_bwd_kv")) != RACE_OK) return st;
+  if (dbeta) {
+    ProfScope ps(s, "race_dbeta_finalize");
+    launch_dbeta_finalize(p, bparts, dbeta, s);
+  }
+  if ((st = check_launch("race_dbeta_finalize")) != RACE_OK) return st;
+  return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
+}
+
+race_status fwd_run(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta, void* O,
+                    void* state, char* ws, hipStream_t s);
 
 // Shared by race_attn_fwd (caller's workspace, at least the documented
 // race_attn_workspace_bytes) and race_attn_fwd_noalloc (the library's own
@@ -690,7 +832,7 @@ race_status fwd_common(const void* Q, const void* K, const void* V, const float*
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(W) ||
       (state && !aligned16(state)) || (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const size_t tbytes = (size_t)(p.BH * p.N * p.d) * elem_size(p.dtype);
   if (overlaps(O, tbytes, Q, tbytes) || overlaps(O, tbytes, K, tbytes) || overlaps(O, tbytes, V, tbytes))
     return fail(RACE_ERR_INVALID_ARG, "O overlaps an input");
   if (own_scratch) {
@@ -700,11 +842,11 @@ race_status fwd_common(const void* Q, const void* K, const void* V, const float*
                                           " bytes of scratch, above the " + std::to_string(workspace_bytes_in) +
                                           " bytes the allocation-free forward holds");
   } else {
-    const size_t need_ws = workspace_bytes(p, false);
+    const size_t need_ws = total_workspace_bytes(p, false);
     if (!workspace || workspace_bytes_in < need_ws)
       return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes");
   }
-  const size_t need_ws = own_scratch ? 0 : workspace_bytes(p, false);
+  const size_t need_ws = own_scratch ? 0 : total_workspace_bytes(p, false);
   const size_t need_state = state_bytes(p);
   if (state && state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
@@ -716,7 +858,24 @@ race_status fwd_common(const void* Q, const void* K, const void* V, const float*
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (p.d == p.D) return fwd_run(p, Q, K, V, W, beta, O, state, ws, s);
+  // the caller's head dim is below the kernels': zero-padded copies of Q, K,
+  // V and O after the forward's own workspace
+  char* r = ws + fwd_workspace_used(p, state != nullptr) - pad_bytes(p, 4);
+  const size_t tb = padded_tensor_bytes(p);
+  void* kt[4] = {r, r + tb, r + 2 * tb, r + 3 * tb};
+  const void* src[] = {Q, K, V};
+  if ((st = copy_rows(p, src, kt, 3, true, s)) != RACE_OK) return st;
+  if ((st = fwd_run(p, kt[0], kt[1], kt[2], W, beta, kt[3], state, ws, s)) != RACE_OK) return st;
+  const void* res[] = {kt[3]};
+  void* out[] = {O};
+  return copy_rows(p, res, out, 1, false, s);
+}
 
+// The forward on token tensors of the kernels' head dim.
+race_status fwd_run(const Plan& p, const void* Q, const void* K, const void* V, const float* W, float beta, void* O,
+                    void* state, char* ws, hipStream_t s) {
+  race_status st;
   if (p.causal) return causal_forward(p, Q, K, V, W, beta, O, state, ws, s);
 
   float* part = reinterpret_cast<float*>(ws);
@@ -781,7 +940,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   if (dbeta && ((uintptr_t)dbeta & 3u)) return fail(RACE_ERR_INVALID_ARG, "dbeta must be 4-byte aligned");
   if (dW && ((uintptr_t)dW & 3u)) return fail(RACE_ERR_INVALID_ARG, "dW must be 4-byte aligned");
   const size_t dw_out = dW ? dw_out_floats(p) * sizeof(float) : 0;
-  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const size_t tbytes = (size_t)(p.BH * p.N * p.d) * elem_size(p.dtype);
   if (!p.causal) O = nullptr;   // the non-causal backward never reads O
   const void* ins[] = {Q, K, V, dO, O};
   void* outs[] = {dQ, dK, dV};
@@ -802,7 +961,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   const size_t need_state = state_bytes(p);
   if (state && state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
-  const size_t need_ws = workspace_bytes(p, true, dW != nullptr, state == nullptr);
+  const size_t need_ws = total_workspace_bytes(p, true, dW != nullptr, state == nullptr);
   if (!workspace || workspace_bytes_in < need_ws)
     return fail(RACE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_ws) + " bytes" +
                                         (dW ? " (backward with dW)" : "") +
@@ -820,74 +979,35 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-
-  if (!state) {
-    // rebuild the forward's state at the end of the workspace: the bank of K,
-    // V (non-causal), or the segment banks and Den (causal; O is not written)
-    char* sreg = ws + workspace_bytes(p, true, dW != nullptr, false);
-    if (p.causal) {
-      float* gpart = reinterpret_cast<float*>(ws + causal_bwd_ws(p).gpart);
-      float* prefix = reinterpret_cast<float*>(sreg);
-      float* den = reinterpret_cast<float*>(sreg + align256(seg_bank_bytes(p)));
-      st = causal_forward_into(p, Q, K, V, W, beta, nullptr, gpart, prefix, den, s);
-    } else {
-      float* content = reinterpret_cast<float*>(sreg);
-      st = noncausal_bank(p, K, V, W, beta, reinterpret_cast<float*>(ws), content,
-                          content + (size_t)p.BH * p.LRP * p.D, s);
-    }
-    if (st != RACE_OK) return st;
-    state = sreg;
-  }
-  if (p.causal) return causal_backward(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
-  if (p.nc_static) return static_backward(p, Q, K, V, W, beta, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
-  char* dwr = dW ? ws + workspace_bytes(p, true, false) : nullptr;
-
-  const float* content = static_cast<const float*>(state);
-  const float* mass = content + (size_t)p.BH * p.LRP * p.D;
-  float* part = reinterpret_cast<float*>(ws);
-  float* dbank = reinterpret_cast<float*>(ws + align256(part_bytes(p)));
-  float* dcontent = dbank;
-  float* dmass = dbank + (size_t)p.BH * p.LRP * p.D;
-  float* bparts = dbeta ? reinterpret_cast<float*>(ws + align256(part_bytes(p)) + align256(bank_bytes(p))) : nullptr;
-
-  race::NCArgs a{};
-  a.X = Q; a.Y = dO; a.out0 = dQ; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
-  a.st_content = content; a.st_mass = mass; a.part = part;
-  a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk; a.dbeta_part = bparts;
-  a.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
-  {
-    ProfScope ps(s, "race_bwd_q");
-    p.ks->bwd_q(a, dim3(p.nchunk, (unsigned)p.BH), s);
-  }
-  if ((st = check_launch("race_bwd_q")) != RACE_OK) return st;
-  {
-    ProfScope ps(s, "race_bank_finalize");
-    launch_finalize(part, p.nchunk, p, dcontent, dmass, s);
-  }
-  if ((st = check_launch("race_bank_finalize")) != RACE_OK) return st;
-  race::NCArgs b{};
-  b.X = K; b.Y = V; b.out0 = dV; b.out1 = dK; b.W = tables(p, W); b.beta = beta; b.L = p.L; b.P = p.P; b.N = p.N;
-  b.st_content = dcontent; b.st_mass = dmass; b.chunk_tokens = p.chunk_tokens; b.nchunk = p.nchunk;
-  b.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
-  b.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
-  {
-    ProfScope ps(s, "race_bwd_kv");
-    p.ks->bwd_kv(b, dim3(p.nchunk, (unsigned)p.BH), s);
-  }
-  if ((st = check_launch("race_bwd_kv")) != RACE_OK) return st;
-  if (dbeta) {
-    ProfScope ps(s, "race_dbeta_finalize");
-    launch_dbeta_finalize(p, bparts, dbeta, s);
-  }
-  if ((st = check_launch("race_dbeta_finalize")) != RACE_OK) return st;
-  return dW ? launch_dw(p, Q, K, dW, dwr, s) : RACE_OK;
+  if (p.d == p.D) return bwd_run(p, Q, K, V, W, beta, O, dO, dQ, dK, dV, dbeta, dW, state, ws, s);
+  // the caller's head dim is below the kernels': zero-padded copies of the
+  // token tensors at the end of the workspace (Q, K, V, dO, O, dQ, dK, dV)
+  char* r = ws + workspace_bytes(p, true, dW != nullptr, state == nullptr);
+  const size_t tb = padded_tensor_bytes(p);
+  void* kt[8];
+  for (int i = 0; i < 8; ++i) kt[i] = r + i * tb;
+  const void* src[] = {Q, K, V, dO, O};
+  if ((st = copy_rows(p, src, kt, 5, true, s)) != RACE_OK) return st;
+  st = bwd_run(p, kt[0], kt[1], kt[2], W, beta, O ? kt[4] : nullptr, kt[3], kt[5], kt[6], kt[7], dbeta, dW, state, ws,
+               s);
+  if (st != RACE_OK) return st;
+  const void* grads[] = {kt[5], kt[6], kt[7]};
+  void* outs_c[] = {dQ, dK, dV};
+  return copy_rows(p, grads, outs_c, 3, false, s);
 }
 
 // ---- recurrent decode: the state is the bank [BH][LRP][d] + mass [BH][LRP]
 race_status decode_plan(const race_shape* shape, int P, int L, Plan* p) {
   race_status st = make_plan(shape, P, L, 0, p, false);
   if (st != RACE_OK) return st;
-  p->ks = find_decode_set(p->dtype, (int)p->D, p->PE, p->LRP);
+  p->ks = nullptr;
+  for (int D : kHeadDims) {
+    if (D < p->d) continue;
+    if ((p->ks = find_decode_set(p->dtype, D, p->PE, p->LRP))) {
+      p->D = D;
+      break;
+    }
+  }
   if (!p->ks) return fail(RACE_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, d, P, L)");
   p->LRP = p->ks->LRP;
   return RACE_OK;
@@ -902,7 +1022,7 @@ size_t race_attn_decode_state_bytes(const race_shape* shape, int P, int L) {
 size_t race_attn_decode_prefill_workspace_bytes(const race_shape* shape, int P, int L) {
   Plan p;
   if (decode_plan(shape, P, L, &p) != RACE_OK) return 0;
-  return align256(part_bytes(p));
+  return align256(part_bytes(p)) + pad_bytes(p, 2);
 }
 
 race_status race_attn_decode_prefill(const void* K, const void* V, const float* W, float beta, int P, int L,
@@ -916,8 +1036,8 @@ race_status race_attn_decode_prefill(const void* K, const void* V, const float* 
   if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
   if (!aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(state) || (workspace && !aligned16(workspace)))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
-  const size_t need_state = bank_bytes(p), need_ws = align256(part_bytes(p));
+  const size_t tbytes = (size_t)(p.BH * p.N * p.d) * elem_size(p.dtype);
+  const size_t need_state = bank_bytes(p), need_ws = align256(part_bytes(p)) + pad_bytes(p, 2);
   if (state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
   if (!workspace || workspace_bytes_in < need_ws)
@@ -929,6 +1049,15 @@ race_status race_attn_decode_prefill(const void* K, const void* V, const float* 
   float* part = static_cast<float*>(workspace);
   float* content = static_cast<float*>(state);
   float* mass = content + (size_t)p.BH * p.LRP * p.D;
+  if (p.d != p.D) {
+    // zero-padded copies of K and V after the partial banks
+    char* r = static_cast<char*>(workspace) + align256(part_bytes(p));
+    void* kt[2] = {r, r + padded_tensor_bytes(p)};
+    const void* src[] = {K, V};
+    if ((st = copy_rows(p, src, kt, 2, true, s)) != RACE_OK) return st;
+    K = kt[0];
+    V = kt[1];
+  }
   race::NCArgs a{};
   a.X = K; a.Y = V; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
   a.part = part; a.chunk_tokens = p.chunk_tokens; a.nchunk = p.nchunk;
@@ -955,7 +1084,7 @@ race_status race_attn_decode(const void* Q, const void* K, const void* V, const 
   if (!std::isfinite(beta)) return fail(RACE_ERR_INVALID_ARG, "beta must be finite");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(O) || !aligned16(state))
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-  const size_t tbytes = (size_t)(p.BH * p.N * p.D) * elem_size(p.dtype);
+  const size_t tbytes = (size_t)(p.BH * p.N * p.d) * elem_size(p.dtype);
   const size_t need_state = bank_bytes(p);
   if (state_bytes_in < need_state)
     return fail(RACE_ERR_WORKSPACE, "state too small: need " + std::to_string(need_state) + " bytes");
@@ -967,6 +1096,7 @@ race_status race_attn_decode(const void* Q, const void* K, const void* V, const 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   race::DArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.W = tables(p, W); a.beta = beta; a.L = p.L; a.P = p.P; a.N = p.N;
+  a.dr = (int)p.d;
   a.content = static_cast<float*>(state);
   a.mass = a.content + (size_t)p.BH * p.LRP * p.D;
   {
@@ -1004,7 +1134,7 @@ race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int c
     if (q && ((uintptr_t)q & 3u)) return fail(RACE_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
   const int64_t nbank = p.BH * (p.causal ? p.nseg : 1);
   const int R = 1 << P;
-  const size_t per_c = (size_t)L * R * p.D * sizeof(float), per_m = (size_t)L * R * sizeof(float);
+  const size_t per_c = (size_t)L * R * p.d * sizeof(float), per_m = (size_t)L * R * sizeof(float);
   const void* outs[] = {content, mass, dcontent, dmass};
   const size_t sizes[] = {nbank * per_c, nbank * per_m, nbank * per_c, nbank * per_m};
   for (int i = 0; i < 4; ++i) {
@@ -1015,7 +1145,7 @@ race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int c
       return fail(RACE_ERR_INVALID_ARG, "an output overlaps the state or the workspace");
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t total = nbank * L * R * (p.D + 1);
+  const int64_t total = nbank * L * R * (p.d + 1);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   const int DP1 = (int)p.D + 1;
   const char* ws = static_cast<const char*>(bwd_workspace);
@@ -1024,11 +1154,11 @@ race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int c
     const float* b = static_cast<const float*>(state);
     if (p.causal) {   // segment banks [BH][nseg][LRP][d+1]: the bank before each segment
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, b, (int64_t)p.LRP * DP1, DP1,
-                         b + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.D, 1.f, content, mass);
+                         b + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.d, 1.f, content, mass);
     } else {          // content [BH][LRP][d], mass [BH][LRP]
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, b, (int64_t)p.LRP * p.D,
                          (int)p.D, b + (size_t)p.BH * p.LRP * p.D, (int64_t)p.LRP, 1, nbank, L, P, p.PE,
-                         (int)p.D, 1.f, content, mass);
+                         (int)p.d, 1.f, content, mass);
     }
     if ((st = check_launch("race_bank_export")) != RACE_OK) return st;
   }
@@ -1036,12 +1166,12 @@ race_status race_bucket_stats_debug(const race_shape* shape, int P, int L, int c
     if (p.causal) {   // gradient banks after each segment [BH][nseg][LRP][d+1]
       const float* g = reinterpret_cast<const float*>(ws + causal_bwd_ws(p).gsuf);
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * DP1, DP1,
-                         g + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.D, gscale, dcontent, dmass);
+                         g + p.D, (int64_t)p.LRP * DP1, DP1, nbank, L, P, p.PE, (int)p.d, gscale, dcontent, dmass);
     } else {          // gradient bank dcontent [BH][LRP][d], dmass [BH][LRP]
       const float* g = reinterpret_cast<const float*>(ws + align256(nc_part_bytes(p)));
       hipLaunchKernelGGL(race::race_bank_export, dim3(blocks), dim3(256), 0, s, g, (int64_t)p.LRP * p.D,
                          (int)p.D, g + (size_t)p.BH * p.LRP * p.D, (int64_t)p.LRP, 1, nbank, L, P, p.PE,
-                         (int)p.D, gscale, dcontent, dmass);
+                         (int)p.d, gscale, dcontent, dmass);
     }
     if ((st = check_launch("race_bank_export")) != RACE_OK) return st;
   }
@@ -1060,7 +1190,7 @@ race_status race_softbucket_debug(const void* X, const float* W, float beta, int
   if (!aligned16(X) || !aligned16(W) || !aligned16(phi_out)) return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   int64_t blocks = (p.N + race::TT - 1) / race::TT;
   if (blocks > 4096) blocks = 4096;
-  p.ks->softbucket_dbg(X, tables(p, W), beta, p.L, p.P, p.N, phi_out, dim3((unsigned)blocks, (unsigned)p.BH),
+  p.ks->softbucket_dbg(X, tables(p, W), beta, p.L, p.P, p.N, (int)p.d, phi_out, dim3((unsigned)blocks, (unsigned)p.BH),
                        reinterpret_cast<hipStream_t>(stream));
   return check_launch("race_softbucket_dbg");
 }

@@ -122,7 +122,7 @@ struct TWLds {
 // W^T frags of the dX contraction for column tile ct, built into registers
 // (same entries as build_wt_frags).
 template <typename T, class G>
-__device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int L, int P, int ct,
+__device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int ld, int L, int P, int ct,
                                              typename Eng<T>::frag (&wt)[G::NQS]) {
   using E = Eng<T>;
   const int lane = lane_id();
@@ -138,7 +138,7 @@ __device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int L,
         const int hp = e % G::NHP, which = e / G::NHP;
         const int l = hp / G::PE, t = hp % G::PE;
         if (l < L && t < P) {
-          const float x = W[(size_t)(l * P + t) * G::D + c];
+          const float x = w_entry(W, ld, l * P + t, c);
           const float xh = E::round(x);
           w = (E::NSPLIT == 2 && which == 2) ? (x - xh) : (E::NSPLIT == 2 ? xh : x);
         }
@@ -197,7 +197,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
 
   frag wt[C::NCTW][G::NQS];
 #pragma unroll
-  for (int j = 0; j < C::NCTW; ++j) wt_frags_reg<T, G>(a.W.at(bh), a.L, a.P, w + C::NM * j, wt[j]);
+  for (int j = 0; j < C::NCTW; ++j) wt_frags_reg<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, w + C::NM * j, wt[j]);
   // identity operands: lane (c, h), element i is 1 where kmap(s, h, i) == c
   frag idn[2];
 #pragma unroll
@@ -306,8 +306,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     }
   };
 
-  if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
-  else build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, S.Wf);
+  if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
+  else build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
   load_stage(0);
   stage(0, 0);
   __syncthreads();

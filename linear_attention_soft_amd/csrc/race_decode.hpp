@@ -28,6 +28,7 @@ struct DArgs {
   float beta;
   int L, P;
   int64_t N;        // new tokens per (batch, head)
+  int dr;           // elements per Q, K, V, O row (the caller's d, at most D; W.ld is the same)
 };
 
 template <class G>
@@ -58,10 +59,11 @@ __global__ __launch_bounds__((DecCfg<G>::NT)) void race_decode(DArgs a) {
   const int c = tid % D, g = tid / D;
   float* content = a.content + (size_t)bh * LRP * D;
   float* mass = a.mass + (size_t)bh * LRP;
-  const T* src[3] = {static_cast<const T*>(a.Q) + (size_t)bh * a.N * D,
-                     static_cast<const T*>(a.K) + (size_t)bh * a.N * D,
-                     static_cast<const T*>(a.V) + (size_t)bh * a.N * D};
-  T* out = static_cast<T*>(a.O) + (size_t)bh * a.N * D;
+  const int dr = a.dr;
+  const T* src[3] = {static_cast<const T*>(a.Q) + (size_t)bh * a.N * dr,
+                     static_cast<const T*>(a.K) + (size_t)bh * a.N * dr,
+                     static_cast<const T*>(a.V) + (size_t)bh * a.N * dr};
+  T* out = static_cast<T*>(a.O) + (size_t)bh * a.N * dr;
 
   float bank[RPT];
 #pragma unroll
@@ -72,16 +74,19 @@ __global__ __launch_bounds__((DecCfg<G>::NT)) void race_decode(DArgs a) {
   const int prole = tid / (G::NHP * TPH), php = (tid / TPH) % G::NHP, pq = tid % TPH;
   const int pl = php / G::PE, pt = php % G::PE;
   const bool pok = tid < 2 * G::NHP * TPH && pl < a.L && pt < a.P;
-  const float* pw = a.W.at(bh) + (size_t)(pok ? pl * a.P + pt : 0) * D;
+  const float* pw = a.W.at(bh) + (size_t)(pok ? pl * a.P + pt : 0) * a.W.ld;
 
   for (int64_t t = 0; t < a.N; ++t) {
-    for (int i = tid; i < 3 * D; i += DEC_NT) xs[i / D][i % D] = (float)src[i / D][t * D + i % D];
+    for (int i = tid; i < 3 * D; i += DEC_NT) {
+      const int e = i % D;
+      xs[i / D][e] = e < dr ? (float)src[i / D][t * dr + e] : 0.f;   // columns past dr are zero
+    }
     __syncthreads();
     // projections: TPH consecutive lanes split d, then tanh and the sigmoid pair
     if (tid < 2 * G::NHP * TPH) {
       float s = 0.f;
       if (pok)
-        for (int e = pq; e < D; e += TPH) s += pw[e] * xs[prole][e];
+        for (int e = pq; e < dr; e += TPH) s += pw[e] * xs[prole][e];
 #pragma unroll
       for (int m = TPH / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
       if (pq == 0) {
@@ -130,7 +135,7 @@ __global__ __launch_bounds__((DecCfg<G>::NT)) void race_decode(DArgs a) {
       float den = 0.f;
 #pragma unroll
       for (int k = 0; k < DEC_NT / 64; ++k) den += red[k];
-      out[t * D + c] = (T)(nn / den);
+      if (c < dr) out[t * dr + c] = (T)(nn / den);
     }
     __syncthreads();
   }

@@ -163,15 +163,23 @@ __device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
-// Projection tables: float32 [L][P][d] shared by every head (hstride 0), or
-// [H][L][P][d] with one set per head (hstride L * P * d).  Sequence bh of a
-// [B][H] batch is head bh % H.
+// Projection tables: float32 [L][P][ld] shared by every head (hstride 0), or
+// [H][L][P][ld] with one set per head (hstride L * P * ld).  Sequence bh of a
+// [B][H] batch is head bh % H.  ld is the caller's head dim, at most the
+// kernel's: columns at or past it read as zero (their token columns are zero
+// too, so they add nothing to a projection).
 struct Tables {
   const float* W;
   int64_t hstride;
   int H;
+  int ld;
   __device__ __forceinline__ const float* at(int64_t bh) const { return W + (size_t)(bh % H) * hstride; }
 };
+
+// Entry (row, c) of a table set with row pitch ld (zero past ld).
+__device__ __forceinline__ float w_entry(const float* __restrict__ W, int ld, int row, int c) {
+  return c < ld ? W[(size_t)row * ld + c] : 0.f;
+}
 
 // ---------------------------------------------------------------- geometry
 // Compile-time geometry of one kernel instance.
@@ -210,7 +218,7 @@ struct Geo {
 // for l >= L or t >= P), in the same buffer: its projection is accumulated in
 // float64 (project_rows_f64).
 template <typename T, class G>
-__device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
+__device__ void build_proj_frags(const float* __restrict__ W, int ld, int L, int P,
                                  typename Eng<T>::frag* __restrict__ Wf) {
   using E = Eng<T>;
   if constexpr (std::is_same<T, float>::value) {
@@ -219,7 +227,7 @@ __device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
     for (int idx = threadIdx.x; idx < G::NHP * G::D; idx += blockDim.x) {
       const int hp = idx / G::D, c = idx % G::D;
       const int l = hp / G::PE, t = hp % G::PE;
-      Wr[idx] = (l < L && t < P) ? W[(size_t)(l * P + t) * G::D + c] : 0.f;
+      Wr[idx] = (l < L && t < P) ? w_entry(W, ld, l * P + t, c) : 0.f;
     }
     return;
   }
@@ -236,7 +244,7 @@ __device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
     const bool ok = (hp < G::NHP) && (l < L) && (t < P);
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ok ? W[(size_t)(l * P + t) * G::D + 16 * q + 8 * h + i] : 0.f;
+    for (int i = 0; i < 8; ++i) v[i] = ok ? w_entry(W, ld, l * P + t, 16 * q + 8 * h + i) : 0.f;
     typename E::frag hi, lo;
     E::split(v, hi, lo);
     Wf[idx] = part ? lo : hi;
@@ -247,7 +255,7 @@ __device__ void build_proj_frags(const float* __restrict__ W, int L, int P,
 // hyperplanes of table l (bf16: rows t then the lo parts at 8 + t; f32: rows
 // t), rows past PE zero, duplicated in both row halves as above.
 template <typename T, class G>
-__device__ void build_table_frags(const float* __restrict__ W, int L, int P,
+__device__ void build_table_frags(const float* __restrict__ W, int ld, int L, int P,
                                   typename Eng<T>::frag* __restrict__ Wt) {
   using E = Eng<T>;
   static_assert(G::PE <= (E::NSPLIT == 2 ? 8 : 16), "one tile per table");
@@ -263,7 +271,7 @@ __device__ void build_table_frags(const float* __restrict__ W, int L, int P,
     const bool ok = (t < G::PE) && (l < L) && (t < P);
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ok ? W[(size_t)(l * P + t) * G::D + 16 * q + 8 * h + i] : 0.f;
+    for (int i = 0; i < 8; ++i) v[i] = ok ? w_entry(W, ld, l * P + t, 16 * q + 8 * h + i) : 0.f;
     typename E::frag hi, lo;
     E::split(v, hi, lo);
     Wt[idx] = part ? lo : hi;
@@ -289,7 +297,7 @@ __device__ __forceinline__ void project_table(const typename Eng<T>::frag* __res
 // dX A operand: W^T[c][e] for the contraction dX = dPre . W.  bf16 entries e
 // cover (hp, W_hi, dPre_hi), (hp, W_hi, dPre_lo), (hp, W_lo, dPre_hi).
 template <typename T, class G>
-__device__ void build_wt_frags(const float* __restrict__ W, int L, int P,
+__device__ void build_wt_frags(const float* __restrict__ W, int ld, int L, int P,
                                typename Eng<T>::frag* __restrict__ WTf) {
   using E = Eng<T>;
   for (int idx = threadIdx.x; idx < G::CT * G::NQS * 64; idx += blockDim.x) {
@@ -306,7 +314,7 @@ __device__ void build_wt_frags(const float* __restrict__ W, int L, int P,
         const int hp = e % G::NHP, which = e / G::NHP;
         const int l = hp / G::PE, t = hp % G::PE;
         if (l < L && t < P) {
-          const float x = W[(size_t)(l * P + t) * G::D + c];
+          const float x = w_entry(W, ld, l * P + t, c);
           const float xh = E::round(x);
           w = (E::NSPLIT == 2 && which == 2) ? (x - xh) : (E::NSPLIT == 2 ? xh : x);
         }

@@ -136,12 +136,12 @@ __global__ __launch_bounds__(256) void race_dw_partial(DWArgs a) {
 
 // dW[hw][l][t][c] = sum over (side, b, h, chunk) of
 // part[side][b * H + h][chunk][l * PE + t][c], with h = hw for per-head
-// tables and every head for shared ones.  One workgroup per output row
+// tables and every head for shared ones; dW rows have ld <= D columns.  One workgroup per output row
 // (hw, l, t): thread (c, g) adds the chunks g, g + G, ... of every (side, b,
 // h) in order, then the G group sums are added in order.
 static __global__ __launch_bounds__(1024) void race_dw_finalize(const float* __restrict__ part, int B, int H,
                                                                 int per_head, int nchunk, int NHP, int PE, int L,
-                                                                int P, int D, float* __restrict__ dW) {
+                                                                int P, int D, int ld, float* __restrict__ dW) {
   __shared__ float red[1024];
   const int row = blockIdx.x;
   const int hw = row / (L * P), lt = row % (L * P);
@@ -158,10 +158,10 @@ static __global__ __launch_bounds__(1024) void race_dw_finalize(const float* __r
       }
   red[threadIdx.x] = s;
   __syncthreads();
-  if (g == 0) {
+  if (g == 0 && c < ld) {
     float t = 0.f;
     for (int k = 0; k < G; ++k) t += red[k * D + c];
-    dW[(size_t)row * D + c] = t;
+    dW[(size_t)row * ld + c] = t;
   }
 }
 

@@ -14,24 +14,29 @@ namespace race {
 static_assert(DW_TT == TT, "dW tiles are the non-causal tiles");
 
 // Soft assignments of token rows written out as float32 [BH][N][L][R]
-// (a test export of the fused front end every kernel uses).
+// (a test export of the fused front end every kernel uses).  Token rows have
+// dr <= D elements (a multiple of 8); the kernel's columns past dr are zero.
 template <typename T, class G>
 __global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, Tables W, float beta,
-                                                           int L, int P, int64_t N, float* out) {
+                                                           int L, int P, int64_t N, int dr, float* out) {
   using E = Eng<T>;
   using frag = typename E::frag;
   __shared__ frag Wf[G::NPT * G::KD * 64];
   const int bh = blockIdx.y;
-  build_proj_frags<T, G>(W.at(bh), L, P, Wf);
+  build_proj_frags<T, G>(W.at(bh), W.ld, L, P, Wf);
   __syncthreads();
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
-  const T* X = static_cast<const T*>(Xv) + (size_t)bh * N * G::D;
+  const T* X = static_cast<const T*>(Xv) + (size_t)bh * N * dr;
   const int LR = L << G::PE;
   for (int64_t base = (int64_t)blockIdx.x * TT + 32 * w; base < N; base += (int64_t)gridDim.x * TT) {
     const int64_t tok = base + n;
     const bool valid = tok < N;
     frag xf[G::KD];
-    load_row_frags<T, G>(valid ? X + tok * G::D : nullptr, xf);
+#pragma unroll
+    for (int q = 0; q < G::KD; ++q) {
+      const int c0 = 16 * q + 8 * h;   // 8 consecutive columns, all inside dr or all past it
+      xf[q] = (valid && c0 < dr) ? *reinterpret_cast<const frag*>(X + tok * dr + c0) : E::zero();
+    }
     float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, xf, pre);
     soft_assign<G>(pre, 2.f * beta, L, u, phi);
@@ -63,9 +68,9 @@ struct Inst {
   static void bwd_kv(const NCArgs& a, dim3 g, hipStream_t s) {
     hipLaunchKernelGGL((race_bwd_kv<T, G>), g, dim3(256), 0, s, a);
   }
-  static void dbg(const void* X, const Tables& W, float beta, int L, int P, int64_t N, float* out,
+  static void dbg(const void* X, const Tables& W, float beta, int L, int P, int64_t N, int dr, float* out,
                   dim3 g, hipStream_t s) {
-    hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, out);
+    hipLaunchKernelGGL((race_softbucket_dbg<T, G>), g, dim3(256), 0, s, X, W, beta, L, P, N, dr, out);
   }
   template <int MODE>
   static void walk(const WArgs& a, dim3 g, hipStream_t s) {

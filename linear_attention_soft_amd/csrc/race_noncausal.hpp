@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
 
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   __syncthreads();
 
   const T* X = static_cast<const T*>(a.X) + (size_t)bh * a.N * G::D;
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   __shared__ T OS[4][OutStage<G::D, T>::ELEMS];
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int lane = lane_id(), n = lane & 31, w = threadIdx.x >> 6;
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   build_readout_frags<T, G>(a.st_content + (size_t)bh * G::LRP * G::D, a.st_mass + (size_t)bh * G::LRP, RF);
   __syncthreads();
 
@@ -414,9 +414,9 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const float* content = a.st_content + (size_t)bh * G::LRP * G::D;
   const float* mass = a.st_mass + (size_t)bh * G::LRP;
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   build_bank_rows_frags<T, G, false>(content, DF);
-  build_wt_frags<T, G>(a.W.at(bh), a.L, a.P, WTf);
+  build_wt_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, WTf);
   for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) massL[i] = mass[i];
   __syncthreads();
 
@@ -539,10 +539,10 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
   const float* dcontent = a.st_content + (size_t)bh * G::LRP * G::D;
   const float* dmass = a.st_mass + (size_t)bh * G::LRP;
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   build_bank_cols_frags<T, G>(dcontent, VF);
   build_bank_rows_frags<T, G, false>(dcontent, KF);
-  build_wt_frags<T, G>(a.W.at(bh), a.L, a.P, WTf);
+  build_wt_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, WTf);
   for (int i = threadIdx.x; i < G::LRP; i += blockDim.x) dmassL[i] = dmass[i];
   __syncthreads();
 

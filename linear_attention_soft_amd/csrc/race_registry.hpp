@@ -15,7 +15,7 @@ struct Tables;
 typedef void (*nc_launch_fn)(const NCArgs&, dim3 grid, hipStream_t);
 typedef void (*tw_launch_fn)(const TWArgs&, dim3 grid, hipStream_t);
 typedef void (*w_launch_fn)(const WArgs&, dim3 grid, hipStream_t);
-typedef void (*dbg_launch_fn)(const void* X, const Tables& W, float beta, int L, int P, int64_t N,
+typedef void (*dbg_launch_fn)(const void* X, const Tables& W, float beta, int L, int P, int64_t N, int dr,
                               float* out, dim3 grid, hipStream_t);
 
 struct KernelSet {

@@ -272,7 +272,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   const int win = w % C::NWIN;
   const int ct = w - C::NF;
 
-  build_proj_frags<T, G>(a.W.at(bh), a.L, a.P, Wf);
+  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   if ((C::MASS && is_f && role_b) || (C::STATIC && C::MBUF && is_f)) {
     for (int r = lane; r < C::WROWS; r += 64) {
       const int row = win * C::WROWS + r;

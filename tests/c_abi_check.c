@@ -53,9 +53,14 @@ int main(void) {
   EXPECT(race_attn_fwd(Q, K, V, W, 1.0f, 4, 2, 0, O, &s, NULL, 0, ws, 16, NULL) == RACE_ERR_WORKSPACE,
          "workspace too small");
   EXPECT(strlen(race_last_error()) > 0, "last error message set");
-  s.d = 96;
+  s.d = 100;
   EXPECT(race_attn_fwd(Q, K, V, W, 1.0f, 4, 2, 0, O, &s, NULL, 0, ws, wf, NULL) == RACE_ERR_UNSUPPORTED,
-         "d = 96 unsupported");
+         "d = 100 (not a multiple of 8) unsupported");
+  s.d = 136;
+  EXPECT(race_attn_fwd(Q, K, V, W, 1.0f, 4, 2, 0, O, &s, NULL, 0, ws, wf, NULL) == RACE_ERR_UNSUPPORTED,
+         "d = 136 (above 128) unsupported");
+  s.d = 96;
+  EXPECT(race_attn_workspace_bytes(&s, 4, 2, 0, RACE_WS_FWD) > wf, "d = 96 runs on padded rows");
   s.d = 128;
   s.w_per_head = 2;
   EXPECT(race_attn_fwd(Q, K, V, W, 1.0f, 4, 2, 0, O, &s, NULL, 0, ws, wf, NULL) == RACE_ERR_INVALID_ARG,

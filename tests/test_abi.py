@@ -68,6 +68,25 @@ def test_size_queries():
         for ph in (1, 2):
             assert (race.race_attn_workspace_bytes(s, 4, 2, causal, ph | 4)
                     > race.race_attn_workspace_bytes(s, 4, 2, causal, ph))
+
+
+@pytest.mark.parametrize("d,D", [(96, 128), (72, 128), (40, 64), (8, 64)])
+def test_head_dims_below_a_compiled_one(d, D):
+    """A head dim d (a multiple of 8) below a compiled one D runs on D's
+    kernels: the same state, plus room for zero-padded token tensors (forward:
+    Q, K, V, O; backward: Q, K, V, dO, O, dQ, dK, dV; prefill: K, V)."""
+    N, P, L = 4096, (4 if D == 128 else 3), 2
+    s, t = _shape(N=N, d=d), _shape(N=N, d=D)
+    tb = -(-2 * N * D * 2 // 256) * 256                # B*H x N x D bf16, 256-byte aligned
+    for causal in (False, True):
+        assert race.race_attn_state_bytes(s, P, L, causal) == race.race_attn_state_bytes(t, P, L, causal)
+        for ph, n in ((0, 4), (1, 8), (2, 8), (5, 8)):
+            assert (race.race_attn_workspace_bytes(s, P, L, causal, ph)
+                    == race.race_attn_workspace_bytes(t, P, L, causal, ph) + n * tb)
+    Lb = _lib()
+    assert Lb.race_attn_decode_state_bytes(ctypes.byref(s), P, L) == Lb.race_attn_decode_state_bytes(ctypes.byref(t), P, L)
+    assert (Lb.race_attn_decode_prefill_workspace_bytes(ctypes.byref(s), P, L)
+            == Lb.race_attn_decode_prefill_workspace_bytes(ctypes.byref(t), P, L) + 2 * tb)
     # invalid arguments give 0
     assert race.race_attn_state_bytes(s, 0, 2, False) == 0
     assert race.race_attn_state_bytes(s, 4, 0, False) == 0
@@ -105,7 +124,8 @@ def test_forward_rejects_bad_arguments(kw, code):
 
 
 @pytest.mark.parametrize("shape,code", [
-    (_shape(d=96), 2), (_shape(d=0), 1), (_shape(N=0), 1), (_shape(B=0), 1), (_shape(dtype=7), 1),
+    (_shape(d=100), 2), (_shape(d=136), 2), (_shape(d=0), 1), (_shape(N=0), 1), (_shape(B=0), 1),
+    (_shape(dtype=7), 1),
     (_shape(w_per_head=2), 1),
 ])
 def test_forward_rejects_bad_shapes(shape, code):
@@ -154,7 +174,7 @@ def test_decode_rejects_bad_arguments():
     base = [FAKE + i * 0x1000000 for i in range(8)]
     nb = Lb.race_attn_decode_state_bytes(ctypes.byref(s), 3, 2)
     assert nb > 0
-    assert Lb.race_attn_decode_state_bytes(ctypes.byref(_shape(d=96)), 3, 2) == 0
+    assert Lb.race_attn_decode_state_bytes(ctypes.byref(_shape(d=100)), 3, 2) == 0
 
     def call(q=base[0], state=base[5], sb=nb, beta=1.0, shape=s):
         return Lb.race_attn_decode(q, base[1], base[2], base[3], ctypes.c_float(beta), 3, 2, base[4],
@@ -165,7 +185,7 @@ def test_decode_rejects_bad_arguments():
     assert call(beta=math.inf) == 1
     assert call(sb=16) == 3
     assert call(q=base[0] + 4) == 1             # misaligned
-    assert call(shape=_shape(d=96)) == 2
+    assert call(shape=_shape(d=100)) == 2
     wb = Lb.race_attn_decode_prefill_workspace_bytes(ctypes.byref(s), 3, 2)
     assert wb > 0
     assert Lb.race_attn_decode_prefill(base[1], base[2], base[3], ctypes.c_float(1.0), 3, 2, ctypes.byref(s),
