@@ -47,6 +47,7 @@ struct KernelSet {
   X(bf16_d64)                   \
   X(bf16_d128_p3)               \
   X(bf16_d128_p4)               \
+  X(bf16_d128_p5)               \
   X(bf16_d128_p6)               \
   X(f32_d64)                    \
   X(f32_d128)

@@ -1,5 +1,6 @@
 """GPU parity of the non-causal layer at 64 corners per table (P = 6, up to
-L = 4 tables: 256 bucket rows), against the fp64 oracle.
+L = 4 tables: 256 bucket rows), and of both variants at 32 corners (P = 5),
+against the fp64 oracle.
 
 Tables this wide run the non-causal layer through the static-bank walks:
 every query reads the one bank of all keys (slides frame "Each bucket
@@ -50,6 +51,27 @@ def test_wide_noncausal_parity(N, B, H, L):
     tol = TOL["bf16"]
     check("O", O, oracle_fwd(inp, False), tol, vmax=float(np.abs(to64(inp["V"])).max()))
     rdQ, rdK, rdV = oracle_bwd(inp, False)
+    check("dQ", dQ, rdQ, tol)
+    check("dK", dK, rdK, tol)
+    check("dV", dV, rdV, tol)
+
+
+@pytest.mark.parametrize("causal,N,L", [(False, 3100, 1), (False, 4500, 4), (True, 2300, 2), (True, 1900, 4)])
+def test_p5_parity(causal, N, L):
+    """P = 5 (32 corners per table): the causal walks and, non-causal, the
+    static-bank walks (the non-causal kernels' LDS stages do not fit a
+    128-row bank at this width)."""
+    w = replace(ri.WORKLOADS[5].with_size(N=N, B=1, H=2), causal=causal, P=5, L=L)
+    inp = ri.make_inputs(w, device="cpu", with_grad_out=True)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    say(f"P=5 causal={causal} N={N} L={L} beta={w.beta}")
+    O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal)
+    dQ, dK, dV = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal,
+                                    dev["dO"], state, O=O if causal else None)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    check("O", O, oracle_fwd(inp, causal), tol, vmax=float(np.abs(to64(inp["V"])).max()))
+    rdQ, rdK, rdV = oracle_bwd(inp, causal)
     check("dQ", dQ, rdQ, tol)
     check("dK", dK, rdK, tol)
     check("dV", dV, rdV, tol)
