@@ -318,24 +318,23 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     const bool valid = t0 + n < s1;
     // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
-    float preA[G::NHP], phA[URP / 2];
+    float preA[G::NHP], evA[G::NHP], phA[URP / 2];
     {
       frag xa[G::KD];
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[bb][n * FS + 16 * q + 8 * h]);
-      float uA[G::NHP];
       if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, preA);
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
-      soft_assign_rows<G, R0, URP>(preA, beta2, a.L, uA, phA);
+      soft_assign_rows<G, R0, URP>(preA, beta2, a.L, evA, phA);
     }
     if constexpr (!STATIC) {
       frag xb[G::KD];
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[bb][n * FS + 16 * q + 8 * h]);
-      float pre[G::NHP], uB[G::NHP], phB[URP / 2];
+      float pre[G::NHP], evB[G::NHP], phB[URP / 2];
       if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
-      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, uB, phB);
+      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, evB, phB);
       T* pt = S.PhiBT[w];
 #pragma unroll
       for (int at = 0; at < ATU; ++at)
@@ -439,7 +438,9 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         }
       } else {
         // half table: exchange the sums with the other half (waves 2j, 2j + 1),
-        // add them in the same order in both, then dU_t = A_t - s tanh(beta u_t)
+        // add them in the same order in both, then dU_t = A_t - s E[v_t] with
+        // E[v_t] = tanh(beta u_t) from the soft assignment; each lane half
+        // takes the hyperplanes it evaluated there
         constexpr bool LOWER = (TG & 1) == 0;
         constexpr int l = R0 / G::R;
         float part[1 + G::PE];
@@ -451,18 +452,18 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         __syncthreads();
         const float s = S.XS[w & ~1][0][n] + S.XS[w | 1][0][n];
 #pragma unroll
-        for (int t = 0; t < G::PE; ++t) {
+        for (int t = 0; t < G::PE; t += 2) {
+          const bool pair = t + 1 < G::PE;
+          const int tt = pair ? t + h : t;
           float uu, s2;
-          tanh_sech2(preA[l * G::PE + t], uu, s2);
-          const float du = (S.XS[w & ~1][1 + t][n] + S.XS[w | 1][1 + t][n]) - s * tanh_f(a.beta * uu);
-          dpre[l * G::PE + t] = a.beta * du * s2;
-          bterm += uu * du;
+          tanh_sech2((pair && h) ? preA[l * G::PE + t + 1] : preA[l * G::PE + t], uu, s2);
+          const float du = (S.XS[w & ~1][1 + tt][n] + S.XS[w | 1][1 + tt][n]) - s * evA[l * G::PE + t];
+          if (pair || h == 0) {
+            bterm += uu * du;
+            if (LOWER) S.DP[bb][n * G::NHP + l * G::PE + tt] = a.beta * du * s2;
+          }
         }
-        if (LOWER && valid && h == 0) bsum += bterm;
-        if (LOWER && h == 0) {
-#pragma unroll
-          for (int t = 0; t < G::PE; ++t) S.DP[bb][n * G::NHP + l * G::PE + t] = dpre[l * G::PE + t];
-        }
+        if (LOWER && valid) bsum += bterm;
       }
     }
     // rows of chunk k + 1: loaded here rather than at the top of the chunk

@@ -161,7 +161,20 @@ __device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
   sm = pos ? q : p;
 }
 
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+// The two 32-lane halves of a wave exchanged in one VALU instruction
+// (v_permlane32_swap): with both operands x it returns lanes 0-31 of x in
+// every half (first) and lanes 32-63 of x in every half (second).
+struct HalfPair { float lo, hi; };
+__device__ __forceinline__ HalfPair halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Value of the same lane in the other half of the wave.
+__device__ __forceinline__ float xor32(float v) {
+  const HalfPair p = halves(v);
+  return (threadIdx.x & 32) ? p.lo : p.hi;
+}
 
 // Projection tables: float32 [L][P][ld] shared by every head (hstride 0), or
 // [H][L][P][ld] with one set per head (hstride L * P * ld).  Sequence bh of a
@@ -461,21 +474,40 @@ __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict_
 // section 2.4): phi_r = prod_t sigma(2 beta u_t v_{r,t}), u = tanh(pre).
 // Lane half h owns the corners whose bit 2 equals h.  Only bucket rows
 // [R0, R0 + NROWS) are produced (R0 and NROWS multiples of 32); rows of tables
-// >= L and padding rows are 0.  u receives tanh(pre) of every hyperplane slot.
+// >= L and padding rows are 0.
+//
+// Both lane halves hold the same token, so of each pair of hyperplanes
+// (t, t + 1) half h evaluates tanh and the sigmoid pair of t + h only, and one
+// half swap hands every lane both (an odd last hyperplane is evaluated in
+// both halves).  ev receives E[v_t] = sigma(2 beta u_t) - sigma(-2 beta u_t)
+// = tanh(beta u_t) of the hyperplane this half evaluated, in slot l * PE + t
+// of the pair's first hyperplane t (the softmax backward of split tables
+// uses it).
 template <class G, int R0, int NROWS>
 __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], float beta2, int L,
-                                                 float (&u)[G::NHP], float (&phi)[NROWS / 2]) {
+                                                 float (&ev)[G::NHP], float (&phi)[NROWS / 2]) {
   static_assert(R0 % 32 == 0 && NROWS % 32 == 0 && R0 + NROWS <= G::LRP, "row window");
   const int h = lane_id() >> 5;
-#pragma unroll
-  for (int hp = 0; hp < G::NHP; ++hp) u[hp] = tanh_f(pre[hp]);
   constexpr int L0 = R0 / G::R;
   constexpr int L1 = cdiv(R0 + NROWS, G::R) < G::LMAX ? cdiv(R0 + NROWS, G::R) : G::LMAX;
 #pragma unroll
   for (int l = L0; l < L1; ++l) {
     float sp[G::PE], sm[G::PE];
 #pragma unroll
-    for (int t = 0; t < G::PE; ++t) sigmoid_pair(beta2 * u[l * G::PE + t], sp[t], sm[t]);
+    for (int t = 0; t < G::PE; t += 2) {
+      if (t + 1 < G::PE) {
+        const float x = h ? pre[l * G::PE + t + 1] : pre[l * G::PE + t];
+        float p, q;
+        sigmoid_pair(beta2 * tanh_f(x), p, q);
+        ev[l * G::PE + t] = p - q;
+        const HalfPair hp = halves(p), hq = halves(q);
+        sp[t] = hp.lo; sp[t + 1] = hp.hi;
+        sm[t] = hq.lo; sm[t + 1] = hq.hi;
+      } else {
+        sigmoid_pair(beta2 * tanh_f(pre[l * G::PE + t]), sp[t], sm[t]);
+        ev[l * G::PE + t] = sp[t] - sm[t];
+      }
+    }
     const float f2 = h ? sp[2] : sm[2];
     float g[4];
     g[0] = sm[0] * sm[1] * f2;
@@ -516,8 +548,8 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
 
 template <class G>
 __device__ __forceinline__ void soft_assign(const float (&pre)[G::NHP], float beta2, int L,
-                                            float (&u)[G::NHP], float (&phi)[G::LRP / 2]) {
-  soft_assign_rows<G, 0, G::LRP>(pre, beta2, L, u, phi);
+                                            float (&ev)[G::NHP], float (&phi)[G::LRP / 2]) {
+  soft_assign_rows<G, 0, G::LRP>(pre, beta2, L, ev, phi);
 }
 
 // B operand of K16 step q from a TLAYOUT vector held in registers.

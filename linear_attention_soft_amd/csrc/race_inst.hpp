@@ -37,9 +37,9 @@ __global__ __launch_bounds__(256) void race_softbucket_dbg(const void* Xv, Table
       const int c0 = 16 * q + 8 * h;   // 8 consecutive columns, all inside dr or all past it
       xf[q] = (valid && c0 < dr) ? *reinterpret_cast<const frag*>(X + tok * dr + c0) : E::zero();
     }
-    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    float pre[G::NHP], ev[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, xf, pre);
-    soft_assign<G>(pre, 2.f * beta, L, u, phi);
+    soft_assign<G>(pre, 2.f * beta, L, ev, phi);
     if (valid) {
 #pragma unroll
       for (int at = 0; at < G::AT; ++at)

@@ -305,10 +305,10 @@ __global__ __launch_bounds__(256) void race_bucket_reduce(NCArgs a) {
   for (int64_t base = t_begin; base < t_end; base += step) {
     const int64_t tok = base + tl;
     const bool valid = tok < t_end;
-    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    float pre[G::NHP], ev[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, xa, pre);
     load_x(base + step);
-    soft_assign<G>(pre, beta2, a.L, u, phi);
+    soft_assign<G>(pre, beta2, a.L, ev, phi);
 #pragma unroll
     for (int at = 0; at < G::AT; ++at)
 #pragma unroll
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(256) void race_readout_norm(NCArgs a) {
   auto tile = [&](const frag (&cx)[G::KD], int64_t base) {
     const int64_t tok = base + n;
     const bool valid = tok < t_end;
-    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    float pre[G::NHP], ev[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, cx, pre);
-    soft_assign<G>(pre, beta2, a.L, u, phi);
+    soft_assign<G>(pre, beta2, a.L, ev, phi);
     f32x16 acc[G::CT + 1];
     readout_mma<T, G>(RF, phi, acc);
     const float inv = 1.f / acc[G::CT][0];
@@ -447,10 +447,10 @@ __global__ __launch_bounds__(256, 2) void race_bwd_q(NCArgs a) {
     frag cy[G::KD];
 #pragma unroll
     for (int q = 0; q < G::KD; ++q) cy[q] = valid ? ya[q] : E::zero();
-    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    float pre[G::NHP], ev[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, xa, pre);
     load_x(base + step);
-    soft_assign<G>(pre, beta2, a.L, u, phi);
+    soft_assign<G>(pre, beta2, a.L, ev, phi);
     if (!valid) {
 #pragma unroll
       for (int i = 0; i < G::LRP / 2; ++i) phi[i] = 0.f;
@@ -559,9 +559,9 @@ __global__ __launch_bounds__(256) void race_bwd_kv(NCArgs a) {
   auto tile = [&](const frag (&cx)[G::KD], const frag (&cy)[G::KD], int64_t base) {
     const int64_t tok = base + n;
     const bool valid = tok < t_end;
-    float pre[G::NHP], u[G::NHP], phi[G::LRP / 2];
+    float pre[G::NHP], ev[G::NHP], phi[G::LRP / 2];
     project<T, G>(Wf, cx, pre);
-    soft_assign<G>(pre, beta2, a.L, u, phi);
+    soft_assign<G>(pre, beta2, a.L, ev, phi);
     // dV = sum_l Phi_K dcontent
     frag pb[G::KL];
 #pragma unroll

@@ -140,9 +140,9 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
   const int64_t tok = t0 + n;
   const bool valid = tok < s1;
-  float pre[G::NHP], u[G::NHP], phi[WROWS / 2];
+  float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
   project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
-  soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, u, phi);
+  soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi);
   frag fq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
