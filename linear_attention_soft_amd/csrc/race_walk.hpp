@@ -25,10 +25,12 @@
 // Modes:
 //   W_SEGSUM  bank of every segment: S = Phi_K^T V, m = Phi_K^T 1
 //   W_GSUM    gradient bank of every segment: Phi_Q^T g, Phi_Q^T h
-//             with g = dO / den, h = -(dO . O) / den
+//             with g = dO / den, h = -(dO . O) / den, formed as
+//             (Phi_Q / den)^T dO and (Phi_Q / den)^T (h den): the state-role
+//             features absorb 1 / den and X = dO stays exact
 //   W_FWD     O = y / den from the segment's starting bank; writes den
 //   W_H       h = -(dO . y) / den^2 (y = O den), without O
-//   W_DV      reverse walk, output role K, state role Q, X = g:
+//   W_DV      reverse walk, output role K, state role Q / den, X = dO:
 //             dV_j = sum_{t >= j} (phi_K,j . phi_Q,t) g_t
 // Static modes (the non-causal layer for bucket counts whose whole bank does
 // not fit one wave): every token reads one fixed bank per (batch, head) (the
@@ -49,7 +51,7 @@ enum { W_SEGSUM = 0, W_GSUM = 1, W_FWD = 2, W_H = 3, W_DV = 4, W_FWD_ST = 5, W_H
 struct WArgs {
   const void* A_src;      // output-role token rows (FWD, H: Q; DV: K)
   const void* B_src;      // state-role token rows (SEGSUM, FWD, H: K; GSUM, DV: Q)
-  const void* X_src;      // state-role values (V; GSUM, DV: dO, divided by den)
+  const void* X_src;      // state-role values (V; GSUM, DV: dO)
   const void* dO;         // H: dO rows of the output role
   void* out;              // FWD: O (NULL: only Den is written); DV: dV
   float* bank_out;        // SEGSUM, GSUM: [BH][nseg][LRP][d+1]
@@ -88,11 +90,13 @@ struct RWCfg {
   static constexpr int NF = ROLES * NWIN;                   // feature waves
   static constexpr int NM = G::CT;                          // bank waves
   static constexpr int NT = 64 * (NF + NM);
-  static constexpr bool XSPLIT = (BM == W_GSUM || BM == W_DV) && !STATIC && Eng<T>::NSPLIT == 2;
   static constexpr bool MASS = (BM == W_SEGSUM || BM == W_GSUM || BM == W_FWD) && !STATIC;   // mass updates
   static constexpr bool MBUF = MASS || (STATIC && BM != W_DV);   // a bucket mass is kept in LDS
   static constexpr bool DEN = BM == W_FWD || (STATIC && BM == W_H);   // feature waves form Phi_A mass
-  static constexpr bool XDEN = (BM == W_GSUM || BM == W_DV) && !STATIC;   // X rows divided by den
+  // GSUM, DV: the state role's features are divided by its token's den, so
+  // that with X = dO the bank sums phi_Q g^T (and, GSUM, with mass weights
+  // h den, phi_Q h)
+  static constexpr bool PHIDEN = (BM == W_GSUM || BM == W_DV) && !STATIC;
   static constexpr bool XROWS = !STATIC;                    // bank waves read X rows
   // frag-ordered feature row per token and bank-wave X tile row (elements):
   // with bf16, rows 12 dwords apart (mod 64 banks) keep both the 16-byte row
@@ -101,7 +105,6 @@ struct RWCfg {
   static constexpr int FR = G::KL * 16 + (std::is_same<T, bf16>::value ? 24 : 8);
   static constexpr int TS = WC + 8;             // transposed feature row per bucket (elements)
   static constexpr int XSP = 32 + (std::is_same<T, bf16>::value ? 24 : 8);
-  static constexpr int NXS = XSPLIT ? 2 : 1;
   // bf16: the state-role features are kept in token-major rows only (PhiB)
   // and read transposed (bank-update operands, bucket masses) with
   // transposing LDS loads; float32 keeps a transposed copy (PhiBT)
@@ -126,8 +129,9 @@ __device__ __forceinline__ int64_t chunk_t0(int64_t s0, int64_t nch, int64_t k) 
 // the mass bookkeeping of the window.
 template <typename T, class G, int MODE, int R0>
 __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename Eng<T>::frag* __restrict__ Wf,
-                                                  const typename Eng<T>::frag (&xf)[G::KD], float hv, bool role_b,
-                                                  int64_t t0, int64_t s1, int b, int fw, T* __restrict__ PhiA,
+                                                  const typename Eng<T>::frag (&xf)[G::KD], float hv, float dv,
+                                                  bool role_b, int64_t t0, int64_t s1, int b, int fw,
+                                                  T* __restrict__ PhiA,
                                                   T* __restrict__ PhiB, T* __restrict__ PhiBT,
                                                   float* __restrict__ mbuf, float* __restrict__ dpart,
                                                   float* __restrict__ hw, int win) {
@@ -143,6 +147,11 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
   project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
   soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi);
+  if (C::PHIDEN && role_b) {
+    const float rden = 1.f / dv;
+#pragma unroll
+    for (int i = 0; i < WROWS / 2; ++i) phi[i] *= rden;
+  }
   frag fq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -181,7 +190,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
       for (int i = 0; i < 8; ++i) bt[(R0 + kmap(q, h, i)) * C::TS + n] = fq[q][i];
   }
   if (C::MASS) {
-    if (C::BM == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv : 0.f;
+    if (C::BM == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv * dv : 0.f;
     wave_lds_sync();
     // mass after the chunk = mass before + column sums of the rounded phi_B
     // (GSUM: weighted by h)
@@ -222,15 +231,16 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
 
 template <typename T, class G, int MODE, int WI>
 __device__ __forceinline__ void rw_feature_dispatch(int win, const WArgs& a, const typename Eng<T>::frag* Wf,
-                                                    const typename Eng<T>::frag (&xf)[G::KD], float hv, bool role_b,
+                                                    const typename Eng<T>::frag (&xf)[G::KD], float hv, float dv,
+                                                    bool role_b,
                                                     int64_t t0, int64_t s1, int b, int fw, T* PhiA, T* PhiB,
                                                     T* PhiBT, float* mbuf, float* dpart, float* hw) {
   using C = RWCfg<T, G, MODE>;
   if (win == WI) {
-    rw_feature_window<T, G, MODE, WI * C::WROWS>(a, Wf, xf, hv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
+    rw_feature_window<T, G, MODE, WI * C::WROWS>(a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
                                                  dpart, hw, WI);
   } else if constexpr (WI + 1 < C::NWIN) {
-    rw_feature_dispatch<T, G, MODE, WI + 1>(win, a, Wf, xf, hv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
+    rw_feature_dispatch<T, G, MODE, WI + 1>(win, a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
                                             dpart, hw);
   }
 }
@@ -252,7 +262,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   __shared__ __attribute__((aligned(16))) T PhiA[C::HAS_A ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiB[C::ROWS_B ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiBT[(C::TRLOAD || C::STATIC) ? 8 : 2 * G::LRP * TS];
-  __shared__ __attribute__((aligned(16))) T Xs[C::NM * C::NXS * WC * XSP];
+  __shared__ __attribute__((aligned(16))) T Xs[C::NM * WC * XSP];
   __shared__ float mbuf[C::MBUF ? 2 * G::LRP : 1];
   __shared__ float dpart[C::DEN ? 2 * C::NWIN * WC : 1];
   __shared__ float hpart[C::BM == W_H ? 2 * C::NM * WC : 1];
@@ -286,37 +296,39 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     // ---------------------------------------------------------------- feature waves
     const T* src = static_cast<const T*>(role_b ? a.B_src : a.A_src) + rb * G::D;
     const float* hsrc = a.hvec + rb;
+    const float* dsrc = a.den + rb;
     frag xa[G::KD], xb[G::KD];
-    float ha = 0.f, hb = 0.f;
+    float ha = 0.f, hb = 0.f, da = 1.f, db = 1.f;   // h and den of the wave's token
     // Loads are issued for every iteration (the chunk index clamped to the
     // last one) so no prefetch sits behind a branch: the compiler then waits
     // only for the rows a projection actually consumes.
-    auto load = [&](int64_t k, frag(&xf)[G::KD], float& hv) {
+    auto load = [&](int64_t k, frag(&xf)[G::KD], float& hv, float& dv) {
       const int64_t t0 = chunk_t0<C::REV>(s0, nch, k < nch ? k : nch - 1);
       const int64_t row = min(t0 + n, s1 - 1);
       if (C::BM == W_GSUM) hv = hsrc[row];
+      if (C::PHIDEN && role_b) dv = dsrc[row];
       load_row_frags_nb<T, G>(src + row * G::D, xf);
     };
-    auto feat = [&](int64_t k, const frag(&xf)[G::KD], float hv) {
+    auto feat = [&](int64_t k, const frag(&xf)[G::KD], float hv, float dv) {
       const int64_t t0 = chunk_t0<C::REV>(s0, nch, k);
-      rw_feature_dispatch<T, G, MODE, 0>(win, a, Wf, xf, hv, role_b, t0, s1, (int)(k & 1), w, PhiA, PhiB, PhiBT,
-                                         mbuf, dpart, hw);
+      rw_feature_dispatch<T, G, MODE, 0>(win, a, Wf, xf, hv, dv, role_b, t0, s1, (int)(k & 1), w, PhiA, PhiB,
+                                         PhiBT, mbuf, dpart, hw);
     };
-    load(0, xa, ha);
-    load(1, xb, hb);
+    load(0, xa, ha, da);
+    load(1, xb, hb, db);
     __syncthreads();
-    feat(0, xa, ha);
+    feat(0, xa, ha, da);
     __syncthreads();
     // iteration k: features of chunk k + 1 (rows in xb), rows of chunk k + 2 -> xa
     for (int64_t k = 0; k < nch; k += 2) {
-      load(k + 2, xa, ha);
+      load(k + 2, xa, ha, da);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 1 < nch) feat(k + 1, xb, hb);
+      if (k + 1 < nch) feat(k + 1, xb, hb, db);
       __syncthreads();
       if (k + 1 >= nch) break;
-      load(k + 3, xb, hb);
+      load(k + 3, xb, hb, db);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 2 < nch) feat(k + 2, xa, ha);
+      if (k + 2 < nch) feat(k + 2, xa, ha, da);
       __syncthreads();
     }
     if (C::MASS && role_b && (C::BM == W_SEGSUM || C::BM == W_GSUM)) {
@@ -343,14 +355,13 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       }
     }
   }
-  T* xs = Xs + ct * C::NXS * WC * XSP;
+  T* xs = Xs + ct * WC * XSP;
   const T* Xg = static_cast<const T*>(a.X_src) + rb * G::D + 32 * ct;
   const T* dOg = (C::BM == W_H) ? static_cast<const T*>(a.dO) + rb * G::D + 32 * ct : nullptr;
   const float* den = a.den + rb;
 
-  // prefetch registers: X row slices (+ den of their rows), dO slices (H)
+  // prefetch registers: X row slices, dO slices (H)
   uint4 xr[XIT];
-  float xd[XIT];
   typename E::vec4 dor[4];
   auto prefetch = [&](int64_t k) {
     const int64_t t0 = chunk_t0<C::REV>(s0, nch, k);
@@ -360,7 +371,6 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
         const int flat = it * 64 + lane;
         const int64_t row = min(t0 + flat / CPR, s1 - 1);
         xr[it] = *reinterpret_cast<const uint4*>(Xg + row * G::D + (flat % CPR) * EPC);
-        if (C::XDEN) xd[it] = den[row];
       }
     }
     if (C::BM == W_H) {
@@ -397,21 +407,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       const int flat = it * 64 + lane;
       const int row = flat / CPR, ch = flat % CPR;
       const bool ok = t0 + row < s1;
-      const T* e = reinterpret_cast<const T*>(&xr[it]);
-      if (C::XDEN || C::XSPLIT) {
-        const float sc = C::XDEN ? 1.f / xd[it] : 1.f;
-        T hi8[EPC], lo8[EPC];
-#pragma unroll
-        for (int kk = 0; kk < EPC; ++kk) {
-          const float f = ok ? (float)e[kk] * sc : 0.f;
-          hi8[kk] = (T)f;
-          lo8[kk] = (T)(f - (float)hi8[kk]);
-        }
-        *reinterpret_cast<uint4*>(xs + row * XSP + ch * EPC) = *reinterpret_cast<const uint4*>(hi8);
-        if (C::XSPLIT) *reinterpret_cast<uint4*>(xs + WC * XSP + row * XSP + ch * EPC) = *reinterpret_cast<const uint4*>(lo8);
-      } else {
-        *reinterpret_cast<uint4*>(xs + row * XSP + ch * EPC) = ok ? xr[it] : make_uint4(0, 0, 0, 0);
-      }
+      *reinterpret_cast<uint4*>(xs + row * XSP + ch * EPC) = ok ? xr[it] : make_uint4(0, 0, 0, 0);
     }
     typename E::vec4 dcur[4];
     if (C::BM == W_H) {
@@ -422,7 +418,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     __builtin_amdgcn_sched_barrier(0);
     wave_lds_sync();
     // X frags, k over tokens by kmap: lane (c, h) holds X[kmap(s, h, i)][c]
-    frag xk[2], xl[2];
+    frag xk[2];
     if constexpr (!C::XROWS) {
       // static modes read no X rows
     } else if constexpr (C::TRLOAD) {
@@ -430,7 +426,6 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         xk[s] = load_kcol_tr(xs, XSP, 16 * s, 0, plain);
-        if (C::XSPLIT) xl[s] = load_kcol_tr(xs + WC * XSP, XSP, 16 * s, 0, plain);
       }
     } else {
 #pragma unroll
@@ -438,7 +433,6 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           xk[s][i] = xs[kmap(s, h, i) * XSP + n];
-          if (C::XSPLIT) xl[s][i] = xs[WC * XSP + kmap(s, h, i) * XSP + n];
         }
     }
 
@@ -489,7 +483,6 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
           for (int i = 0; i < 8; ++i) s8[i] = sc[8 * s + i];
           const frag sb = E::pack(s8);
           E::mma(xk[s], sb, y);
-          if (C::XSPLIT) E::mma(xl[s], sb, y);
         }
       }
       // static H: Den of this chunk's tokens from the feature waves' parts
@@ -566,7 +559,6 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
 #pragma unroll
         for (int at = 0; at < G::AT; ++at) {
           E::mma(af[at], xk[s], st[at]);
-          if (C::XSPLIT) E::mma(af[at], xl[s], st[at]);
         }
       }
     }
