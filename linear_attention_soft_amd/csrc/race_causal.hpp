@@ -91,6 +91,14 @@ struct TWCfg {
   // writes (rows 4 apart fall 96 bytes apart) and its 8-byte operand reads (32
   // consecutive rows start on distinct 8-byte bank pairs) free of bank conflicts
   static constexpr int TSP = WC + 12;
+  // bf16: the state-role features of the chunk are kept token-major per
+  // wave (rows of the wave's URP bucket rows, RS elements apart) and read
+  // transposed by transposing LDS loads (intra and bank-update operands,
+  // bucket masses).  Rows 24 dwords apart: the four rows that one 16-lane
+  // group of such a load reads fall on disjoint banks.  float32 keeps the
+  // transposed copy (TSP-element rows per bucket row).
+  static constexpr bool TRB = std::is_same<T, bf16>::value;
+  static constexpr int RS = URP + 16;
   static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
   static constexpr int EPC = 16 / (int)sizeof(T);
   static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
@@ -108,7 +116,7 @@ struct TWLds {
   static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
   typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
-  alignas(16) T PhiBT[C::NM][STATIC ? 8 : C::URP * C::TSP];   // wave-private Phi_B^T of the current chunk
+  alignas(16) T PhiBT[C::NM][STATIC ? 8 : (C::TRB ? WC * C::RS : C::URP * C::TSP)];   // wave-private Phi_B
   alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
   alignas(16) T AR[2][WC * C::FS];               // output-role rows (projection operands)
   alignas(16) T BR[2][SROWS];                    // state-role rows
@@ -176,6 +184,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
   constexpr int EPC = C::EPC, CPR = C::CPR;
   using WT = WinTiles<G, R0, URP>;
   typedef T T4 __attribute__((ext_vector_type(4)));
+  auto plain = [](int c) { return c; };
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
   const int w = TG;
   const int tid = threadIdx.x;
@@ -235,7 +244,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       pu[i] = *reinterpret_cast<const uint4*>(Ug + row * G::D + cc * EPC);
       pa[i] = *reinterpret_cast<const uint4*>(Ag + row * G::D + cc * EPC);
       if (!STATIC) pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
-      if (!STATIC) pd[i] = den[row];
+      if (REV && !STATIC) pd[i] = den[row];
     }
     const int64_t row = min(t0 + n, s1 - 1);
     tk_h = hv[row];
@@ -252,19 +261,29 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         const bool ok = t0 + r < s1;
         *reinterpret_cast<uint4*>(&S.AR[bb][r * FS + cc * EPC]) = pa[i];
         if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[bb][r * FS + cc * EPC]) = pb[i];
-        const T* xe8 = reinterpret_cast<const T*>(&px[i]);
-        const T* ue8 = reinterpret_cast<const T*>(&pu[i]);
-        const float sc = (REV && !STATIC) ? 1.f / pd[i] : 1.f;
+        // rows past the segment end are zero; only X = g = dO / den of the
+        // reverse walk is converted (bf16: hi + lo parts), the rest is copied
+        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 uv = ok ? pu[i] : zero4;
+        uint4 xv = ok ? px[i] : zero4, xlv = zero4;
+        if constexpr (REV && !STATIC) {
+          const T* xe8 = reinterpret_cast<const T*>(&px[i]);
+          const float sc = 1.f / pd[i];
+          T xh[EPC], xl[EPC];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            const float f = ok ? (float)xe8[e] * sc : 0.f;
+            xh[e] = (T)f;
+            xl[e] = (T)(f - (float)xh[e]);
+          }
+          xv = *reinterpret_cast<const uint4*>(xh);
+          xlv = *reinterpret_cast<const uint4*>(xl);
+        }
         // kmap frag order: column 16 q + 8 hh + e sits at 16 q + 8 (e / 4) + 4 hh + e % 4,
         // so a 16-byte chunk of bf16 goes out as two 8-byte halves
-        T xh[EPC], xl[EPC], uu[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float f = ok ? (float)xe8[e] * sc : 0.f;
-          xh[e] = (T)f;
-          xl[e] = (T)(f - (float)xh[e]);
-          uu[e] = ok ? ue8[e] : (T)0.f;
-        }
+        const T* uu = reinterpret_cast<const T*>(&uv);
+        const T* xh = reinterpret_cast<const T*>(&xv);
+        const T* xl = reinterpret_cast<const T*>(&xlv);
 #pragma unroll
         for (int g4 = 0; g4 < EPC / 4; ++g4) {
           const int col = cc * EPC + 4 * g4;
@@ -336,13 +355,26 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, evB, phB);
       T* pt = S.PhiBT[w];
+      if constexpr (C::TRB) {
+        // token row n: bucket rows 8 g + 4 h .. + 3 of each 32-row tile
 #pragma unroll
-      for (int at = 0; at < ATU; ++at)
+        for (int at = 0; at < ATU; ++at)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-          pt[lr * TSP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
-        }
+          for (int g = 0; g < 4; ++g) {
+            T4 v4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] = valid ? (T)phB[16 * at + 4 * g + j] : (T)0.f;
+            *reinterpret_cast<T4*>(pt + n * C::RS + 32 * at + 8 * g + 4 * h) = v4;
+          }
+      } else {
+#pragma unroll
+        for (int at = 0; at < ATU; ++at)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
+            pt[lr * TSP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
+          }
+      }
     }
     wave_lds_sync();
 
@@ -404,14 +436,18 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         E::split(m8, mh, ml);
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
-          const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
-          const T4 lo4 = *reinterpret_cast<const T4*>(r);
-          const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
           frag af;
+          if constexpr (C::TRB) {
+            af = load_kcol_tr(pt, C::RS, 16 * s, 32 * at, plain);
+          } else {
+            const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
+            const T4 lo4 = *reinterpret_cast<const T4*>(r);
+            const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            af[i] = lo4[i];
-            af[4 + i] = hi4[i];
+            for (int i = 0; i < 4; ++i) {
+              af[i] = lo4[i];
+              af[4 + i] = hi4[i];
+            }
           }
           E::mma(af, mh, dp[at]);
           if (E::NSPLIT == 2) E::mma(af, ml, dp[at]);
@@ -479,13 +515,17 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
-          const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
-          const T4 lo4 = *reinterpret_cast<const T4*>(r);
-          const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
+          if constexpr (C::TRB) {
+            pb[s][at] = load_kcol_tr(pt, C::RS, 16 * s, 32 * at, plain);
+          } else {
+            const T* r = pt + (32 * at + n) * TSP + 16 * s + 4 * h;
+            const T4 lo4 = *reinterpret_cast<const T4*>(r);
+            const T4 hi4 = *reinterpret_cast<const T4*>(r + 8);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pb[s][at][i] = lo4[i];
-            pb[s][at][4 + i] = hi4[i];
+            for (int i = 0; i < 4; ++i) {
+              pb[s][at][i] = lo4[i];
+              pb[s][at][4 + i] = hi4[i];
+            }
           }
         }
 #pragma unroll
@@ -519,13 +559,22 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           }
         }
       }
-      // mass: lane half h sums tokens 16 h .. 16 h + 15 of row 32 at + n
+      // mass: bf16, lane (n, h) sums the tokens of its bank-update operands
+      // (16 s + kmap(0, h, i)); float32: lane half h sums tokens 16 h .. 16 h
+      // + 15 of row 32 at + n
 #pragma unroll
       for (int at = 0; at < ATU; ++at) {
-        const T* r = pt + (32 * at + n) * TSP + 16 * h;
         float sm = 0.f;
+        if constexpr (C::TRB) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) sm += (float)r[t] * S.TK[bb][0][16 * h + t];
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm += (float)pb[s][at][i] * S.TK[bb][0][16 * s + kmap(0, h, i)];
+        } else {
+          const T* r = pt + (32 * at + n) * TSP + 16 * h;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) sm += (float)r[t] * S.TK[bb][0][16 * h + t];
+        }
         sm += xor32(sm);
         if (h == 0) S.Mw[w][32 * at + n] += sm;
       }
