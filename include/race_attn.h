@@ -35,7 +35,8 @@
  *    error nothing is enqueued and no output is written.
  *  - Supported: P in [1, 8]; L >= 1 with L * 2^max(P,3) <= 256;
  *    N >= 1; B*H >= 1; d a multiple of 8 up to 128, for the (dtype, P, L,
- *    causal) combinations with a compiled kernel set.  The kernels are
+ *    causal) combinations with a compiled kernel set (bf16 at d = 128: every
+ *    P in [1, 8] in both variants; dW is not compiled at P = 7).  The kernels are
  *    compiled for head dims D = 64 and 128; a smaller d runs on the next
  *    one up with its token rows padded by zero columns in the workspace
  *    (zero columns add nothing to a projection and give zero output

@@ -939,6 +939,7 @@ race_status race_attn_bwd(const void* Q, const void* K, const void* V, const flo
     return fail(RACE_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   if (dbeta && ((uintptr_t)dbeta & 3u)) return fail(RACE_ERR_INVALID_ARG, "dbeta must be 4-byte aligned");
   if (dW && ((uintptr_t)dW & 3u)) return fail(RACE_ERR_INVALID_ARG, "dW must be 4-byte aligned");
+  if (dW && !p.ks->dw_partial) return fail(RACE_ERR_UNSUPPORTED, "dW is not compiled for this (dtype, d, P, L)");
   const size_t dw_out = dW ? dw_out_floats(p) * sizeof(float) : 0;
   const size_t tbytes = (size_t)(p.BH * p.N * p.d) * elem_size(p.dtype);
   if (!p.causal) O = nullptr;   // the non-causal backward never reads O

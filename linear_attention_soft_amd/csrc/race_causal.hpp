@@ -68,10 +68,10 @@ struct TWArgs {
   int nseg;
 };
 
-// One wave per window of 32 bucket rows: whole tables when 2^PE <= 32, half
-// a table at 2^PE = 64 (SPL = 2 waves per table, which exchange their
-// softmax-backward sums once per chunk).  The workgroup walks one (segment,
-// batch x head).
+// One wave per window of 32 bucket rows: whole tables when 2^PE <= 32, else
+// a 32-corner part of a table (SPL = 2^PE / 32 = 2, 4 or 8 waves per table,
+// which exchange their softmax-backward sums once per chunk).  The workgroup
+// walks one (segment, batch x head).
 template <typename T, class G, bool REV, bool STATIC = false>
 struct TWCfg {
   // STATIC: the non-causal layer for wide banks: every token of the
@@ -80,7 +80,7 @@ struct TWCfg {
   static constexpr bool ST = STATIC;
   static constexpr int URP = 32;
   static constexpr int SPL = G::R > 32 ? G::R / 32 : 1;   // waves per table
-  static_assert(SPL <= 2 && G::PE + 1 <= 8, "tables of at most 64 corners");
+  static_assert(G::PE <= 8 && SPL <= G::LRP / URP, "a table spans at most the workgroup's waves");
   static constexpr int NM = G::LRP / URP;             // waves
   static constexpr int ATU = URP / 32;                // 32-row tiles per wave
   static constexpr int NT = 64 * NM;
@@ -124,7 +124,7 @@ struct TWLds {
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
-  alignas(16) float XS[C::SPL > 1 ? C::NM : 1][8][WC];   // half-table softmax-backward sums (SPL = 2)
+  alignas(16) float XS[C::SPL > 1 ? C::NM : 1][G::PE + 1][WC];   // split-table softmax-backward sums
 };
 
 // W^T frags of the dX contraction for column tile ct, built into registers
@@ -473,33 +473,41 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
         }
       } else {
-        // half table: exchange the sums with the other half (waves 2j, 2j + 1),
-        // add them in the same order in both, then dU_t = A_t - s E[v_t] with
-        // E[v_t] = tanh(beta u_t) from the soft assignment; each lane half
-        // takes the hyperplanes it evaluated there
-        constexpr bool LOWER = (TG & 1) == 0;
+        // split table: exchange the sums with the table's other waves (TG0 ..
+        // TG0 + SPL - 1), add them in the same order in every one of them,
+        // then dU_t = A_t - s E[v_t] with E[v_t] = tanh(beta u_t) from the
+        // soft assignment; each lane half takes the hyperplanes it evaluated
+        // there, and the table's first wave writes dPre
+        constexpr int TG0 = TG - TG % C::SPL;
+        constexpr bool FIRST = TG == TG0;
         constexpr int l = R0 / G::R;
         float part[1 + G::PE];
-        assign_partials_half<G, R0>(phA, dphi, part);
+        assign_partials_split<G, R0>(phA, dphi, part);
         if (h == 0) {
 #pragma unroll
           for (int i = 0; i <= G::PE; ++i) S.XS[w][i][n] = part[i];
         }
         __syncthreads();
-        const float s = S.XS[w & ~1][0][n] + S.XS[w | 1][0][n];
+        auto table_sum = [&](int i) {
+          float v = S.XS[TG0][i][n];
+#pragma unroll
+          for (int j = 1; j < C::SPL; ++j) v += S.XS[TG0 + j][i][n];
+          return v;
+        };
+        const float s = table_sum(0);
 #pragma unroll
         for (int t = 0; t < G::PE; t += 2) {
           const bool pair = t + 1 < G::PE;
           const int tt = pair ? t + h : t;
           float uu, s2;
           tanh_sech2((pair && h) ? preA[l * G::PE + t + 1] : preA[l * G::PE + t], uu, s2);
-          const float du = (S.XS[w & ~1][1 + tt][n] + S.XS[w | 1][1 + tt][n]) - s * evA[l * G::PE + t];
+          const float du = table_sum(1 + tt) - s * evA[l * G::PE + t];
           if (pair || h == 0) {
             bterm += uu * du;
-            if (LOWER) S.DP[bb][n * G::NHP + l * G::PE + tt] = a.beta * du * s2;
+            if (FIRST) S.DP[bb][n * G::NHP + l * G::PE + tt] = a.beta * du * s2;
           }
         }
-        if (LOWER && valid) bsum += bterm;
+        if (FIRST && valid) bsum += bterm;
       }
     }
     // rows of chunk k + 1: loaded here rather than at the top of the chunk

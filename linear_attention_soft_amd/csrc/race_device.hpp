@@ -626,22 +626,22 @@ __device__ __forceinline__ void assign_backward_rows(const float (&phi)[NROWS / 
   }
 }
 
-// Softmax-backward sums of one token over the 32 corners of a half table
-// (bucket rows [R0, R0 + 32), R0 a multiple of 32, 2^PE = 64): out[0] =
+// Softmax-backward sums of one token over the 32 corners of a table part
+// (bucket rows [R0, R0 + 32), R0 a multiple of 32, 2^PE >= 64): out[0] =
 // sum_r phi_r dphi_r and out[1 + t] = sum_r phi_r dphi_r v_{r,t}.  Both lane
-// halves end with the sums over all 32 corners.  The two halves of a table
-// give dU_t = A_t - s E[v_t] with s, A the sums over the whole table and
+// halves end with the sums over the 32 corners.  The parts of a table give
+// dU_t = A_t - s E[v_t] with s, A the sums over the whole table and
 // E[v_t] = sum_r phi_r v_{r,t} = tanh(beta u_t) (phi factorises over the
 // corner bits, each bit a two-way softmax).
 template <class G, int R0>
-__device__ __forceinline__ void assign_partials_half(const float (&phi)[16], const float (&dphi)[16],
-                                                     float (&out)[1 + G::PE]) {
-  static_assert(R0 % 32 == 0 && G::R == 64, "half tables of 64 corners");
+__device__ __forceinline__ void assign_partials_split(const float (&phi)[16], const float (&dphi)[16],
+                                                      float (&out)[1 + G::PE]) {
+  static_assert(R0 % 32 == 0 && G::R >= 64, "tables of at least 64 corners, 32 per part");
   const int h = lane_id() >> 5;
-  // register v holds corner r = R0 % 64 + 8 (v / 4) + 4 h + v % 4: bits 0, 1
+  // register v holds corner r = R0 % R + 8 (v / 4) + 4 h + v % 4: bits 0, 1
   // of r are bits 0, 1 of v, bits 3, 4 of r bits 2, 3 of v, bit 2 is h and
-  // bit 5 is fixed per half.  Signed sums over one bit at a time by a
-  // butterfly over the bits of v.
+  // bits 5 and up are fixed per part.  Signed sums over one bit at a time by
+  // a butterfly over the bits of v.
   float a[8], m0 = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {

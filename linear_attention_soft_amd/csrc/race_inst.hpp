@@ -101,7 +101,8 @@ struct Inst {
     k.reduce = reduce;
     k.softbucket_dbg = dbg;
     k.decode = decode;
-    k.dw_partial = dw_partial;
+    // the table-gradient partials read dPre rows as float4: NHP a multiple of 4
+    if constexpr (G::NHP % 4 == 0) k.dw_partial = dw_partial;
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
       k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;

@@ -37,7 +37,8 @@ struct KernelSet {
   void (*h_from_o)(const void* dO, const void* O, const float* den, float* h, int64_t total, hipStream_t);
   // recurrent decode step (grid: BH)
   void (*decode)(const DArgs&, unsigned grid, hipStream_t);
-  // table-gradient partials (grid: chunks x BH x 2 sides)
+  // table-gradient partials (grid: chunks x BH x 2 sides); null when the
+  // set's dPre rows (NHP slots) are not a multiple of 4 floats
   void (*dw_partial)(const DWArgs&, dim3 grid, hipStream_t);
 };
 
@@ -49,6 +50,7 @@ struct KernelSet {
   X(bf16_d128_p4)               \
   X(bf16_d128_p5)               \
   X(bf16_d128_p6)               \
+  X(bf16_d128_p78)              \
   X(f32_d64)                    \
   X(f32_d128)
 

@@ -1,6 +1,6 @@
 """GPU parity of the non-causal layer at 64 corners per table (P = 6, up to
-L = 4 tables: 256 bucket rows), and of both variants at 32 corners (P = 5),
-against the fp64 oracle.
+L = 4 tables: 256 bucket rows), and of both variants at 32, 128 and 256
+corners (P = 5, 7, 8), against the fp64 oracle.
 
 Tables this wide run the non-causal layer through the static-bank walks:
 every query reads the one bank of all keys (slides frame "Each bucket
@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import race_inputs as ri
+from oracle import race_oracle as orc
 from parity_util import TOL, check, oracle_bwd, oracle_fwd, say, to64
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +76,65 @@ def test_p5_parity(causal, N, L):
     check("dQ", dQ, rdQ, tol)
     check("dK", dK, rdK, tol)
     check("dV", dV, rdV, tol)
+
+
+@pytest.mark.parametrize("P,L,causal,N", [(7, 1, False, 3300), (7, 2, False, 2500), (7, 2, True, 2200),
+                                           (7, 1, True, 1700), (8, 1, False, 3000), (8, 1, True, 2100)])
+def test_p7_p8_parity(P, L, causal, N):
+    """Tables of 128 and 256 corners (P = 7, 8): a table spans 4 or 8 waves of
+    the transposed walks; non-causal on the static-bank walks.  dbeta too."""
+    w = replace(ri.WORKLOADS[5].with_size(N=N, B=1, H=2), causal=causal, P=P, L=L)
+    inp = ri.make_inputs(w, device="cpu", with_grad_out=True)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    say(f"P={P} L={L} causal={causal} N={N} beta={w.beta}")
+    O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal)
+    dQ, dK, dV = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal,
+                                    dev["dO"], state, O=O if causal else None)
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    check("O", O, oracle_fwd(inp, causal), tol, vmax=float(np.abs(to64(inp["V"])).max()))
+    rdQ, rdK, rdV = oracle_bwd(inp, causal)
+    check("dQ", dQ, rdQ, tol)
+    check("dK", dK, rdK, tol)
+    check("dV", dV, rdV, tol)
+
+
+@pytest.mark.parametrize("P,L,causal", [(8, 1, False), (8, 1, True), (7, 2, True)])
+def test_p7_p8_dbeta_dW(P, L, causal):
+    """dbeta (upstream gradient dO = O, so it is not a small remainder) and,
+    at P = 8, dW against the oracle; at P = 7 the dPre rows hold 14 slots and
+    dW is refused as unsupported."""
+    w = replace(ri.WORKLOADS[5].with_size(N=1500, B=1, H=2), causal=causal, P=P, L=L)
+    inp = ri.make_inputs(w, device="cpu", with_grad_out=False)
+    Q, K, V = (to64(inp[k]) for k in ("Q", "K", "V"))
+    Wn = inp["W"].double().numpy()
+    inp["dO"] = torch.from_numpy(orc.forward(Q, K, V, Wn, w.beta, causal)).to(inp["Q"].dtype)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    O, state = race.race_attn_fwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal)
+    *_, db = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal, dev["dO"],
+                                state, O=O if causal else None, dbeta=True)
+    torch.cuda.synchronize()
+    dO = to64(inp["dO"])
+    ref, scale = 0.0, 0.0
+    for h in range(2):
+        tq, tk = orc.dbeta_head(Q[0, h], K[0, h], V[0, h], Wn, w.beta, dO[0, h], causal)
+        ref += float(tq.sum() + tk.sum())
+        scale += float(np.abs(tq).sum() + np.abs(tk).sum())
+    err = abs(float(db[0]) - ref)
+    say(f"P={P} causal={causal} dbeta gpu {float(db[0]):.6e} ref {ref:.6e} |err|/|ref| {err / abs(ref):.3e} "
+        f"(|ref| / sum|terms| {abs(ref) / scale:.3f})")
+    assert abs(ref) >= 0.3 * scale
+    assert err <= TOL["bf16"] * abs(ref)
+    if P == 7:
+        with pytest.raises(race.RaceError) as e:
+            race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal, dev["dO"],
+                               state, O=O if causal else None, dW=True)
+        assert e.value.name == "RACE_ERR_UNSUPPORTED"
+        return
+    *_, dW = race.race_attn_bwd(dev["Q"], dev["K"], dev["V"], dev["W"], w.beta, w.P, w.L, causal, dev["dO"],
+                                state, O=O if causal else None, dW=True)
+    torch.cuda.synchronize()
+    check("dW", dW, orc.dW(to64(inp["Q"]), to64(inp["K"]), to64(inp["V"]), Wn, w.beta, dO, causal), TOL["bf16"])
 
 
 def test_wide_noncausal_stateless_and_deterministic():
