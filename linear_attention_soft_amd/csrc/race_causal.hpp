@@ -86,7 +86,13 @@ struct TWCfg {
   static constexpr int NT = 64 * NM;
   static constexpr bool XSPLIT = REV && !STATIC && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
   static constexpr int NXS = XSPLIT ? 2 : 1;
-  static constexpr int FS = G::D + 16 / (int)sizeof(T);   // staged row (elements)
+  // staged row (elements): with bf16 at d = 128, rows 76 dwords apart (12
+  // mod 64 banks) keep both the 16-byte row reads and the transposing loads
+  // of X free of bank conflicts; the reverse walk's hi + lo X rows leave no
+  // LDS for that padding and keep 68 (4 mod 64: two-way on the transposing
+  // loads).  d = 64 rows are 36 dwords apart, conflict-free for both.
+  static constexpr int FS = G::D + ((std::is_same<T, bf16>::value && G::D == 128 && !XSPLIT) ? 24
+                                                                                           : 16 / (int)sizeof(T));
   // Phi_B^T row (elements): an 88-byte stride keeps both its 2-byte transposed
   // writes (rows 4 apart fall 96 bytes apart) and its 8-byte operand reads (32
   // consecutive rows start on distinct 8-byte bank pairs) free of bank conflicts
@@ -98,7 +104,10 @@ struct TWCfg {
   // group of such a load reads fall on disjoint banks.  float32 keeps the
   // transposed copy (TSP-element rows per bucket row).
   static constexpr bool TRB = std::is_same<T, bf16>::value;
-  static constexpr int RS = URP + 16;
+  static constexpr int RS = URP + 4;   // 18 dwords: the 8-byte row writes of the 32 tokens are conflict-free too
+  // dPre row per token (floats): an odd number of 16-byte groups, so that 16
+  // lanes' 16-byte accesses of 16 tokens fall on distinct banks
+  static constexpr int DPS = 4 * ((cdiv(G::NHP, 4) | 1));
   static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
   static constexpr int EPC = 16 / (int)sizeof(T);
   static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
@@ -122,7 +131,7 @@ struct TWLds {
   alignas(16) T BR[2][SROWS];                    // state-role rows
   alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
-  alignas(16) float DP[2][WC * G::NHP];          // dPre of every table
+  alignas(16) float DP[2][WC * C::DPS];          // dPre of every table
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
   alignas(16) float XS[C::SPL > 1 ? C::NM : 1][G::PE + 1][WC];   // split-table softmax-backward sums
 };
@@ -307,7 +316,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     float dp[G::NHP];
 #pragma unroll
-    for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * G::NHP + i];
+    for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * C::DPS + i];
     if (a.dpre_out && w == 0 && t0 + n < s1)
       store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + t0 + n) * G::NHP, dp, h);
     frag bq[G::NQS];
@@ -470,7 +479,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         if (valid && h == 0) bsum += bterm;
         if (h == 0) {
 #pragma unroll
-          for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * G::NHP + hp] = dpre[hp];
+          for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * C::DPS + hp] = dpre[hp];
         }
       } else {
         // split table: exchange the sums with the table's other waves (TG0 ..
@@ -504,7 +513,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           const float du = table_sum(1 + tt) - s * evA[l * G::PE + t];
           if (pair || h == 0) {
             bterm += uu * du;
-            if (FIRST) S.DP[bb][n * G::NHP + l * G::PE + tt] = a.beta * du * s2;
+            if (FIRST) S.DP[bb][n * C::DPS + l * G::PE + tt] = a.beta * du * s2;
           }
         }
         if (FIRST && valid) bsum += bterm;
