@@ -398,9 +398,19 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       const T* uf = S.UF[bb] + n * FS + 8 * h;
       const T* xf = S.XF[bb][0] + n * FS + 8 * h;
       const T* xl = S.XF[bb][C::NXS - 1] + n * FS + 8 * h;
+      // operands of step q + 1 are loaded before the MFMAs of step q
+      frag ubq[2], xfq[2], xlq[2];
+      auto ldq = [&](int q) {
+        const int sl = q & 1;
+        ubq[sl] = *reinterpret_cast<const frag*>(uf + 16 * q);
+        xfq[sl] = STATIC ? E::zero() : *reinterpret_cast<const frag*>(xf + 16 * q);
+        xlq[sl] = C::XSPLIT ? *reinterpret_cast<const frag*>(xl + 16 * q) : E::zero();
+      };
+      ldq(0);
 #pragma unroll
       for (int q = 0; q < G::KD; ++q) {
-        const frag ub = *reinterpret_cast<const frag*>(uf + 16 * q);
+        const frag ub = ubq[q & 1], xfv = xfq[q & 1], xlv = xlq[q & 1];
+        if (q + 1 < G::KD) ldq(q + 1);
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
           float v8[8];
@@ -415,17 +425,25 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
             E::mma(E::pack(v8), ub, dp[at]);
           }
         }
-        if (!STATIC) E::mma(*reinterpret_cast<const frag*>(xf + 16 * q), ub, mf);
-        if (C::XSPLIT) E::mma(*reinterpret_cast<const frag*>(xl + 16 * q), ub, mf);
+        if (!STATIC) E::mma(xfv, ub, mf);
+        if (C::XSPLIT) E::mma(xlv, ub, mf);
       }
     }
     const float ue = S.TK[bb][1][n];
     if constexpr (!STATIC) {
+      // xe of the lane's 16 score rows (four runs of 4 consecutive tokens),
+      // read whether masked or not: a load under the mask compiles to a
+      // branch and a wait per element
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tb = 8 * (v >> 2) + 4 * h + (v & 3);
-        const bool keep = REV ? (tb >= n) : (tb <= n);
-        mf[v] = keep ? mf[v] + S.TK[bb][0][tb] * ue : 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 xe4 = *reinterpret_cast<const f32x4*>(&S.TK[bb][0][8 * g + 4 * h]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * g + j, tb = 8 * g + 4 * h + j;
+          const bool keep = REV ? (tb >= n) : (tb <= n);
+          const float m = mf[v] + xe4[j] * ue;
+          mf[v] = keep ? m : 0.f;
+        }
       }
     }
     // mass term and intra part: dp[lr][a] += m[lr] ue_a + sum_b phi_B,b[lr] mf[b][a]
@@ -545,19 +563,27 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
             }
           }
         }
+      if constexpr (std::is_same<T, bf16>::value) {
+        // X^T operands straight from the staged rows through transposing LDS
+        // loads, issued PF steps ahead of their MFMAs; step j: part j / (2 CT),
+        // column tile (j / 2) % CT, token half j % 2
+        constexpr int NSTEP = C::NXS * G::CT * 2, PF = 4;
+        auto ldx = [&](int j) {
+          return load_kcol_tr(S.XF[bb][j / (2 * G::CT)], FS, 16 * (j & 1), 32 * ((j >> 1) % G::CT), kmap_run_pos);
+        };
+        frag xq[PF];
 #pragma unroll
-      for (int sp = 0; sp < C::NXS; ++sp) {
-        if constexpr (std::is_same<T, bf16>::value) {
-          // X^T operands straight from the staged rows: transposing LDS loads
+        for (int j = 0; j < PF; ++j) xq[j] = ldx(j);
 #pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct)
+        for (int j = 0; j < NSTEP; ++j) {
+          const frag xa = xq[j % PF];
+          if (j + PF < NSTEP) xq[j % PF] = ldx(j + PF);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const frag xa = load_kcol_tr(S.XF[bb][sp], FS, 16 * s, 32 * ct, kmap_run_pos);
+          for (int at = 0; at < ATU; ++at) E::mma(xa, pb[j & 1][at], acc[at][(j >> 1) % G::CT]);
+        }
+      } else {
 #pragma unroll
-              for (int at = 0; at < ATU; ++at) E::mma(xa, pb[s][at], acc[at][ct]);
-            }
-        } else {
+        for (int sp = 0; sp < C::NXS; ++sp) {
           const T* xf = S.XF[bb][sp] + n * FS + 8 * h;
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) {
