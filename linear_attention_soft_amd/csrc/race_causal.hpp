@@ -108,6 +108,15 @@ struct TWCfg {
   // dPre row per token (floats): an odd number of 16-byte groups, so that 16
   // lanes' 16-byte accesses of 16 tokens fall on distinct banks
   static constexpr int DPS = 4 * ((cdiv(G::NHP, 4) | 1));
+  // bf16: the waves that form dPre write the B operands of dX = dPre . W
+  // directly, as one bf16 row per token whose entry e is the hi part of
+  // dPre[e % NHP] (e < NHP or e >= 2 NHP) or its lo part (NHP <= e < 2 NHP),
+  // matching the W^T entries (W hi, W hi, W lo); each K16 step of the dX MFMA
+  // is then one 16-byte read.  Rows 4 (2 NQS + 1) dwords apart: the 16-byte
+  // reads of 16 lanes fall on distinct banks.  Used where the stages still fit
+  // the 160 KB of LDS with these rows (TWLds::DXB); otherwise float32 dPre
+  // rows are kept and every dX wave builds the operands.
+  static constexpr int DBS = 16 * G::NQS + 8;
   static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
   static constexpr int EPC = 16 / (int)sizeof(T);
   static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
@@ -119,9 +128,10 @@ struct TWCfg {
   static_assert(G::LRP % URP == 0, "windows of 32 rows");
 };
 
-template <typename T, class G, bool REV, bool STATIC = false>
-struct TWLds {
+template <typename T, class G, bool REV, bool STATIC, bool DXB_>
+struct TWLdsT {
   using C = TWCfg<T, G, REV, STATIC>;
+  static constexpr bool DXB = DXB_;
   static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
   typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
@@ -131,10 +141,16 @@ struct TWLds {
   alignas(16) T BR[2][SROWS];                    // state-role rows
   alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
-  alignas(16) float DP[2][WC * C::DPS];          // dPre of every table
+  alignas(16) float DP[2][DXB ? 4 : WC * C::DPS];    // dPre of every table (float32 rows)
+  alignas(16) T DB[2][DXB ? WC * C::DBS : 8];        // dX B-operand rows (bf16 I/O)
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
   alignas(16) float XS[C::SPL > 1 ? C::NM : 1][G::PE + 1][WC];   // split-table softmax-backward sums
 };
+
+constexpr size_t kLdsBytes = 160 * 1024;
+template <typename T, class G, bool REV, bool STATIC = false>
+using TWLds = TWLdsT<T, G, REV, STATIC,
+                     std::is_same<T, bf16>::value && sizeof(TWLdsT<T, G, REV, STATIC, true>) <= kLdsBytes>;
 
 // W^T frags of the dX contraction for column tile ct, built into registers
 // (same entries as build_wt_frags).
@@ -184,6 +200,7 @@ __device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int ld
 template <typename T, class G, bool REV, int TG, bool STATIC = false>
 __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC>& S) {
   using C = TWCfg<T, G, REV, STATIC>;
+  using SL = TWLds<T, G, REV, STATIC>;
   using E = Eng<T>;
   using frag = typename E::frag;
   constexpr int R0 = TG * C::URP;
@@ -277,7 +294,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         uint4 xv = ok ? px[i] : zero4, xlv = zero4;
         if constexpr (REV && !STATIC) {
           const T* xe8 = reinterpret_cast<const T*>(&px[i]);
-          const float sc = 1.f / pd[i];
+          const float sc = rcp(pd[i]);
           T xh[EPC], xl[EPC];
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
@@ -311,17 +328,37 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       S.TK[bb][2][tid] = ok ? 1.f / tk_d : 0.f;                 // 1 / den
     }
   };
-  // ---- dX = dPre . W for chunk k (from DP[bb]), this wave's column tiles
+  // ---- dPre of slot hp of this lane's token (chunk starting at t0) into buffer bb
+  auto put_dpre = [&](int bb, int64_t t0, int hp, float x) {
+    if constexpr (SL::DXB) {
+      T* r = S.DB[bb] + n * C::DBS;
+      const T xh = (T)x;
+      const T xl = (T)(x - (float)xh);
+      r[hp] = xh;
+      r[G::NHP + hp] = xl;
+      r[2 * G::NHP + hp] = xh;
+      if (a.dpre_out && t0 + n < s1) a.dpre_out[((size_t)bh * a.N + t0 + n) * G::NHP + hp] = x;
+    } else {
+      S.DP[bb][n * C::DPS + hp] = x;
+    }
+  };
+  // ---- dX = dPre . W for chunk k (from DP[bb] / DB[bb]), this wave's column tiles
   auto dx_out = [&](int64_t k, int bb) {
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
-    float dp[G::NHP];
-#pragma unroll
-    for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * C::DPS + i];
-    if (a.dpre_out && w == 0 && t0 + n < s1)
-      store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + t0 + n) * G::NHP, dp, h);
     frag bq[G::NQS];
+    if constexpr (SL::DXB) {
+      const T* r = S.DB[bb] + n * C::DBS + 8 * h;
 #pragma unroll
-    for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dp, qs);
+      for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = *reinterpret_cast<const frag*>(r + 16 * qs);
+    } else {
+      float dp[G::NHP];
+#pragma unroll
+      for (int i = 0; i < G::NHP; ++i) dp[i] = S.DP[bb][n * C::DPS + i];
+      if (a.dpre_out && w == 0 && t0 + n < s1)
+        store_dpre_half<G>(a.dpre_out + ((size_t)bh * a.N + t0 + n) * G::NHP, dp, h);
+#pragma unroll
+      for (int qs = 0; qs < G::NQS; ++qs) bq[qs] = dpre_frag<T, G>(dp, qs);
+    }
 #pragma unroll
     for (int j = 0; j < C::NCTW; ++j) {
       const int ct = w + C::NM * j;
@@ -336,6 +373,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
 
   if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
   else build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
+  if constexpr (SL::DXB) {
+    // entries past 3 NHP are never written: zero (W^T is zero there too)
+    for (int i = tid; i < 2 * WC * C::DBS; i += C::NT) (&S.DB[0][0])[i] = (T)0.f;
+  }
   load_stage(0);
   stage(0, 0);
   __syncthreads();
@@ -372,8 +413,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           for (int g = 0; g < 4; ++g) {
             T4 v4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v4[j] = valid ? (T)phB[16 * at + 4 * g + j] : (T)0.f;
-            *reinterpret_cast<T4*>(pt + n * C::RS + 32 * at + 8 * g + 4 * h) = v4;
+            for (int j = 0; j < 4; ++j) v4[j] = (T)phB[16 * at + 4 * g + j];
+            // tokens past the segment end: zero rows (one select per 8 bytes)
+            const uint64_t u = valid ? __builtin_bit_cast(uint64_t, v4) : 0ull;
+            *reinterpret_cast<uint64_t*>(pt + n * C::RS + 32 * at + 8 * g + 4 * h) = u;
           }
       } else {
 #pragma unroll
@@ -497,7 +540,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         if (valid && h == 0) bsum += bterm;
         if (h == 0) {
 #pragma unroll
-          for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) S.DP[bb][n * C::DPS + hp] = dpre[hp];
+          for (int hp = WT::L0 * G::PE; hp < WT::L1 * G::PE; ++hp) put_dpre(bb, t0, hp, dpre[hp]);
         }
       } else {
         // split table: exchange the sums with the table's other waves (TG0 ..
@@ -531,7 +574,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           const float du = table_sum(1 + tt) - s * evA[l * G::PE + t];
           if (pair || h == 0) {
             bterm += uu * du;
-            if (FIRST) S.DP[bb][n * C::DPS + l * G::PE + tt] = a.beta * du * s2;
+            if (FIRST) put_dpre(bb, t0, l * G::PE + tt, a.beta * du * s2);
           }
         }
         if (FIRST && valid) bsum += bterm;

@@ -508,7 +508,9 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
         ev[l * G::PE + t] = sp[t] - sm[t];
       }
     }
-    const float f2 = h ? sp[2] : sm[2];
+    // tables >= L get zero rows: the factor of bit 2 carries the liveness
+    // (sigmoids are finite, so the products are exactly 0)
+    const float f2 = (l < L) ? (h ? sp[2] : sm[2]) : 0.f;
     float g[4];
     g[0] = sm[0] * sm[1] * f2;
     g[1] = sp[0] * sm[1] * f2;
@@ -526,7 +528,6 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
         hi[x] = hi[x] * sm[t];
       }
     }
-    const bool live = l < L;
 #pragma unroll
     for (int a = 0; a < NROWS / 32; ++a) {
 #pragma unroll
@@ -534,7 +535,7 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
         const int lr0 = R0 + 32 * a + 8 * (v >> 2) + (v & 3);
         if (lr0 / G::R == l) {
           const int r0 = lr0 % G::R;
-          phi[16 * a + v] = live ? g[r0 & 3] * hi[r0 >> 3] : 0.f;
+          phi[16 * a + v] = g[r0 & 3] * hi[r0 >> 3];
         }
       }
     }
