@@ -117,6 +117,14 @@ struct TWCfg {
   // the 160 KB of LDS with these rows (TWLds::DXB); otherwise float32 dPre
   // rows are kept and every dX wave builds the operands.
   static constexpr int DBS = 16 * G::NQS + 8;
+  // Shared intra-chunk scores (TWLds::SHSC, with at least four waves and where
+  // the LDS still fits): mf[b][a] (b: state-role token, a: output-role
+  // token) is computed once per chunk as four 16 x 16 sub-tiles by four waves
+  // and read by every wave as the B operand of its intra term, instead of
+  // every wave forming the whole 32 x 32 tile.  One row per output token a
+  // with entry b at the kmap frag position of b (bits 2 and 3 of b
+  // exchanged); bf16 keeps hi and lo parts.  Rows 4 x odd dwords apart.
+  static constexpr int MS = std::is_same<T, bf16>::value ? 40 : 36;
   static constexpr int NCTW = cdiv(G::CT, NM);        // dX column tiles per wave
   static constexpr int EPC = 16 / (int)sizeof(T);
   static constexpr int CPR = G::D / EPC;              // 16-byte chunks per value row
@@ -128,10 +136,14 @@ struct TWCfg {
   static_assert(G::LRP % URP == 0, "windows of 32 rows");
 };
 
-template <typename T, class G, bool REV, bool STATIC, bool DXB_>
+template <typename T, class G, bool REV, bool STATIC, bool DXB_, bool SHSC_>
 struct TWLdsT {
   using C = TWCfg<T, G, REV, STATIC>;
-  static constexpr bool DXB = DXB_;
+  static constexpr bool DXB = DXB_, SHSC = SHSC_;
+  // one buffer of dPre rows when a workgroup barrier separates the previous
+  // chunk's dX reads (at the top of a chunk) from this chunk's dPre writes
+  // (the shared-score barrier or the split-table exchange), two otherwise
+  static constexpr int NDB = (SHSC || C::SPL > 1) ? 1 : 2;
   static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
   typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
@@ -141,16 +153,27 @@ struct TWLdsT {
   alignas(16) T BR[2][SROWS];                    // state-role rows
   alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
-  alignas(16) float DP[2][DXB ? 4 : WC * C::DPS];    // dPre of every table (float32 rows)
-  alignas(16) T DB[2][DXB ? WC * C::DBS : 8];        // dX B-operand rows (bf16 I/O)
+  alignas(16) float DP[NDB][DXB ? 4 : WC * C::DPS];    // dPre of every table (float32 rows)
+  alignas(16) T DB[NDB][DXB ? WC * C::DBS : 8];        // dX B-operand rows (bf16 I/O)
+  alignas(16) T MFT[SHSC ? Eng<T>::NSPLIT : 1][SHSC ? WC * C::MS : 8];   // shared intra-chunk scores
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
   alignas(16) float XS[C::SPL > 1 ? C::NM : 1][G::PE + 1][WC];   // split-table softmax-backward sums
 };
 
+// Stage layout: shared scores first, then bf16 dX rows, as far as 160 KB allow.
 constexpr size_t kLdsBytes = 160 * 1024;
+template <typename T, class G, bool REV, bool STATIC>
+struct TWPick {
+  static constexpr bool BF = std::is_same<T, bf16>::value;
+  static constexpr bool FIT_TT = sizeof(TWLdsT<T, G, REV, STATIC, true, true>) <= kLdsBytes;
+  static constexpr bool FIT_FT = sizeof(TWLdsT<T, G, REV, STATIC, false, true>) <= kLdsBytes;
+  static constexpr bool FIT_TF = sizeof(TWLdsT<T, G, REV, STATIC, true, false>) <= kLdsBytes;
+  static constexpr bool SH = !STATIC && TWCfg<T, G, REV, STATIC>::NM >= 4 && ((BF && FIT_TT) || FIT_FT);
+  static constexpr bool DX = BF && (SH ? FIT_TT : FIT_TF);
+  using type = TWLdsT<T, G, REV, STATIC, DX, SH>;
+};
 template <typename T, class G, bool REV, bool STATIC = false>
-using TWLds = TWLdsT<T, G, REV, STATIC,
-                     std::is_same<T, bf16>::value && sizeof(TWLdsT<T, G, REV, STATIC, true>) <= kLdsBytes>;
+using TWLds = typename TWPick<T, G, REV, STATIC>::type;
 
 // W^T frags of the dX contraction for column tile ct, built into registers
 // (same entries as build_wt_frags).
@@ -330,6 +353,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
   };
   // ---- dPre of slot hp of this lane's token (chunk starting at t0) into buffer bb
   auto put_dpre = [&](int bb, int64_t t0, int hp, float x) {
+    bb = SL::NDB == 2 ? bb : 0;
     if constexpr (SL::DXB) {
       T* r = S.DB[bb] + n * C::DBS;
       const T xh = (T)x;
@@ -344,6 +368,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
   };
   // ---- dX = dPre . W for chunk k (from DP[bb] / DB[bb]), this wave's column tiles
   auto dx_out = [&](int64_t k, int bb) {
+    bb = SL::NDB == 2 ? bb : 0;
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     frag bq[G::NQS];
     if constexpr (SL::DXB) {
@@ -371,11 +396,56 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     }
   };
 
+  // ---- intra-chunk scores of the chunk staged in buffer bb: sub-tile i =
+  // (b rows 16 (i / 2) .., a columns 16 (i % 2) ..) by wave NM - 1 - i (mod
+  // NM): mf[b][a] = X_b . U_a + xe_b ue_a, masked (b <= a forward, b >= a
+  // reverse), on the 16 x 16 MFMA
+  auto score_tiles = [&](int bb) {
+    if constexpr (SL::SHSC) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (((C::NM - 1 - i) % C::NM + C::NM) % C::NM != TG) continue;
+      const int bt = i >> 1, at2 = i & 1;
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      const T* xr = S.XF[bb][0] + (16 * bt + l16) * FS + 8 * g4;
+      const T* xl = S.XF[bb][C::NXS - 1] + (16 * bt + l16) * FS + 8 * g4;
+      const T* ur = S.UF[bb] + (16 * at2 + l16) * FS + 8 * g4;
+#pragma unroll
+      for (int st = 0; st < G::D / 32; ++st) {
+        const frag ub = *reinterpret_cast<const frag*>(ur + 32 * st);
+        E::mma16(*reinterpret_cast<const frag*>(xr + 32 * st), ub, c);
+        if (C::XSPLIT) E::mma16(*reinterpret_cast<const frag*>(xl + 32 * st), ub, c);
+      }
+      // lane (l16, g4) holds b = 16 bt + 4 g4 + r, a = 16 at2 + l16
+      const int ta = 16 * at2 + l16, b0 = 16 * bt + 4 * g4;
+      const float ue = S.TK[bb][1][ta];
+      const f32x4 xe4 = *reinterpret_cast<const f32x4*>(&S.TK[bb][0][b0]);
+      float m4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = REV ? (b0 + r >= ta) : (b0 + r <= ta);
+        const float m = c[r] + xe4[r] * ue;
+        m4[r] = keep ? m : 0.f;
+      }
+      const int pos = (b0 & ~15) + 8 * ((b0 >> 2) & 1) + 4 * ((b0 >> 3) & 1);
+      typename E::vec4 hv, lv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hv[r] = (T)m4[r];
+        lv[r] = (T)(m4[r] - (float)hv[r]);
+      }
+      *reinterpret_cast<typename E::vec4*>(S.MFT[0] + ta * C::MS + pos) = hv;
+      if (E::NSPLIT == 2) *reinterpret_cast<typename E::vec4*>(S.MFT[E::NSPLIT - 1] + ta * C::MS + pos) = lv;
+    }
+    }
+  };
+
   if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
   else build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
   if constexpr (SL::DXB) {
     // entries past 3 NHP are never written: zero (W^T is zero there too)
-    for (int i = tid; i < 2 * WC * C::DBS; i += C::NT) (&S.DB[0][0])[i] = (T)0.f;
+    for (int i = tid; i < SL::NDB * WC * C::DBS; i += C::NT) (&S.DB[0][0])[i] = (T)0.f;
   }
   load_stage(0);
   stage(0, 0);
@@ -386,6 +456,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     const int bb = (int)(k & 1);
     const int64_t t0 = chunk_t0<REV>(s0, nch, k);
     const bool valid = t0 + n < s1;
+    // dX of chunk k - 1 (its dPre rows are complete since the last barrier),
+    // then this wave's share of the chunk's intra scores
+    if (k > 0) dx_out(k - 1, bb ^ 1);
+    if constexpr (SL::SHSC) score_tiles(bb);
     // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
     float preA[G::NHP], evA[G::NHP], phA[URP / 2];
     {
@@ -436,6 +510,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     f32x16 dp[ATU];
 #pragma unroll
     for (int at = 0; at < ATU; ++at) dp[at] = zero16();
+    // per-wave intra scores (without shared scores): mf[b][a] = X_b . U_a
+    constexpr bool OWN = !STATIC && !SL::SHSC;
     f32x16 mf = zero16();
     {
       const T* uf = S.UF[bb] + n * FS + 8 * h;
@@ -446,8 +522,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       auto ldq = [&](int q) {
         const int sl = q & 1;
         ubq[sl] = *reinterpret_cast<const frag*>(uf + 16 * q);
-        xfq[sl] = STATIC ? E::zero() : *reinterpret_cast<const frag*>(xf + 16 * q);
-        xlq[sl] = C::XSPLIT ? *reinterpret_cast<const frag*>(xl + 16 * q) : E::zero();
+        xfq[sl] = OWN ? *reinterpret_cast<const frag*>(xf + 16 * q) : E::zero();
+        xlq[sl] = (OWN && C::XSPLIT) ? *reinterpret_cast<const frag*>(xl + 16 * q) : E::zero();
       };
       ldq(0);
 #pragma unroll
@@ -468,12 +544,12 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
             E::mma(E::pack(v8), ub, dp[at]);
           }
         }
-        if (!STATIC) E::mma(xfv, ub, mf);
-        if (C::XSPLIT) E::mma(xlv, ub, mf);
+        if (OWN) E::mma(xfv, ub, mf);
+        if (OWN && C::XSPLIT) E::mma(xlv, ub, mf);
       }
     }
     const float ue = S.TK[bb][1][n];
-    if constexpr (!STATIC) {
+    if constexpr (OWN) {
       // xe of the lane's 16 score rows (four runs of 4 consecutive tokens),
       // read whether masked or not: a load under the mask compiles to a
       // branch and a wait per element
@@ -489,6 +565,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         }
       }
     }
+    // the chunk's shared intra scores are complete
+    if constexpr (SL::SHSC) __syncthreads();
     // mass term and intra part: dp[lr][a] += m[lr] ue_a + sum_b phi_B,b[lr] mf[b][a]
     {
       const T* pt = S.PhiBT[w];
@@ -499,11 +577,17 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       }
 #pragma unroll
       for (int s = 0; s < (STATIC ? 0 : 2); ++s) {
-        float m8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m8[i] = mf[8 * s + i];
         frag mh, ml;
-        E::split(m8, mh, ml);
+        if constexpr (SL::SHSC) {
+          const T* mr = S.MFT[0] + n * C::MS + 16 * s + 8 * h;
+          mh = *reinterpret_cast<const frag*>(mr);
+          ml = *reinterpret_cast<const frag*>(S.MFT[E::NSPLIT - 1] + n * C::MS + 16 * s + 8 * h);
+        } else {
+          float m8[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m8[i] = mf[8 * s + i];
+          E::split(m8, mh, ml);
+        }
 #pragma unroll
         for (int at = 0; at < ATU; ++at) {
           frag af;
@@ -665,9 +749,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         if (h == 0) S.Mw[w][32 * at + n] += sm;
       }
     }
-    // staging of chunk k + 1, dX of chunk k - 1
+    // staging of chunk k + 1
     if (k + 1 < nch) stage(k + 1, bb ^ 1);
-    if (k > 0) dx_out(k - 1, bb ^ 1);
     __syncthreads();
   }
   dx_out(nch - 1, (int)((nch - 1) & 1));
