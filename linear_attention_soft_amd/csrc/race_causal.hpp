@@ -157,6 +157,7 @@ struct TWLdsT {
   alignas(16) T DB[NDB][DXB ? WC * C::DBS : 8];        // dX B-operand rows (bf16 I/O)
   alignas(16) T MFT[SHSC ? Eng<T>::NSPLIT : 1][SHSC ? WC * C::MS : 8];   // shared intra-chunk scores
   alignas(16) float TK[2][3][WC];                // per token: xe (X extra), ue (U extra), 1/den
+  alignas(16) T XEB[2][2][C::TRB ? WC : 4];      // bf16: xe as hi + lo (mass sums on v_dot2)
   alignas(16) float XS[C::SPL > 1 ? C::NM : 1][G::PE + 1][WC];   // split-table softmax-backward sums
 };
 
@@ -349,6 +350,12 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       S.TK[bb][0][tid] = ok ? (REV ? tk_h : 1.f) : 0.f;        // xe
       S.TK[bb][1][tid] = ok ? (REV ? 1.f : tk_h * tk_d) : 0.f; // ue
       S.TK[bb][2][tid] = ok ? 1.f / tk_d : 0.f;                 // 1 / den
+      if constexpr (C::TRB) {
+        const float xe = ok ? (REV ? tk_h : 1.f) : 0.f;
+        const T xh = (T)xe;
+        S.XEB[bb][0][tid] = xh;
+        S.XEB[bb][1][tid] = (T)(xe - (float)xh);
+      }
     }
   };
   // ---- dPre of slot hp of this lane's token (chunk starting at t0) into buffer bb
@@ -736,10 +743,12 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       for (int at = 0; at < ATU; ++at) {
         float sm = 0.f;
         if constexpr (C::TRB) {
+          // xe as hi + lo (forward walk: 0 or 1, exact in bf16, no lo part)
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sm += (float)pb[s][at][i] * S.TK[bb][0][16 * s + kmap(0, h, i)];
+          for (int s = 0; s < 2; ++s) {
+            sm = dot8_bf16(pb[s][at], load_kmap8(S.XEB[bb][0], 16 * s, h), sm);
+            if (REV) sm = dot8_bf16(pb[s][at], load_kmap8(S.XEB[bb][1], 16 * s, h), sm);
+          }
         } else {
           const T* r = pt + (32 * at + n) * TSP + 16 * h;
 #pragma unroll

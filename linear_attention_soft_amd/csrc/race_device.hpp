@@ -27,6 +27,7 @@ namespace race {
 using bf16 = __bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -159,6 +160,24 @@ __device__ __forceinline__ void sigmoid_pair(float z, float& sp, float& sm) {
   bool pos = z >= 0.f;
   sp = pos ? p : q;
   sm = pos ? q : p;
+}
+
+// c + sum_i a[i] b[i] over 8 bf16 pairs, two products per v_dot2_f32_bf16
+// (bf16 products are exact in float32)
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), c, false);
+  return c;
+}
+
+// Eight bf16 values of a row kept in natural order at positions kmap(q, h, i)
+// (two runs of four: q16 + 4 h and q16 + 8 + 4 h), as one operand.
+__device__ __forceinline__ bf16x8 load_kmap8(const bf16* row, int q16, int h) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + q16 + 4 * h);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + q16 + 8 + 4 * h);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // The two 32-lane halves of a wave exchanged in one VALU instruction

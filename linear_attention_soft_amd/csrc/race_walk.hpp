@@ -93,6 +93,9 @@ struct RWCfg {
   static constexpr bool MASS = (BM == W_SEGSUM || BM == W_GSUM || BM == W_FWD) && !STATIC;   // mass updates
   static constexpr bool MBUF = MASS || (STATIC && BM != W_DV);   // a bucket mass is kept in LDS
   static constexpr bool DEN = BM == W_FWD || (STATIC && BM == W_H);   // feature waves form Phi_A mass
+  // bf16: the mass is also kept as bf16 hi + lo rows (after the float32 rows
+  // of mbuf), so that Phi_A . mass runs on v_dot2
+  static constexpr bool DENB = DEN && std::is_same<T, bf16>::value;
   // GSUM, DV: the state role's features are divided by its token's den, so
   // that with X = dO the bank sums phi_Q g^T (and, GSUM, with mass weights
   // h den, phi_Q h)
@@ -115,6 +118,19 @@ struct RWCfg {
   // BANK_LO the rounding residual is contracted as well.
   static constexpr bool BANK_LO = false;
 };
+
+// Bucket mass of row `row` into buffer `buf` of mbuf (float32 rows [2][LRP],
+// then with BF the bf16 hi and lo rows [2][2][LRP]).
+template <typename T, class G, bool BF>
+__device__ __forceinline__ void put_mass(float* mbuf, int buf, int row, float v) {
+  mbuf[buf * G::LRP + row] = v;
+  if constexpr (BF) {
+    T* mb = reinterpret_cast<T*>(mbuf + 2 * G::LRP) + (2 * buf) * G::LRP + row;
+    const T vh = (T)v;
+    mb[0] = vh;
+    mb[G::LRP] = (T)(v - (float)vh);
+  }
+}
 
 // First token of the k-th chunk in walk order.
 template <bool REV>
@@ -144,6 +160,7 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
   const int64_t tok = t0 + n;
   const bool valid = tok < s1;
+  T* hwb = reinterpret_cast<T*>(hw + C::NF * WC);
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
   project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
   soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi);
@@ -165,12 +182,22 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
     if (C::DEN) {
       // den (inter part) over this window: rounded phi_A . mass before the
       // chunk (static modes: the fixed mass, kept in buffer 1)
-      const float* m = mbuf + (C::STATIC ? 1 : (b ^ 1)) * G::LRP + R0;
+      const int mb = C::STATIC ? 1 : (b ^ 1);
       float d = 0.f;
+      if constexpr (C::DENB) {
+        const T* mh = reinterpret_cast<const T*>(mbuf + 2 * G::LRP) + (2 * mb) * G::LRP + R0;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
+        for (int q = 0; q < NQ; ++q) {
+          d = dot8_bf16(fq[q], load_kmap8(mh, 16 * q, h), d);
+          d = dot8_bf16(fq[q], load_kmap8(mh + G::LRP, 16 * q, h), d);
+        }
+      } else {
+        const float* m = mbuf + mb * G::LRP + R0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d += (float)fq[q][i] * m[kmap(q, h, i)];
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d += (float)fq[q][i] * m[kmap(q, h, i)];
+      }
       d += xor32(d);
       if (h == 0) dpart[(b * C::NWIN + win) * WC + n] = d;
     }
@@ -190,7 +217,16 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
       for (int i = 0; i < 8; ++i) bt[(R0 + kmap(q, h, i)) * C::TS + n] = fq[q][i];
   }
   if (C::MASS) {
-    if (C::BM == W_GSUM && h == 0) hw[fw * WC + n] = valid ? hv * dv : 0.f;
+    if (C::BM == W_GSUM && h == 0) {
+      const float wv = valid ? hv * dv : 0.f;
+      hw[fw * WC + n] = wv;
+      if constexpr (C::TRLOAD) {
+        // the weights as bf16 hi + lo for the mass sums on v_dot2
+        const T wh = (T)wv;
+        hwb[(2 * fw) * WC + n] = wh;
+        hwb[(2 * fw + 1) * WC + n] = (T)(wv - (float)wh);
+      }
+    }
     wave_lds_sync();
     // mass after the chunk = mass before + column sums of the rounded phi_B
     // (GSUM: weighted by h)
@@ -204,13 +240,16 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
 #pragma unroll
         for (int sidx = 0; sidx < 2; ++sidx) {
           const frag v = load_kcol_tr(rows, C::FR, 16 * sidx, R0 + 32 * at, kmap_run_pos);
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            sm += (C::BM == W_GSUM) ? (float)v[i] * hw[fw * WC + 16 * sidx + kmap(0, h, i)] : (float)v[i];
+          if constexpr (C::BM == W_GSUM) {
+            sm = dot8_bf16(v, load_kmap8(hwb + (2 * fw) * WC, 16 * sidx, h), sm);
+            sm = dot8_bf16(v, load_kmap8(hwb + (2 * fw + 1) * WC, 16 * sidx, h), sm);
+          } else {
+            sm = dot8_bf16(v, E::ones(), sm);
+          }
         }
         sm += xor32(sm);
         const int row = R0 + 32 * at + n;
-        if (h == 0) mbuf[b * G::LRP + row] = mbuf[(b ^ 1) * G::LRP + row] + sm;
+        if (h == 0) put_mass<T, G, C::DENB>(mbuf, b, row, mbuf[(b ^ 1) * G::LRP + row] + sm);
       }
     } else {
       const T* bt = PhiBT + b * G::LRP * C::TS;
@@ -263,10 +302,12 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   __shared__ __attribute__((aligned(16))) T PhiB[C::ROWS_B ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiBT[(C::TRLOAD || C::STATIC) ? 8 : 2 * G::LRP * TS];
   __shared__ __attribute__((aligned(16))) T Xs[C::NM * WC * XSP];
-  __shared__ float mbuf[C::MBUF ? 2 * G::LRP : 1];
+  __shared__ float mbuf[C::MBUF ? (C::DENB ? 4 : 2) * G::LRP : 1];
   __shared__ float dpart[C::DEN ? 2 * C::NWIN * WC : 1];
   __shared__ float hpart[C::BM == W_H ? 2 * C::NM * WC : 1];
-  __shared__ float hw[C::BM == W_GSUM ? C::NF * WC : 1];
+  // GSUM: mass weights h den per feature wave and token, then (bf16) the
+  // same weights as hi + lo parts
+  __shared__ float hw[C::BM == W_GSUM ? 2 * C::NF * WC : 1];
 
   const int64_t seg = blockIdx.x, bh = blockIdx.y;
   const int lane = lane_id(), n = lane & 31, h = lane >> 5, w = threadIdx.x >> 6;
@@ -286,9 +327,10 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   if ((C::MASS && is_f && role_b) || (C::STATIC && C::MBUF && is_f)) {
     for (int r = lane; r < C::WROWS; r += 64) {
       const int row = win * C::WROWS + r;
-      mbuf[G::LRP + row] = C::STATIC            ? a.mass_in[(size_t)bh * G::LRP + row]
-                           : (C::BM == W_FWD) ? a.bank_in[bank_off + (size_t)row * DP1 + G::D]
-                                              : 0.f;
+      put_mass<T, G, C::DENB>(mbuf, 1, row,
+                              C::STATIC          ? a.mass_in[(size_t)bh * G::LRP + row]
+                              : (C::BM == W_FWD) ? a.bank_in[bank_off + (size_t)row * DP1 + G::D]
+                                                 : 0.f);
     }
   }
 
