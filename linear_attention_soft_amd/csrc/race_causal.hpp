@@ -484,7 +484,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       float pre[G::NHP], evB[G::NHP], phB[URP / 2];
       if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
-      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, evB, phB);
+      soft_assign_rows<G, R0, URP>(pre, beta2, a.L, evB, phB, valid);   // zero rows past the segment end
       T* pt = S.PhiBT[w];
       if constexpr (C::TRB) {
         // token row n: bucket rows 8 g + 4 h .. + 3 of each 32-row tile
@@ -495,9 +495,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
             T4 v4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v4[j] = (T)phB[16 * at + 4 * g + j];
-            // tokens past the segment end: zero rows (one select per 8 bytes)
-            const uint64_t u = valid ? __builtin_bit_cast(uint64_t, v4) : 0ull;
-            *reinterpret_cast<uint64_t*>(pt + n * C::RS + 32 * at + 8 * g + 4 * h) = u;
+            *reinterpret_cast<T4*>(pt + n * C::RS + 32 * at + 8 * g + 4 * h) = v4;
           }
       } else {
 #pragma unroll
@@ -505,7 +503,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int lr = 32 * at + 8 * (v >> 2) + 4 * h + (v & 3);
-            pt[lr * TSP + n] = valid ? (T)phB[16 * at + v] : (T)0.f;
+            pt[lr * TSP + n] = (T)phB[16 * at + v];
           }
       }
     }

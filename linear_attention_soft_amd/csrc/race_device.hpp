@@ -504,7 +504,8 @@ __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict_
 // uses it).
 template <class G, int R0, int NROWS>
 __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], float beta2, int L,
-                                                 float (&ev)[G::NHP], float (&phi)[NROWS / 2]) {
+                                                 float (&ev)[G::NHP], float (&phi)[NROWS / 2], bool keep = true,
+                                                 float scale = 1.f) {
   static_assert(R0 % 32 == 0 && NROWS % 32 == 0 && R0 + NROWS <= G::LRP, "row window");
   const int h = lane_id() >> 5;
   constexpr int L0 = R0 / G::R;
@@ -527,9 +528,10 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
         ev[l * G::PE + t] = sp[t] - sm[t];
       }
     }
-    // tables >= L get zero rows: the factor of bit 2 carries the liveness
+    // tables >= L (and every table of a token with keep false) get zero rows,
+    // and every row is multiplied by scale: the factor of bit 2 carries both
     // (sigmoids are finite, so the products are exactly 0)
-    const float f2 = (l < L) ? (h ? sp[2] : sm[2]) : 0.f;
+    const float f2 = (l < L && keep) ? (h ? sp[2] : sm[2]) * scale : 0.f;
     float g[4];
     g[0] = sm[0] * sm[1] * f2;
     g[1] = sp[0] * sm[1] * f2;

@@ -163,18 +163,12 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   T* hwb = reinterpret_cast<T*>(hw + C::NF * WC);
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
   project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
-  soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi);
-  if (C::PHIDEN && role_b) {
-    const float rden = 1.f / dv;
-#pragma unroll
-    for (int i = 0; i < WROWS / 2; ++i) phi[i] *= rden;
-  }
+  // tokens past the segment end: zero rows; state role of GSUM, DV: / den
+  soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi, valid,
+                                 (C::PHIDEN && role_b) ? 1.f / dv : 1.f);
   frag fq[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    fq[q] = tl_frag<T, WROWS>(phi, q);
-    if (!valid) fq[q] = E::zero();
-  }
+  for (int q = 0; q < NQ; ++q) fq[q] = tl_frag<T, WROWS>(phi, q);
   if (!role_b) {
     T* dst = PhiA + b * WC * C::FR + n * C::FR + (R0 / 16) * 16 + h * 8;
 #pragma unroll
