@@ -87,6 +87,11 @@ struct RWCfg {
   static constexpr int ROLES = (HAS_A && !STATIC) ? 2 : 1;  // feature roles
   static constexpr int NWIN = div_le(G::LRP / 32, ROLES == 2 ? 2 : 4);   // row windows per role
   static constexpr int WROWS = G::LRP / NWIN;
+  // bf16, one table per feature window: each table gets its own projection
+  // tile (hi + lo rows), so every window projects exactly one tile (shared
+  // 8-slot tiles would give windows whose table straddles two tiles twice
+  // the work)
+  static constexpr bool TABLE_TILES = std::is_same<T, bf16>::value && WROWS == G::R && G::PE <= 8;
   static constexpr int NF = ROLES * NWIN;                   // feature waves
   static constexpr int NM = G::CT;                          // bank waves
   static constexpr int NT = 64 * (NF + NM);
@@ -162,7 +167,8 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   const bool valid = tok < s1;
   T* hwb = reinterpret_cast<T*>(hw + C::NF * WC);
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
-  project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
+  if constexpr (C::TABLE_TILES) project_table<T, G, R0 / G::R>(Wf, xf, pre);
+  else project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
   // tokens past the segment end: zero rows; state role of GSUM, DV: / den
   soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi, valid,
                                  (C::PHIDEN && role_b) ? 1.f / dv : 1.f);
@@ -291,7 +297,7 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   constexpr int XIT = WC * CPR / 64;         // row-slice loads per lane
   constexpr int DP1 = G::D + 1;
 
-  __shared__ frag Wf[G::NPT * G::KD * 64];
+  __shared__ frag Wf[(C::TABLE_TILES ? G::LMAX : G::NPT) * G::KD * 64];
   __shared__ __attribute__((aligned(16))) T PhiA[C::HAS_A ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiB[C::ROWS_B ? 2 * WC * FR : 8];
   __shared__ __attribute__((aligned(16))) T PhiBT[(C::TRLOAD || C::STATIC) ? 8 : 2 * G::LRP * TS];
@@ -317,7 +323,8 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
   const int win = w % C::NWIN;
   const int ct = w - C::NF;
 
-  build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
+  if constexpr (C::TABLE_TILES) build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
+  else build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, Wf);
   if ((C::MASS && is_f && role_b) || (C::STATIC && C::MBUF && is_f)) {
     for (int r = lane; r < C::WROWS; r += 64) {
       const int row = win * C::WROWS + r;
