@@ -636,9 +636,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         // TG0 + SPL - 1), add them in the same order in every one of them,
         // then dU_t = A_t - s E[v_t] with E[v_t] = tanh(beta u_t) from the
         // soft assignment; each lane half takes the hyperplanes it evaluated
-        // there, and the table's first wave writes dPre
+        // there, and the pairs of hyperplanes (t, t + 1) are dealt to the
+        // table's waves in turn (pair t / 2 to wave TG0 + (t / 2) % SPL), which
+        // write their dPre and add their dbeta terms
         constexpr int TG0 = TG - TG % C::SPL;
-        constexpr bool FIRST = TG == TG0;
         constexpr int l = R0 / G::R;
         float part[1 + G::PE];
         assign_partials_split<G, R0>(phA, dphi, part);
@@ -656,6 +657,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         const float s = table_sum(0);
 #pragma unroll
         for (int t = 0; t < G::PE; t += 2) {
+          if ((t / 2) % C::SPL != TG - TG0) continue;
           const bool pair = t + 1 < G::PE;
           const int tt = pair ? t + h : t;
           float uu, s2;
@@ -663,10 +665,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           const float du = table_sum(1 + tt) - s * evA[l * G::PE + t];
           if (pair || h == 0) {
             bterm += uu * du;
-            if (FIRST) put_dpre(bb, t0, l * G::PE + tt, a.beta * du * s2);
+            put_dpre(bb, t0, l * G::PE + tt, a.beta * du * s2);
           }
         }
-        if (FIRST && valid) bsum += bterm;
+        if (valid) bsum += bterm;
       }
     }
     // rows of chunk k + 1: loaded here rather than at the top of the chunk
