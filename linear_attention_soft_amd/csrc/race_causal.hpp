@@ -88,11 +88,9 @@ struct TWCfg {
   static constexpr int NXS = XSPLIT ? 2 : 1;
   // staged row (elements): with bf16 at d = 128, rows 76 dwords apart (12
   // mod 64 banks) keep both the 16-byte row reads and the transposing loads
-  // of X free of bank conflicts; the reverse walk's hi + lo X rows leave no
-  // LDS for that padding and keep 68 (4 mod 64: two-way on the transposing
-  // loads).  d = 64 rows are 36 dwords apart, conflict-free for both.
-  static constexpr int FS = G::D + ((std::is_same<T, bf16>::value && G::D == 128 && !XSPLIT) ? 24
-                                                                                           : 16 / (int)sizeof(T));
+  // of X free of bank conflicts.  d = 64 rows are 36 dwords apart,
+  // conflict-free for both.
+  static constexpr int FS = G::D + ((std::is_same<T, bf16>::value && G::D == 128) ? 24 : 16 / (int)sizeof(T));
   // Phi_B^T row (elements): an 88-byte stride keeps both its 2-byte transposed
   // writes (rows 4 apart fall 96 bytes apart) and its 8-byte operand reads (32
   // consecutive rows start on distinct 8-byte bank pairs) free of bank conflicts
@@ -144,14 +142,20 @@ struct TWLdsT {
   // chunk's dX reads (at the top of a chunk) from this chunk's dPre writes
   // (the shared-score barrier or the split-table exchange), two otherwise
   static constexpr int NDB = (SHSC || C::SPL > 1) ? 1 : 2;
+  // one buffer of output-role, state-role and U rows when a workgroup barrier
+  // (shared scores, split-table exchange) follows their last reads in a
+  // chunk, so the next chunk's rows, staged at its end, cannot overwrite rows
+  // another wave still reads; two otherwise.  X rows, read by the bank
+  // update after those barriers, keep two.
+  static constexpr int NSB = (SHSC || C::SPL > 1) ? 1 : 2;
   static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
   typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
   alignas(16) T PhiBT[C::NM][STATIC ? 8 : (C::TRB ? WC * C::RS : C::URP * C::TSP)];   // wave-private Phi_B
   alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
-  alignas(16) T AR[2][WC * C::FS];               // output-role rows (projection operands)
-  alignas(16) T BR[2][SROWS];                    // state-role rows
-  alignas(16) T UF[2][WC * C::FS];               // U rows, kmap frag order
+  alignas(16) T AR[NSB][WC * C::FS];             // output-role rows (projection operands)
+  alignas(16) T BR[NSB][SROWS];                  // state-role rows
+  alignas(16) T UF[NSB][WC * C::FS];             // U rows, kmap frag order
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[NDB][DXB ? 4 : WC * C::DPS];    // dPre of every table (float32 rows)
   alignas(16) T DB[NDB][DXB ? WC * C::DBS : 8];        // dX B-operand rows (bf16 I/O)
@@ -225,6 +229,7 @@ template <typename T, class G, bool REV, int TG, bool STATIC = false>
 __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC>& S) {
   using C = TWCfg<T, G, REV, STATIC>;
   using SL = TWLds<T, G, REV, STATIC>;
+  auto sb = [](int bb) { return SL::NSB == 2 ? bb : 0; };   // buffer of the AR, BR, UF rows
   using E = Eng<T>;
   using frag = typename E::frag;
   constexpr int R0 = TG * C::URP;
@@ -309,8 +314,8 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       if (idx < WC * CPR) {
         const int r = idx / CPR, cc = idx % CPR;
         const bool ok = t0 + r < s1;
-        *reinterpret_cast<uint4*>(&S.AR[bb][r * FS + cc * EPC]) = pa[i];
-        if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[bb][r * FS + cc * EPC]) = pb[i];
+        *reinterpret_cast<uint4*>(&S.AR[sb(bb)][r * FS + cc * EPC]) = pa[i];
+        if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[sb(bb)][r * FS + cc * EPC]) = pb[i];
         // rows past the segment end are zero; only X = g = dO / den of the
         // reverse walk is converted (bf16: hi + lo parts), the rest is copied
         const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
@@ -339,7 +344,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
           const int col = cc * EPC + 4 * g4;
           const int q = col >> 4, o = col & 15, hh = o >> 3, ee = o & 7;
           const int pos = r * FS + 16 * q + 8 * (ee >> 2) + 4 * hh;
-          *reinterpret_cast<T4*>(&S.UF[bb][pos]) = *reinterpret_cast<const T4*>(&uu[4 * g4]);
+          *reinterpret_cast<T4*>(&S.UF[sb(bb)][pos]) = *reinterpret_cast<const T4*>(&uu[4 * g4]);
           if (!STATIC) *reinterpret_cast<T4*>(&S.XF[bb][0][pos]) = *reinterpret_cast<const T4*>(&xh[4 * g4]);
           if (C::XSPLIT) *reinterpret_cast<T4*>(&S.XF[bb][1][pos]) = *reinterpret_cast<const T4*>(&xl[4 * g4]);
         }
@@ -417,7 +422,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
       const T* xr = S.XF[bb][0] + (16 * bt + l16) * FS + 8 * g4;
       const T* xl = S.XF[bb][C::NXS - 1] + (16 * bt + l16) * FS + 8 * g4;
-      const T* ur = S.UF[bb] + (16 * at2 + l16) * FS + 8 * g4;
+      const T* ur = S.UF[sb(bb)] + (16 * at2 + l16) * FS + 8 * g4;
 #pragma unroll
       for (int st = 0; st < G::D / 32; ++st) {
         const frag ub = *reinterpret_cast<const frag*>(ur + 32 * st);
@@ -472,7 +477,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     {
       frag xa[G::KD];
 #pragma unroll
-      for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[bb][n * FS + 16 * q + 8 * h]);
+      for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[sb(bb)][n * FS + 16 * q + 8 * h]);
       if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, preA);
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
       soft_assign_rows<G, R0, URP>(preA, beta2, a.L, evA, phA);
@@ -480,7 +485,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     if constexpr (!STATIC) {
       frag xb[G::KD];
 #pragma unroll
-      for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[bb][n * FS + 16 * q + 8 * h]);
+      for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[sb(bb)][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP], evB[G::NHP], phB[URP / 2];
       if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
       else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
@@ -519,7 +524,7 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     constexpr bool OWN = !STATIC && !SL::SHSC;
     f32x16 mf = zero16();
     {
-      const T* uf = S.UF[bb] + n * FS + 8 * h;
+      const T* uf = S.UF[sb(bb)] + n * FS + 8 * h;
       const T* xf = S.XF[bb][0] + n * FS + 8 * h;
       const T* xl = S.XF[bb][C::NXS - 1] + n * FS + 8 * h;
       // operands of step q + 1 are loaded before the MFMAs of step q
