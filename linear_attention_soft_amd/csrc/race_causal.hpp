@@ -8,10 +8,11 @@
 // segments.  Contractions of the bank over buckets (O, den, h, dV) run in the
 // cooperative readout-layout walks of race_walk.hpp.  This file holds the
 // walks that contract the bank over value columns:
-//   race_walk_tw  one wave per window of whole tables (bucket rows), the
-//                 workgroup walking one (segment, batch x head): dPhi_Q on a
-//                 forward walk, dPhi_K on a reverse walk, then softmax, tanh
-//                 and projection backward of those tables and dX = dPre . W.
+//   race_walk_tw  one wave per window of 32 bucket rows (whole tables, or a
+//                 part of a table of 64 to 256 corners), the workgroup walking
+//                 one (segment, batch x head): dPhi_Q on a forward walk,
+//                 dPhi_K on a reverse walk, then softmax, tanh and projection
+//                 backward of those tables and dX = dPre . W.
 // Backward (exact gradient of the causal forward map, W and beta fixed):
 //   g_t = dO_t / Den_t,  h_t = -(dO_t . O_t) / Den_t
 //   dPhi_Q,t = sum_{j<=t} phi_K,j (V_j . g_t + h_t)          (forward walk)
@@ -220,11 +221,13 @@ __device__ __forceinline__ void wt_frags_reg(const float* __restrict__ W, int ld
 //   reverse walk (dPhi_K): U = V,  ue = 1,     xe = h, X = g = dO / den
 //   softmax, tanh backward of the wave's tables -> dPre (to LDS)
 //   B[c][lr] += sum_b X_b[c] phi_B,b[lr],  m[lr] += sum_b phi_B,b[lr] xe_b
-// and, one chunk behind, dX = dPre . W for the wave's column tiles.  Rows of
-// the next chunk are staged into double-buffered LDS by the whole workgroup
-// (one barrier per chunk); X^T operands of the bank update come from the
-// staged rows through transposing LDS loads (bf16; float32 I/O multiplies the
-// rows by an identity operand).
+// and, at the top of the next chunk, dX = dPre . W for the wave's column
+// tiles.  The masked intra scores are formed once per chunk by four waves
+// and shared through LDS behind a workgroup barrier (where the stages fit;
+// else each wave forms them).  Rows of the next chunk are staged into LDS by
+// the whole workgroup at the end of the chunk (one barrier); X^T operands of
+// the bank update come from the staged rows through transposing LDS loads
+// (bf16; float32 I/O multiplies the rows by an identity operand).
 template <typename T, class G, bool REV, int TG, bool STATIC = false>
 __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC>& S) {
   using C = TWCfg<T, G, REV, STATIC>;
