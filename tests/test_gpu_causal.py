@@ -87,6 +87,23 @@ def test_causal_wide_buckets_reduced():
     check("dV", dV, rdV, TOL["bf16"])
 
 
+@pytest.mark.parametrize("N", [31, 32, 33, 95])
+def test_causal_wide_buckets_one_to_three_chunks(N):
+    """The wide-bucket recipe (P=6, L=4, d=128, bf16) over one partial chunk,
+    exactly one chunk, one chunk and a one-token tail, and a 31-token tail:
+    the transposed walks' split tables, shared score tiles and staging at
+    their smallest extents."""
+    w, inp, dev = _case(5, N, 1, 2, "bf16")
+    say(f"causal fwd+bwd {w.name} at N={N}")
+    O, state, (dQ, dK, dV) = _fwd_bwd(w, dev)
+    vmax = float(np.abs(to64(inp["V"])).max())
+    check("O", O, oracle_fwd(inp, True), TOL["bf16"], vmax=vmax)
+    rdQ, rdK, rdV = oracle_bwd(inp, True)
+    check("dQ", dQ, rdQ, TOL["bf16"])
+    check("dK", dK, rdK, TOL["bf16"])
+    check("dV", dV, rdV, TOL["bf16"])
+
+
 def test_causal_degenerate():
     """O_1 = V_1; constant V gives that constant; beta = 0 gives running means;
     one-token sequences."""

@@ -40,7 +40,7 @@ def _case(N, B, H, L, seed=None):
     return w, inp, dev
 
 
-@pytest.mark.parametrize("N,B,H,L", [(777, 1, 2, 1), (2113, 1, 2, 4), (5000, 2, 1, 2),
+@pytest.mark.parametrize("N,B,H,L", [(31, 1, 2, 4), (33, 1, 2, 4), (777, 1, 2, 1), (2113, 1, 2, 4), (5000, 2, 1, 2),
                                      (9001, 1, 2, 3), (20000, 1, 1, 4)])
 def test_wide_noncausal_parity(N, B, H, L):
     w, inp, dev = _case(N, B, H, L)
