@@ -318,8 +318,17 @@ int64_t dbeta_parts_per_side(const Plan& p) {
 }
 size_t dbeta_bytes(const Plan& p) { return align256(2 * (size_t)dbeta_parts_per_side(p) * sizeof(float)); }
 
+// Table gradient: dPre of both sides [2][BH][N][NHP] and the partials
+// [2][BH][nchunk][NHP][d] of race_dw_partial.
+int nhp(const Plan& p) { return p.ks ? p.ks->NHP : 0; }
+size_t dpre_side_bytes(const Plan& p) { return align256((size_t)p.BH * p.N * nhp(p) * sizeof(float)); }
+
+// Causal backward workspace: h, the gradient segment banks and their
+// suffixes, dbeta shares, and (kernel sets whose transposed walks read them)
+// the projections W Q and W K made once by the gradient-sum and dV walks for
+// the walks after them (float32 [BH][N][NHP] each, the size of one dPre side).
 struct CausalBwdWs {
-  size_t h, gpart, gsuf, dbeta, total;
+  size_t h, gpart, gsuf, dbeta, preq, prek, total;
 };
 CausalBwdWs causal_bwd_ws(const Plan& p) {
   CausalBwdWs w{};
@@ -328,14 +337,15 @@ CausalBwdWs causal_bwd_ws(const Plan& p) {
   w.gpart = off; off += align256(seg_bank_bytes(p));
   w.gsuf = off;  off += align256(seg_bank_bytes(p));
   w.dbeta = off; off += dbeta_bytes(p);
+  const size_t pre = (p.ks && p.ks->tw_pre) ? dpre_side_bytes(p) : 0;
+  w.preq = off;  off += pre;
+  w.prek = off;  off += pre;
   w.total = off;
   return w;
 }
 
-// Table gradient: dPre of both sides [2][BH][N][NHP] and the partials
-// [2][BH][nchunk][NHP][d] of race_dw_partial.
-int nhp(const Plan& p) { return p.ks ? p.ks->NHP : 0; }
-size_t dpre_side_bytes(const Plan& p) { return align256((size_t)p.BH * p.N * nhp(p) * sizeof(float)); }
+// dW partials [2][BH][nchunk][NHP][d] of race_dw_partial (after the dPre
+// rows of both sides).
 size_t dw_part_bytes(const Plan& p) {
   return align256(2 * (size_t)p.BH * p.nchunk * nhp(p) * p.D * sizeof(float));
 }
@@ -548,6 +558,8 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   float* h = reinterpret_cast<float*>(ws + L.h);
   float* gpart = reinterpret_cast<float*>(ws + L.gpart);
   float* gsuf = reinterpret_cast<float*>(ws + L.gsuf);
+  float* preq = p.ks->tw_pre ? reinterpret_cast<float*>(ws + L.preq) : nullptr;
+  float* prek = p.ks->tw_pre ? reinterpret_cast<float*>(ws + L.prek) : nullptr;
   const dim3 grid((unsigned)p.nseg, (unsigned)p.BH);
 
   // 1. h = -(dO . O) / Den: elementwise from O when the caller has it, else
@@ -562,9 +574,10 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
     p.ks->w_h(w, grid, s);
   }
   if ((st = check_launch("race_causal_h")) != RACE_OK) return st;
-  // 2. gradient segment sums Phi_Q^T [g | h], reverse exclusive scan
+  // 2. gradient segment sums Phi_Q^T [g | h], reverse exclusive scan; the
+  //    walk keeps its projections W Q for the walks below
   w = walk_args(p, W, beta);
-  w.B_src = Q; w.X_src = dO; w.den = den; w.hvec = h; w.bank_out = gpart;
+  w.B_src = Q; w.X_src = dO; w.den = den; w.hvec = h; w.bank_out = gpart; w.pre_out = preq;
   {
     ProfScope ps(s, "race_causal_gradsum");
     p.ks->w_gsum(w, grid, s);
@@ -572,9 +585,10 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
   launch_seg_scan(p, gpart, gsuf, 1, s);
   if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
-  // 3. dV: reverse walk with Phi_K as output role, Phi_Q as state role, g as values
+  // 3. dV: reverse walk with Phi_K as output role, Phi_Q as state role, g as
+  //    values; it keeps its projections W K
   w = walk_args(p, W, beta);
-  w.A_src = K; w.B_src = Q; w.X_src = dO; w.den = den; w.bank_in = gsuf; w.out = dV;
+  w.A_src = K; w.B_src = Q; w.X_src = dO; w.den = den; w.bank_in = gsuf; w.out = dV; w.pre_out = prek;
   {
     ProfScope ps(s, "race_causal_dv");
     p.ks->w_dv(w, grid, s);
@@ -587,6 +601,7 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   float* bparts = dbeta ? reinterpret_cast<float*>(ws + L.dbeta) : nullptr;
   char* dwr = dW ? ws + L.total : nullptr;
   t.A_src = Q; t.B_src = K; t.X_src = V; t.U_src = dO; t.bank_in = prefix; t.dX = dQ; t.dbeta_part = bparts;
+  t.preA_in = preq; t.preB_in = prek;
   t.dpre_out = dwr ? reinterpret_cast<float*>(dwr) : nullptr;
   {
     ProfScope ps(s, "race_causal_dq");
@@ -595,6 +610,7 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   if ((st = check_launch("race_causal_dq")) != RACE_OK) return st;
   // 5. dK: reverse transposed walk (dPhi_K) from the gradient suffix banks
   t.A_src = K; t.B_src = Q; t.X_src = dO; t.U_src = V; t.bank_in = gsuf; t.dX = dK;
+  t.preA_in = prek; t.preB_in = preq;
   t.dbeta_part = bparts ? bparts + dbeta_parts_per_side(p) : nullptr;
   t.dpre_out = dwr ? reinterpret_cast<float*>(dwr + dpre_side_bytes(p)) : nullptr;
   {

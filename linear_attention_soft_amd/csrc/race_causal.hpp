@@ -62,6 +62,10 @@ struct TWArgs {
   Tables W;
   float* dbeta_part;      // when set: [BH][nseg][waves] shares of dL/dbeta
   float* dpre_out;        // when set: dL/dPre of every token, float32 [BH][N][NHP]
+  // causal walks: stored projections W x of the output and state roles
+  // (float32 [BH][N][NHP], slot l PE + t), made once by the readout walks
+  const float* preA_in;
+  const float* preB_in;
   float beta;
   int L, P;
   int64_t N;
@@ -86,6 +90,11 @@ struct TWCfg {
   static constexpr int ATU = URP / 32;                // 32-row tiles per wave
   static constexpr int NT = 64 * NM;
   static constexpr bool XSPLIT = REV && !STATIC && Eng<T>::NSPLIT == 2;   // X = dO / den is not exact in T
+  // causal walks with split tables read both roles' stored projections
+  // instead of staging the Q and K rows and projecting them (whole-table
+  // waves would hold more slots in registers than they save; static walks
+  // project)
+  static constexpr bool PRE = !STATIC && SPL > 1;
   static constexpr int NXS = XSPLIT ? 2 : 1;
   // staged row (elements): with bf16 at d = 128, rows 76 dwords apart (12
   // mod 64 banks) keep both the 16-byte row reads and the transposing loads
@@ -151,11 +160,11 @@ struct TWLdsT {
   static constexpr int NSB = (SHSC || C::SPL > 1) ? 1 : 2;
   static constexpr int SROWS = STATIC ? 8 : WC * C::FS;   // state-role stages (none when static)
   // projection operands: shared 8- or 16-slot tiles, or one tile per table (SPL = 2)
-  typename Eng<T>::frag Wf[(C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
+  typename Eng<T>::frag Wf[C::PRE ? 1 : (C::SPL > 1 ? G::LMAX : G::NPT) * G::KD * 64];
   alignas(16) T PhiBT[C::NM][STATIC ? 8 : (C::TRB ? WC * C::RS : C::URP * C::TSP)];   // wave-private Phi_B
   alignas(16) float Mw[C::NM][C::URP];           // wave-private mass (forward) / h-weighted mass (reverse)
-  alignas(16) T AR[NSB][WC * C::FS];             // output-role rows (projection operands)
-  alignas(16) T BR[NSB][SROWS];                  // state-role rows
+  alignas(16) T AR[NSB][C::PRE ? 8 : WC * C::FS];   // output-role rows (projection operands)
+  alignas(16) T BR[NSB][C::PRE ? 8 : SROWS];        // state-role rows
   alignas(16) T UF[NSB][WC * C::FS];             // U rows, kmap frag order
   alignas(16) T XF[2][C::NXS][SROWS];            // X rows, kmap frag order (hi, lo)
   alignas(16) float DP[NDB][DXB ? 4 : WC * C::DPS];    // dPre of every table (float32 rows)
@@ -291,6 +300,12 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
   uint4 px[C::NPS], pu[C::NPS], pa[C::NPS], pb[C::NPS];
   float pd[C::NPS];
   float tk_h = 0.f, tk_d = 1.f;
+  // PRE: this wave's tables' stored projections of the lane's token, both
+  // roles: loaded with the staging loads, kept in registers from the staging
+  constexpr int NSW = (WT::L1 - WT::L0) * G::PE;
+  float qa[C::PRE ? NSW : 1], qb[C::PRE ? NSW : 1], ca[C::PRE ? NSW : 1], cb[C::PRE ? NSW : 1];
+  const float* preAg = C::PRE ? a.preA_in + rb * G::NHP + WT::L0 * G::PE : nullptr;
+  const float* preBg = C::PRE ? a.preB_in + rb * G::NHP + WT::L0 * G::PE : nullptr;
   auto load_stage = [&](int64_t k) {
     const int64_t t0 = chunk_t0<REV>(s0, nch, k < nch ? k : nch - 1);
 #pragma unroll
@@ -300,13 +315,20 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       const int cc = idx % CPR;
       if (!STATIC) px[i] = *reinterpret_cast<const uint4*>(Xg + row * G::D + cc * EPC);
       pu[i] = *reinterpret_cast<const uint4*>(Ug + row * G::D + cc * EPC);
-      pa[i] = *reinterpret_cast<const uint4*>(Ag + row * G::D + cc * EPC);
-      if (!STATIC) pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
+      if (!C::PRE) pa[i] = *reinterpret_cast<const uint4*>(Ag + row * G::D + cc * EPC);
+      if (!STATIC && !C::PRE) pb[i] = *reinterpret_cast<const uint4*>(Bg + row * G::D + cc * EPC);
       if (REV && !STATIC) pd[i] = den[row];
     }
     const int64_t row = min(t0 + n, s1 - 1);
     tk_h = hv[row];
     tk_d = den[row];
+    if constexpr (C::PRE) {
+#pragma unroll
+      for (int j = 0; j < NSW; ++j) {
+        qa[j] = preAg[row * G::NHP + j];
+        qb[j] = preBg[row * G::NHP + j];
+      }
+    }
   };
   // ---- write the staged chunk k into buffer bb
   auto stage = [&](int64_t k, int bb) {
@@ -317,8 +339,10 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
       if (idx < WC * CPR) {
         const int r = idx / CPR, cc = idx % CPR;
         const bool ok = t0 + r < s1;
-        *reinterpret_cast<uint4*>(&S.AR[sb(bb)][r * FS + cc * EPC]) = pa[i];
-        if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[sb(bb)][r * FS + cc * EPC]) = pb[i];
+        if constexpr (!C::PRE) {
+          *reinterpret_cast<uint4*>(&S.AR[sb(bb)][r * FS + cc * EPC]) = pa[i];
+          if (!STATIC) *reinterpret_cast<uint4*>(&S.BR[sb(bb)][r * FS + cc * EPC]) = pb[i];
+        }
         // rows past the segment end are zero; only X = g = dO / den of the
         // reverse walk is converted (bf16: hi + lo parts), the rest is copied
         const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
@@ -363,6 +387,13 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
         const T xh = (T)xe;
         S.XEB[bb][0][tid] = xh;
         S.XEB[bb][1][tid] = (T)(xe - (float)xh);
+      }
+    }
+    if constexpr (C::PRE) {
+#pragma unroll
+      for (int j = 0; j < NSW; ++j) {
+        ca[j] = qa[j];
+        cb[j] = qb[j];
       }
     }
   };
@@ -456,8 +487,13 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     }
   };
 
-  if constexpr (C::SPL > 1) build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
-  else build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
+  if constexpr (C::PRE) {
+    // projections come stored
+  } else if constexpr (C::SPL > 1) {
+    build_table_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
+  } else {
+    build_proj_frags<T, G>(a.W.at(bh), a.W.ld, a.L, a.P, S.Wf);
+  }
   if constexpr (SL::DXB) {
     // entries past 3 NHP are never written: zero (W^T is zero there too)
     for (int i = tid; i < SL::NDB * WC * C::DBS; i += C::NT) (&S.DB[0][0])[i] = (T)0.f;
@@ -478,20 +514,34 @@ __device__ __forceinline__ void tw_body(const TWArgs& a, TWLds<T, G, REV, STATIC
     // features of chunk k: output role (float32, kept), state role (rounded, to LDS)
     float preA[G::NHP], evA[G::NHP], phA[URP / 2];
     {
-      frag xa[G::KD];
+      if constexpr (C::PRE) {
 #pragma unroll
-      for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[sb(bb)][n * FS + 16 * q + 8 * h]);
-      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, preA);
-      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
+        for (int hp = 0; hp < G::NHP; ++hp) preA[hp] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) preA[WT::L0 * G::PE + j] = ca[j];
+      } else {
+        frag xa[G::KD];
+#pragma unroll
+        for (int q = 0; q < G::KD; ++q) xa[q] = *reinterpret_cast<const frag*>(&S.AR[sb(bb)][n * FS + 16 * q + 8 * h]);
+        if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xa, preA);
+        else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xa, preA);
+      }
       soft_assign_rows<G, R0, URP>(preA, beta2, a.L, evA, phA);
     }
     if constexpr (!STATIC) {
-      frag xb[G::KD];
-#pragma unroll
-      for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[sb(bb)][n * FS + 16 * q + 8 * h]);
       float pre[G::NHP], evB[G::NHP], phB[URP / 2];
-      if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
-      else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
+      if constexpr (C::PRE) {
+#pragma unroll
+        for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) pre[WT::L0 * G::PE + j] = cb[j];
+      } else {
+        frag xb[G::KD];
+#pragma unroll
+        for (int q = 0; q < G::KD; ++q) xb[q] = *reinterpret_cast<const frag*>(&S.BR[sb(bb)][n * FS + 16 * q + 8 * h]);
+        if constexpr (C::SPL > 1) project_table<T, G, R0 / G::R>(S.Wf, xb, pre);
+        else project_tiles<T, G, WT::PT0, WT::PT1>(S.Wf, xb, pre);
+      }
       soft_assign_rows<G, R0, URP>(pre, beta2, a.L, evB, phB, valid);   // zero rows past the segment end
       T* pt = S.PhiBT[w];
       if constexpr (C::TRB) {

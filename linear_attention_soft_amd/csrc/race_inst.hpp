@@ -106,6 +106,7 @@ struct Inst {
     if constexpr (NC) { k.readout = readout; k.bwd_q = bwd_q; k.bwd_kv = bwd_kv; }
     if constexpr (CAUSAL) {
       k.tw_dq = tw<false>; k.tw_dk = tw<true>; k.h_from_o = h_from_o;
+      k.tw_pre = TWCfg<T, G, false, false>::PRE ? 1 : 0;
       k.w_segsum = walk<W_SEGSUM>; k.w_gsum = walk<W_GSUM>; k.w_fwd = walk<W_FWD>; k.w_h = walk<W_H>;
       k.w_dv = walk<W_DV>;
     }

@@ -29,6 +29,9 @@ struct KernelSet {
   // causal walks (grid: segments x BH): readout layout, then transposed layout
   w_launch_fn w_segsum, w_gsum, w_fwd, w_h, w_dv;
   tw_launch_fn tw_dq, tw_dk;
+  // the causal transposed walks read the projections W Q and W K that the
+  // gradient-sum and dV walks store (split tables: 2^PE > 32)
+  int tw_pre;
   // non-causal layer through static-bank walks (tables too wide for the
   // non-causal kernels' waves; the segment-sum walks come with them); null
   // when not compiled

@@ -62,6 +62,10 @@ struct WArgs {
   float* den_out;         // FWD: [BH][N]
   const float* hvec;      // GSUM: h [BH][N]
   float* h_out;           // H: [BH][N]
+  // causal backward, when set: the projections W x that GSUM makes of its
+  // state role (Q) and DV of its output role (K), float32 [BH][N][NHP] (slot
+  // l PE + t), kept for the transposed walks
+  float* pre_out;
   Tables W;
   float beta;
   int L, P;
@@ -105,6 +109,9 @@ struct RWCfg {
   // that with X = dO the bank sums phi_Q g^T (and, GSUM, with mass weights
   // h den, phi_Q h)
   static constexpr bool PHIDEN = (BM == W_GSUM || BM == W_DV) && !STATIC;
+  // GSUM (state role) and DV (output role) store the projections they make
+  static constexpr bool PRE_OUT_A = BM == W_DV && !STATIC;
+  static constexpr bool PRE_OUT_B = BM == W_GSUM && !STATIC;
   static constexpr bool XROWS = !STATIC;                    // bank waves read X rows
   // frag-ordered feature row per token and bank-wave X tile row (elements):
   // with bf16, rows 12 dwords apart (mod 64 banks) keep both the 16-byte row
@@ -169,6 +176,12 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
   if constexpr (C::TABLE_TILES) project_table<T, G, R0 / G::R>(Wf, xf, pre);
   else project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
+  if ((role_b ? C::PRE_OUT_B : C::PRE_OUT_A) && a.pre_out && h == 0 && valid) {
+    // the slots of the window's tables
+    float* dst = a.pre_out + ((size_t)blockIdx.y * a.N + tok) * G::NHP + WT::L0 * G::PE;
+#pragma unroll
+    for (int j = 0; j < (WT::L1 - WT::L0) * G::PE; ++j) dst[j] = pre[WT::L0 * G::PE + j];
+  }
   // tokens past the segment end: zero rows; state role of GSUM, DV: / den
   soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi, valid,
                                  (C::PHIDEN && role_b) ? 1.f / dv : 1.f);
