@@ -585,10 +585,11 @@ race_status causal_backward(const Plan& p, const void* Q, const void* K, const v
   if ((st = check_launch("race_causal_gradsum")) != RACE_OK) return st;
   launch_seg_scan(p, gpart, gsuf, 1, s);
   if ((st = check_launch("race_seg_scan")) != RACE_OK) return st;
-  // 3. dV: reverse walk with Phi_K as output role, Phi_Q as state role, g as
-  //    values; it keeps its projections W K
+  // 3. dV: reverse walk with Phi_K as output role, Phi_Q as state role (from
+  //    the stored W Q where kept), g as values; it keeps its projections W K
   w = walk_args(p, W, beta);
   w.A_src = K; w.B_src = Q; w.X_src = dO; w.den = den; w.bank_in = gsuf; w.out = dV; w.pre_out = prek;
+  w.preB_in = preq;
   {
     ProfScope ps(s, "race_causal_dv");
     p.ks->w_dv(w, grid, s);

@@ -501,8 +501,11 @@ __device__ __forceinline__ void project(const typename Eng<T>::frag* __restrict_
 // both halves).  ev receives E[v_t] = sigma(2 beta u_t) - sigma(-2 beta u_t)
 // = tanh(beta u_t) of the hyperplane this half evaluated, in slot l * PE + t
 // of the pair's first hyperplane t (the softmax backward of split tables
-// uses it).
-template <class G, int R0, int NROWS>
+// uses it).  BITSEL: each half takes its hyperplane's value with a bit mask
+// instead of a select (same value; pre-activations that were loaded rather
+// than projected otherwise become one load at a lane-dependent index, which
+// moves them out of registers).
+template <class G, int R0, int NROWS, bool BITSEL = false>
 __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], float beta2, int L,
                                                  float (&ev)[G::NHP], float (&phi)[NROWS / 2], bool keep = true,
                                                  float scale = 1.f) {
@@ -516,7 +519,13 @@ __device__ __forceinline__ void soft_assign_rows(const float (&pre)[G::NHP], flo
 #pragma unroll
     for (int t = 0; t < G::PE; t += 2) {
       if (t + 1 < G::PE) {
-        const float x = h ? pre[l * G::PE + t + 1] : pre[l * G::PE + t];
+        float x;
+        if constexpr (BITSEL) {
+          const int m = h ? -1 : 0;
+          x = __int_as_float((__float_as_int(pre[l * G::PE + t + 1]) & m) | (__float_as_int(pre[l * G::PE + t]) & ~m));
+        } else {
+          x = h ? pre[l * G::PE + t + 1] : pre[l * G::PE + t];
+        }
         float p, q;
         sigmoid_pair(beta2 * tanh_f(x), p, q);
         ev[l * G::PE + t] = p - q;

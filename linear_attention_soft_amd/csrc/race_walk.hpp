@@ -64,8 +64,10 @@ struct WArgs {
   float* h_out;           // H: [BH][N]
   // causal backward, when set: the projections W x that GSUM makes of its
   // state role (Q) and DV of its output role (K), float32 [BH][N][NHP] (slot
-  // l PE + t), kept for the transposed walks
+  // l PE + t), kept for the transposed walks; with split tables DV's
+  // state-role waves read GSUM's (preB_in) instead of projecting Q
   float* pre_out;
+  const float* preB_in;
   Tables W;
   float beta;
   int L, P;
@@ -112,6 +114,14 @@ struct RWCfg {
   // GSUM (state role) and DV (output role) store the projections they make
   static constexpr bool PRE_OUT_A = BM == W_DV && !STATIC;
   static constexpr bool PRE_OUT_B = BM == W_GSUM && !STATIC;
+  // projection slots of one window: its tables, or the one table it is part of
+  static constexpr int NSW = (WROWS >= G::R ? WROWS / G::R : 1) * G::PE;
+  // split tables (the sets whose transposed walks read stored projections):
+  // DV's state-role waves load GSUM's stored W Q into the registers that
+  // otherwise hold the Q row (FPF floats per row fragment), so reading them
+  // costs no registers
+  static constexpr int FPF = (int)(sizeof(typename Eng<T>::frag) / sizeof(float));
+  static constexpr bool PRE_B = BM == W_DV && !STATIC && G::R > 32 && (NSW + FPF - 1) / FPF <= G::KD;
   static constexpr bool XROWS = !STATIC;                    // bank waves read X rows
   // frag-ordered feature row per token and bank-wave X tile row (elements):
   // with bf16, rows 12 dwords apart (mod 64 banks) keep both the 16-byte row
@@ -154,11 +164,13 @@ __device__ __forceinline__ int64_t chunk_t0(int64_t s0, int64_t nch, int64_t k) 
 // Soft-assign the 32 rows of one chunk for bucket rows [R0, R0 + WROWS) and
 // publish them: output role as frag-ordered rows (B operands of the readout),
 // state role as frag-ordered rows and transposed rows (bank update), plus
-// the mass bookkeeping of the window.
-template <typename T, class G, int MODE, int R0>
+// the mass bookkeeping of the window.  RBM: the wave's role when fixed at
+// compile time (0 output, 1 state), -1 when taken from role_b (PRE_B walks
+// instantiate the two roles separately).
+template <typename T, class G, int MODE, int R0, int RBM = -1>
 __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename Eng<T>::frag* __restrict__ Wf,
                                                   const typename Eng<T>::frag (&xf)[G::KD], float hv, float dv,
-                                                  bool role_b, int64_t t0, int64_t s1, int b, int fw,
+                                                  bool role_b_rt, int64_t t0, int64_t s1, int b, int fw,
                                                   T* __restrict__ PhiA,
                                                   T* __restrict__ PhiB, T* __restrict__ PhiBT,
                                                   float* __restrict__ mbuf, float* __restrict__ dpart,
@@ -172,19 +184,30 @@ __device__ __forceinline__ void rw_feature_window(const WArgs& a, const typename
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
   const int64_t tok = t0 + n;
   const bool valid = tok < s1;
+  const bool role_b = RBM < 0 ? role_b_rt : RBM == 1;
   T* hwb = reinterpret_cast<T*>(hw + C::NF * WC);
   float pre[G::NHP], ev[G::NHP], phi[WROWS / 2];
-  if constexpr (C::TABLE_TILES) project_table<T, G, R0 / G::R>(Wf, xf, pre);
-  else project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
-  if ((role_b ? C::PRE_OUT_B : C::PRE_OUT_A) && a.pre_out && h == 0 && valid) {
-    // the slots of the window's tables
-    float* dst = a.pre_out + ((size_t)blockIdx.y * a.N + tok) * G::NHP + WT::L0 * G::PE;
+  static_assert((WT::L1 - WT::L0) * G::PE == C::NSW, "window slots");
+  if constexpr (C::PRE_B && RBM == 1) {
+    // the stored projections of the window's tables, carried in xf
+    typedef float fv __attribute__((ext_vector_type(C::FPF)));
 #pragma unroll
-    for (int j = 0; j < (WT::L1 - WT::L0) * G::PE; ++j) dst[j] = pre[WT::L0 * G::PE + j];
+    for (int hp = 0; hp < G::NHP; ++hp) pre[hp] = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::NSW; ++j) pre[WT::L0 * G::PE + j] = __builtin_bit_cast(fv, xf[j / C::FPF])[j % C::FPF];
+  } else {
+    if constexpr (C::TABLE_TILES) project_table<T, G, R0 / G::R>(Wf, xf, pre);
+    else project_tiles<T, G, WT::PT0, WT::PT1>(Wf, xf, pre);
+    if ((role_b ? C::PRE_OUT_B : C::PRE_OUT_A) && a.pre_out && h == 0 && valid) {
+      // the slots of the window's tables
+      float* dst = a.pre_out + ((size_t)blockIdx.y * a.N + tok) * G::NHP + WT::L0 * G::PE;
+#pragma unroll
+      for (int j = 0; j < C::NSW; ++j) dst[j] = pre[WT::L0 * G::PE + j];
+    }
   }
   // tokens past the segment end: zero rows; state role of GSUM, DV: / den
-  soft_assign_rows<G, R0, WROWS>(pre, 2.f * a.beta, a.L, ev, phi, valid,
-                                 (C::PHIDEN && role_b) ? 1.f / dv : 1.f);
+  soft_assign_rows<G, R0, WROWS, C::PRE_B && RBM == 1>(pre, 2.f * a.beta, a.L, ev, phi, valid,
+                                                       (C::PHIDEN && role_b) ? 1.f / dv : 1.f);
   frag fq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) fq[q] = tl_frag<T, WROWS>(phi, q);
@@ -289,8 +312,17 @@ __device__ __forceinline__ void rw_feature_dispatch(int win, const WArgs& a, con
                                                     T* PhiBT, float* mbuf, float* dpart, float* hw) {
   using C = RWCfg<T, G, MODE>;
   if (win == WI) {
-    rw_feature_window<T, G, MODE, WI * C::WROWS>(a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
-                                                 dpart, hw, WI);
+    if constexpr (C::PRE_B) {
+      if (role_b)
+        rw_feature_window<T, G, MODE, WI * C::WROWS, 1>(a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB,
+                                                        PhiBT, mbuf, dpart, hw, WI);
+      else
+        rw_feature_window<T, G, MODE, WI * C::WROWS, 0>(a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB,
+                                                        PhiBT, mbuf, dpart, hw, WI);
+    } else {
+      rw_feature_window<T, G, MODE, WI * C::WROWS>(a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT,
+                                                   mbuf, dpart, hw, WI);
+    }
   } else if constexpr (WI + 1 < C::NWIN) {
     rw_feature_dispatch<T, G, MODE, WI + 1>(win, a, Wf, xf, hv, dv, role_b, t0, s1, b, fw, PhiA, PhiB, PhiBT, mbuf,
                                             dpart, hw);
@@ -355,6 +387,8 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
     const float* dsrc = a.den + rb;
     frag xa[G::KD], xb[G::KD];
     float ha = 0.f, hb = 0.f, da = 1.f, db = 1.f;   // h and den of the wave's token
+    // PRE_B state role: the window's stored projections W Q
+    const float* psrc = C::PRE_B ? a.preB_in + rb * G::NHP + (win * C::WROWS / G::R) * G::PE : nullptr;
     // Loads are issued for every iteration (the chunk index clamped to the
     // last one) so no prefetch sits behind a branch: the compiler then waits
     // only for the rows a projection actually consumes.
@@ -363,7 +397,18 @@ __global__ __launch_bounds__((RWCfg<T, G, MODE>::NT)) void race_walk_rw(WArgs a)
       const int64_t row = min(t0 + n, s1 - 1);
       if (C::BM == W_GSUM) hv = hsrc[row];
       if (C::PHIDEN && role_b) dv = dsrc[row];
-      load_row_frags_nb<T, G>(src + row * G::D, xf);
+      if (C::PRE_B && role_b) {
+        typedef float fv __attribute__((ext_vector_type(C::FPF)));
+#pragma unroll
+        for (int q = 0; q < (C::NSW + C::FPF - 1) / C::FPF; ++q) {
+          fv v;
+#pragma unroll
+          for (int i = 0; i < C::FPF; ++i) v[i] = q * C::FPF + i < C::NSW ? psrc[row * G::NHP + q * C::FPF + i] : 0.f;
+          xf[q] = __builtin_bit_cast(frag, v);
+        }
+      } else {
+        load_row_frags_nb<T, G>(src + row * G::D, xf);
+      }
     };
     auto feat = [&](int64_t k, const frag(&xf)[G::KD], float hv, float dv) {
       const int64_t t0 = chunk_t0<C::REV>(s0, nch, k);
